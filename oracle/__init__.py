@@ -1,0 +1,36 @@
+"""CPU oracle for the quantized MoE grouped GEMM path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The product (the HIP
+library and its Python binding) never imports, links or calls it, and this
+package shares no code with it.
+
+Every function is the plain definition of what the path computes, written in
+numpy with float64 (and exact integer) arithmetic, no blocking, fusion or
+reordering.  Sources, by page:
+  * CUTLASS discussion #2855, "How to implement dequantization of row and
+    column broadcast in Epilogue of GroupGemm" (W4A4 INT4 grouped GEMM with
+    per-token x per-channel scales; the [E+1] row-offset table).
+  * CUTLASS issue #2087, "how to use groupwise scaling along M for FP8 gemm to
+    implement per-token-per-128-channel and blockwise" (FP8 e4m3 with 1x128 A
+    scales and 128x128 B scales; the M-contiguous A-scale layout).
+  * nvfp4-megamoe-kernel, tilelang_kernels.py, grouped_gemm_fp4 (NVFP4 routed
+    grouped GEMM and weighted scatter-add).
+  * megamoe_rm.cu (route_prep, fc1_rm, fc2_rm, combine kernels: stable
+    per-expert ordering, -1 ids, per-expert global scale, SiLU-gated FC1,
+    k-ordered fp32 combine).
+
+Parity pins: every function here is checked, in tests/test_oracle_*.py,
+against something other than itself (torch's codecs, brute force in pure
+Python, a differently structured algorithm, invariants).  No function is
+parity unpinned.
+"""
+from .formats import (unpack_nibbles, int4_value, e2m1_value, e4m3fn_value, ue4m3_value,
+                      bf16_value, round_to_f16, round_to_bf16, round_to)
+from .route import route_prep
+from .gemm import (grouped_gemm_qint4, grouped_gemm_qfp8_block, grouped_gemm_qnvfp4, silu_mul,
+                   gemm_rows)
+from .combine import scatter_combine
+from .layer import int4_layer, nvfp4_layer, fp8_dense
+
+__all__ = [n for n in dir() if not n.startswith("_")]
