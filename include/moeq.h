@@ -1,0 +1,212 @@
+/*
+ * moeq.h - C ABI of the quantized mixture-of-experts grouped GEMM library
+ *          for AMD Instinct MI355X (gfx950).
+ *
+ * The routed MoE hot path in five calls:
+ *   moe_route_prep          group (token, slot) pairs by expert
+ *   grouped_gemm_qint4      W4A4 INT4 GEMM, per-token x per-channel scales
+ *   grouped_gemm_qfp8_block FP8 e4m3 GEMM, 1x128 A / 128x128 B block scales
+ *   grouped_gemm_qnvfp4     NVFP4 (E2M1 + UE4M3 per-16 + global) x bf16 GEMM
+ *   moe_scatter_combine     top-k weighted sum back to token rows
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is a DEVICE pointer (memory the caller allocated
+ *     on the current HIP device) unless marked "host".  The caller owns all
+ *     memory, scratch included; the library allocates nothing, keeps no state
+ *     between calls and never synchronizes the host with the device.
+ *   - Every call only validates its arguments on the host and enqueues
+ *     kernels on `stream` (a hipStream_t; NULL = the null stream).  Results
+ *     are visible to later work on that stream.
+ *   - Argument errors are detected before anything is enqueued and returned
+ *     as a status; moeq_last_error() then gives a text for the calling
+ *     thread.  A failed launch returns MOEQ_EHIP.  Nothing throws.
+ *   - Shorthands: T tokens, topk = k slots per token, E experts,
+ *     P = T*topk pairs, pair id p = t*topk + j for topk_ids[t][j].
+ *   - 4-bit codes (INT4 and E2M1) are packed two per byte, element 2b in the
+ *     low nibble of byte b.  Matrices are row-major; a weight matrix W[e] is
+ *     stored [N][K] with K contiguous (y = x . W^T).
+ *   - Grouped GEMM rows: sorted position s in [0, expert_offsets[E]) belongs
+ *     to expert e with expert_offsets[e] <= s < expert_offsets[e+1]; its
+ *     output row is out[s][:].  Rows past expert_offsets[E] are not written.
+ *     The activation row used for s is chosen by moeq_arow:
+ *       MOEQ_AROW_TOKEN : row sorted_pair_ids[s] / topk  (token-major input
+ *                         [T][K], each token feeding its k experts)
+ *       MOEQ_AROW_SORTED: row s  (input already in sorted order, e.g. the
+ *                         output of a previous grouped GEMM)
+ *     With sorted_pair_ids == NULL the rows are the identity (SORTED).
+ *
+ * Sources (web pages on quantized MoE grouped GEMMs; cited by title):
+ *   [W4A4]   CUTLASS discussion #2855, "How to implement dequantization of
+ *            row and column broadcast in Epilogue of GroupGemm"
+ *   [FP8BLK] CUTLASS issue #2087, "how to use groupwise scaling along M for
+ *            FP8 gemm to implement per-token-per-128-channel and blockwise"
+ *   [TLK]    nvfp4-megamoe-kernel, tilelang_kernels.py (grouped_gemm_fp4)
+ *   [MMRM]   megamoe_rm.cu (route_prep, fc1_rm, fc2_rm, combine)
+ */
+#ifndef MOEQ_H
+#define MOEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOEQ_OK = 0,
+  MOEQ_EINVAL = 1,       /* null pointer, negative or inconsistent size */
+  MOEQ_EALIGN = 2,       /* pointer or dimension not aligned as required */
+  MOEQ_EUNSUPPORTED = 3, /* dtype / act / mode combination not provided */
+  MOEQ_EHIP = 4          /* a HIP launch failed */
+} moeq_status;
+
+typedef enum { MOEQ_F16 = 1, MOEQ_BF16 = 2, MOEQ_F32 = 3, MOEQ_I32 = 4 } moeq_dtype;
+
+/* MOEQ_ACT_SILU_MUL: the GEMM's N = 2I columns are [gate | up]
+ * (columns [0, I) gate, [I, 2I) up); the call writes I columns
+ * h = silu(gate) * up, silu(g) = g / (1 + exp(-g)). */
+typedef enum { MOEQ_ACT_NONE = 0, MOEQ_ACT_SILU_MUL = 1 } moeq_act;
+
+typedef enum { MOEQ_AROW_TOKEN = 0, MOEQ_AROW_SORTED = 1 } moeq_arow;
+
+/* Schedule hint for the grouped GEMMs.  Both schedules compute the same
+ * result for every input; AUTO picks by the average rows per expert
+ * (P / E): the weight-streaming DECODE schedule for few rows per expert,
+ * the MFMA-tiled PREFILL schedule otherwise. */
+typedef enum { MOEQ_SCHED_AUTO = 0, MOEQ_SCHED_DECODE = 1, MOEQ_SCHED_PREFILL = 2 } moeq_sched;
+
+/* Text describing the last non-OK status returned on the calling thread
+ * (host, thread-local, owned by the library; valid until the next call). */
+const char* moeq_last_error(void);
+
+/* Library ABI version (host). */
+int32_t moeq_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * moe_route_prep - group the P = T*topk (token, slot) pairs by expert.
+ * [MMRM] route_prep (pair id token*topk + k; a pair's place is its rank
+ * among earlier pairs of the same expert, so the table is unique; id -1
+ * means no expert); [W4A4] the [E+1] per-expert row-offset table.
+ *
+ *   topk_ids        int32 [T][topk]   expert id per slot; -1 = none
+ *   expert_offsets  int32 [E+1] out   exclusive prefix of per-expert counts
+ *   sorted_pair_ids int32 [P]   out   valid pairs ordered by (expert, pair
+ *                                     id); positions >= expert_offsets[E]
+ *                                     hold -1
+ *   pair_to_sorted  int32 [P]   out   inverse: sorted position of pair p,
+ *                                     -1 if p was skipped
+ *   n_invalid       int32 [1]   out   number of ids outside [0, E) other
+ *                                     than -1 (those pairs are skipped too)
+ *   workspace       device scratch of moe_route_prep_workspace_bytes() bytes
+ *                   (may be NULL when that is 0); contents on entry ignored
+ * Requires T >= 0, 1 <= topk <= 64, 1 <= E <= 4096, T*topk < 2^31.
+ * T == 0 writes expert_offsets = 0 and n_invalid = 0.
+ * ---------------------------------------------------------------------- */
+size_t moe_route_prep_workspace_bytes(int64_t T, int32_t topk, int32_t E); /* host */
+
+moeq_status moe_route_prep(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
+                           int32_t* expert_offsets, int32_t* sorted_pair_ids,
+                           int32_t* pair_to_sorted, int32_t* n_invalid, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * grouped_gemm_qint4 - W4A4 INT4 grouped GEMM with the dequantization fused
+ * into the epilogue.  [W4A4] problem statement: activations quantized per
+ * token, weights per output channel, int32 accumulation,
+ * y = scale_act * scale_weight * accumulator.
+ *
+ *   a          uint8 [rows_a][K/2]   int4 activations (two's complement)
+ *   a_scale    f32   [rows_a]        per-row activation scale
+ *   w          uint8 [E][N][K/2]     int4 weights
+ *   w_scale    f32   [E][N]          per-output-channel weight scale
+ *   expert_offsets, sorted_pair_ids  from moe_route_prep (see top)
+ *   P          rows of `out` (>= expert_offsets[E]); topk as routed
+ *   out        [P][N] (act NONE) or [P][N/2] (SILU_MUL) of out_dtype:
+ *                F16 | BF16 | F32: a_scale[r] * w_scale[e][n] * acc
+ *                I32: the raw accumulator acc (act NONE only), bit-exact
+ * Computed exactly in integers (int8 MFMA on nibbles scaled by 16), then
+ * scaled in fp32 and rounded to nearest even.
+ * Requires K % 128 == 0, N % 64 == 0 (SILU_MUL: N % 128 == 0), all
+ * pointers 16-byte aligned, E >= 1.
+ * ---------------------------------------------------------------------- */
+moeq_status grouped_gemm_qint4(const uint8_t* a, const float* a_scale, int64_t rows_a,
+                               moeq_arow a_row, const uint8_t* w, const float* w_scale,
+                               const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
+                               int64_t P, int32_t topk, int32_t E, int64_t N, int64_t K,
+                               moeq_act act, moeq_dtype out_dtype, void* out, moeq_sched sched,
+                               void* stream);
+
+/* ------------------------------------------------------------------------
+ * grouped_gemm_qfp8_block - FP8 e4m3 block-scaled grouped GEMM.  [FP8BLK]:
+ * A scaled per token per 128 columns of K, B per 128x128 block; scales
+ * applied per 128-wide K group inside the main loop (fp32 accumulation).
+ *
+ *   a        uint8 [rows_a][K]        OCP e4m3fn activations
+ *   a_scale  f32   [K/128][rows_a]    per (K group, row); rows contiguous,
+ *                                     the M-contiguous layout [FP8BLK]
+ *                                     recommends so scale loads coalesce
+ *   w        uint8 [E][N][K]          OCP e4m3fn weights
+ *   w_scale  f32   [E][N/128][K/128]  per 128x128 weight block
+ *   out      [P][N] out_dtype (BF16 | F16 | F32)
+ *   y[s][n] = sum_g a_scale[g][r] * w_scale[e][n/128][g]
+ *                   * sum_{k in group g} a[r][k] * w[e][n][k]
+ * Requires K % 128 == 0, N % 128 == 0, 16-byte aligned pointers.
+ * ---------------------------------------------------------------------- */
+moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int64_t rows_a,
+                                    moeq_arow a_row, const uint8_t* w, const float* w_scale,
+                                    const int32_t* expert_offsets,
+                                    const int32_t* sorted_pair_ids, int64_t P, int32_t topk,
+                                    int32_t E, int64_t N, int64_t K, moeq_dtype out_dtype,
+                                    void* out, moeq_sched sched, void* stream);
+
+/* ------------------------------------------------------------------------
+ * grouped_gemm_qnvfp4 - NVFP4 W4A16 grouped GEMM.  [TLK] grouped_gemm_fp4
+ * (E2M1 weights with UE4M3 scales per 16 along K, bf16 activations) with
+ * the per-expert global scale of [MMRM] (alpha = weight_scale_2 /
+ * input_scale).  Weights are dequantized exactly (every E2M1 x UE4M3
+ * product is a bf16 value) in registers, never as a separate pass.
+ *
+ *   x         bf16  [rows_a][K]       activations
+ *   w         uint8 [E][N][K/2]       E2M1 codes
+ *   w_sf      uint8 [E][N][K/16]      UE4M3 block scales (sign bit clear;
+ *                                     0x7F is not a valid scale)
+ *   w_gscale  f32   [E]               per-expert global scale
+ *   out       [P][N] (NONE) or [P][N/2] (SILU_MUL), BF16 | F16 | F32
+ *   y[s][n] = w_gscale[e] * sum_k x[r][k] * e2m1(w[e][n][k])
+ *                                  * ue4m3(w_sf[e][n][k/16])
+ * Requires K % 128 == 0, N % 64 == 0 (SILU_MUL: N % 128 == 0), 16-byte
+ * aligned pointers.
+ * ---------------------------------------------------------------------- */
+moeq_status grouped_gemm_qnvfp4(const void* x, int64_t rows_a, moeq_arow a_row,
+                                const uint8_t* w, const uint8_t* w_sf, const float* w_gscale,
+                                const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
+                                int64_t P, int32_t topk, int32_t E, int64_t N, int64_t K,
+                                moeq_act act, moeq_dtype out_dtype, void* out,
+                                moeq_sched sched, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_scatter_combine - weighted sum of each token's expert rows.
+ * [MMRM] combine (a token's pairs that have an expert, summed in slot
+ * order in fp32, one rounding); [TLK] zero output plus weighted
+ * scatter-add.
+ *
+ *   y             [P][N] y_dtype (F16 | BF16 | F32), rows in sorted order
+ *   pair_to_sorted int32 [T*topk] from moe_route_prep
+ *   topk_weights  f32 [T][topk]
+ *   out           [T][N] out_dtype (F16 | BF16 | F32)
+ *   out[t][:] = sum_{j < topk, pair_to_sorted[t*topk+j] >= 0}
+ *                 topk_weights[t][j] * y[pair_to_sorted[t*topk+j]][:]
+ * accumulated in fp32 in slot order and rounded once (nearest even);
+ * a token with no routed pair gets a zero row.
+ * Requires N % 8 == 0, 16-byte aligned pointers.
+ * ---------------------------------------------------------------------- */
+moeq_status moe_scatter_combine(const void* y, moeq_dtype y_dtype, const int32_t* pair_to_sorted,
+                                const float* topk_weights, int64_t T, int32_t topk, int64_t N,
+                                moeq_dtype out_dtype, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEQ_H */

@@ -1,0 +1,248 @@
+"""Quantized MoE grouped GEMM for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over the C-ABI library libmoeq.so (include/moeq.h).
+Each function here only checks and marshals its torch arguments (device
+pointers, sizes, torch's current HIP stream) and calls the C entry point of
+the same name; every step of the computation runs in the library's HIP
+kernels.  PyTorch supplies device memory and streams only.
+
+If libmoeq.so is missing or cannot be loaded, every call raises: there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoeq.so")
+
+# Status codes and enums of include/moeq.h.
+OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP = 0, 1, 2, 3, 4
+F16, BF16, F32, I32 = 1, 2, 3, 4
+ACT = {"none": 0, "silu_mul": 1}
+AROW = {"token": 0, "sorted": 1}
+SCHED = {"auto": 0, "decode": 1, "prefill": 2}
+
+_DTYPE_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32, torch.int32: I32}
+
+EXPORTS = ("moeq_last_error", "moeq_abi_version", "moe_route_prep_workspace_bytes",
+           "moe_route_prep", "grouped_gemm_qint4", "grouped_gemm_qfp8_block",
+           "grouped_gemm_qnvfp4", "moe_scatter_combine")
+
+
+class MoeqError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m quantized_moe_grouped_route_amd.build`")
+    L = C.CDLL(LIB_PATH)
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    sig = {
+        "moeq_last_error": (C.c_char_p, []),
+        "moeq_abi_version": (i32, []),
+        "moe_route_prep_workspace_bytes": (sz, [i64, i32, i32]),
+        "moe_route_prep": (i32, [vp, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "grouped_gemm_qint4": (i32, [vp, vp, i64, i32, vp, vp, vp, vp, i64, i32, i32, i64, i64,
+                                     i32, i32, vp, i32, vp]),
+        "grouped_gemm_qfp8_block": (i32, [vp, vp, i64, i32, vp, vp, vp, vp, i64, i32, i32, i64,
+                                          i64, i32, vp, i32, vp]),
+        "grouped_gemm_qnvfp4": (i32, [vp, i64, i32, vp, vp, vp, vp, vp, i64, i32, i32, i64, i64,
+                                      i32, i32, vp, i32, vp]),
+        "moe_scatter_combine": (i32, [vp, i32, vp, vp, i64, i32, i64, i32, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    _lib = L
+    return L
+
+
+def _check(fn: str, st: int):
+    if st != OK:
+        raise MoeqError(fn, st, lib().moeq_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t, name, dtype=None, ndim=None, device=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+
+
+def route_workspace_bytes(T: int, topk: int, E: int) -> int:
+    return int(lib().moe_route_prep_workspace_bytes(T, topk, E))
+
+
+def moe_route_prep(topk_ids, E: int, *, out=None, workspace=None):
+    """Group the (token, slot) pairs by expert.
+
+    topk_ids int32 [T][topk] on the GPU.  Returns (expert_offsets [E+1],
+    sorted_pair_ids [P], pair_to_sorted [P], n_invalid [1]), all int32;
+    `out` may supply these four tensors preallocated, `workspace` a uint8
+    tensor of route_workspace_bytes(T, topk, E) bytes."""
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    T, k = topk_ids.shape
+    P = T * k
+    dev = topk_ids.device
+    if out is None:
+        out = (torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(P, dtype=torch.int32, device=dev),
+               torch.empty(P, dtype=torch.int32, device=dev),
+               torch.empty(1, dtype=torch.int32, device=dev))
+    offs, srt, p2s, ninv = out
+    for t, n, sz in ((offs, "expert_offsets", E + 1), (srt, "sorted_pair_ids", P),
+                     (p2s, "pair_to_sorted", P), (ninv, "n_invalid", 1)):
+        _need(t, n, torch.int32)
+        if t.numel() < sz:
+            raise ValueError(f"{n} needs {sz} elements")
+    need = route_workspace_bytes(T, k, E)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().moe_route_prep(_ptr(topk_ids), T, k, E, _ptr(offs), _ptr(srt), _ptr(p2s),
+                              _ptr(ninv), _ptr(workspace), wsb, _stream())
+    _check("moe_route_prep", st)
+    return offs, srt, p2s, ninv
+
+
+def _grouped_common(a, expert_offsets, sorted_pair_ids, a_row, P):
+    _need(expert_offsets, "expert_offsets", torch.int32, 1)
+    if sorted_pair_ids is not None:
+        _need(sorted_pair_ids, "sorted_pair_ids", torch.int32, 1)
+    E = expert_offsets.numel() - 1
+    if P is None:
+        P = sorted_pair_ids.numel() if sorted_pair_ids is not None else a.shape[0]
+    return E, P, AROW[a_row]
+
+
+def _out(out, P, n_out, dtype, dev):
+    if out is None:
+        return torch.empty(P, n_out, dtype=dtype, device=dev)
+    _need(out, "out", dtype, 2)
+    if out.shape[0] < P or out.shape[1] != n_out:
+        raise ValueError(f"out must be [{P}][{n_out}], got {tuple(out.shape)}")
+    return out
+
+
+def grouped_gemm_qint4(a, a_scale, w, w_scale, expert_offsets, sorted_pair_ids, topk: int, *,
+                       a_row="token", act="none", out_dtype=torch.float16, out=None, P=None,
+                       sched="auto"):
+    """W4A4 INT4 grouped GEMM: a uint8 [rows_a][K/2], a_scale f32 [rows_a],
+    w uint8 [E][N][K/2], w_scale f32 [E][N].  Returns out [P][N] (act
+    'none') or [P][N/2] ('silu_mul'); out_dtype torch.int32 gives the raw
+    accumulators."""
+    _need(a, "a", torch.uint8, 2)
+    _need(a_scale, "a_scale", torch.float32, 1)
+    _need(w, "w", torch.uint8, 3)
+    _need(w_scale, "w_scale", torch.float32, 2)
+    E, P, arow = _grouped_common(a, expert_offsets, sorted_pair_ids, a_row, P)
+    En, N, Kh = w.shape
+    K = 2 * Kh
+    if En != E or a.shape[1] != Kh or tuple(w_scale.shape) != (E, N) or a_scale.numel() != a.shape[0]:
+        raise ValueError("inconsistent INT4 operand shapes")
+    out = _out(out, P, N // 2 if act == "silu_mul" else N, out_dtype, a.device)
+    st = lib().grouped_gemm_qint4(_ptr(a), _ptr(a_scale), a.shape[0], arow, _ptr(w), _ptr(w_scale),
+                                  _ptr(expert_offsets), _ptr(sorted_pair_ids), P, topk, E, N, K,
+                                  ACT[act], _DTYPE_CODE[out_dtype], _ptr(out), SCHED[sched],
+                                  _stream())
+    _check("grouped_gemm_qint4", st)
+    return out
+
+
+def grouped_gemm_qfp8_block(a, a_scale, w, w_scale, expert_offsets, sorted_pair_ids, topk: int, *,
+                            a_row="token", out_dtype=torch.bfloat16, out=None, P=None,
+                            sched="auto"):
+    """FP8 e4m3 block-scaled grouped GEMM: a uint8 [rows_a][K] (e4m3 bits),
+    a_scale f32 [K/128][rows_a], w uint8 [E][N][K], w_scale f32
+    [E][N/128][K/128].  Returns out [P][N]."""
+    _need(a, "a", torch.uint8, 2)
+    _need(a_scale, "a_scale", torch.float32, 2)
+    _need(w, "w", torch.uint8, 3)
+    _need(w_scale, "w_scale", torch.float32, 3)
+    E, P, arow = _grouped_common(a, expert_offsets, sorted_pair_ids, a_row, P)
+    En, N, K = w.shape
+    if (En != E or a.shape[1] != K or tuple(a_scale.shape) != (K // 128, a.shape[0])
+            or tuple(w_scale.shape) != (E, N // 128, K // 128)):
+        raise ValueError("inconsistent FP8 operand shapes")
+    out = _out(out, P, N, out_dtype, a.device)
+    st = lib().grouped_gemm_qfp8_block(_ptr(a), _ptr(a_scale), a.shape[0], arow, _ptr(w),
+                                       _ptr(w_scale), _ptr(expert_offsets), _ptr(sorted_pair_ids),
+                                       P, topk, E, N, K, _DTYPE_CODE[out_dtype], _ptr(out),
+                                       SCHED[sched], _stream())
+    _check("grouped_gemm_qfp8_block", st)
+    return out
+
+
+def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, topk: int, *,
+                        a_row="token", act="none", out_dtype=torch.bfloat16, out=None, P=None,
+                        sched="auto"):
+    """NVFP4 W4A16 grouped GEMM: x bf16 [rows_a][K], w uint8 [E][N][K/2]
+    (E2M1), w_sf uint8 [E][N][K/16] (UE4M3), w_gscale f32 [E].  Returns out
+    [P][N] (act 'none') or [P][N/2] ('silu_mul')."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w, "w", torch.uint8, 3)
+    _need(w_sf, "w_sf", torch.uint8, 3)
+    _need(w_gscale, "w_gscale", torch.float32, 1)
+    E, P, arow = _grouped_common(x, expert_offsets, sorted_pair_ids, a_row, P)
+    En, N, Kh = w.shape
+    K = 2 * Kh
+    if En != E or x.shape[1] != K or tuple(w_sf.shape) != (E, N, K // 16) or w_gscale.numel() != E:
+        raise ValueError("inconsistent NVFP4 operand shapes")
+    out = _out(out, P, N // 2 if act == "silu_mul" else N, out_dtype, x.device)
+    st = lib().grouped_gemm_qnvfp4(_ptr(x), x.shape[0], arow, _ptr(w), _ptr(w_sf), _ptr(w_gscale),
+                                   _ptr(expert_offsets), _ptr(sorted_pair_ids), P, topk, E, N, K,
+                                   ACT[act], _DTYPE_CODE[out_dtype], _ptr(out), SCHED[sched],
+                                   _stream())
+    _check("grouped_gemm_qnvfp4", st)
+    return out
+
+
+def moe_scatter_combine(y, pair_to_sorted, topk_weights, *, out_dtype=None, out=None):
+    """out[t] = sum_j topk_weights[t, j] * y[pair_to_sorted[t*k+j]] over the
+    routed slots of token t, fp32 in slot order, one rounding."""
+    _need(y, "y", (torch.float16, torch.bfloat16, torch.float32), 2)
+    _need(pair_to_sorted, "pair_to_sorted", torch.int32, 1)
+    _need(topk_weights, "topk_weights", torch.float32, 2)
+    T, k = topk_weights.shape
+    N = y.shape[1]
+    if pair_to_sorted.numel() != T * k:
+        raise ValueError("pair_to_sorted must have T*topk entries")
+    if y.shape[0] < T * k:
+        raise ValueError("y must have at least T*topk rows (sorted positions index into it)")
+    out_dtype = out_dtype or y.dtype
+    if out is None:
+        out = torch.empty(T, N, dtype=out_dtype, device=y.device)
+    _need(out, "out", out_dtype, 2)
+    st = lib().moe_scatter_combine(_ptr(y), _DTYPE_CODE[y.dtype], _ptr(pair_to_sorted),
+                                   _ptr(topk_weights), T, k, N, _DTYPE_CODE[out_dtype], _ptr(out),
+                                   _stream())
+    _check("moe_scatter_combine", st)
+    return out

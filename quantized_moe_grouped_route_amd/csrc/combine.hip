@@ -1,0 +1,111 @@
+// Top-k weighted scatter back to token rows (megamoe_rm.cu's combine: a
+// token's pairs that have an expert, summed in slot order in fp32 and
+// rounded once; tilelang_kernels.py: zero output plus weighted rows).
+//
+// One thread owns 8 consecutive columns of one token row: it reads the
+// pair table entries of its token, then 8 elements (16 or 32 bytes) of each
+// routed expert row, so every wave reads and writes contiguous runs.
+#include "common.h"
+#include "kernels.h"
+
+namespace moeq {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int YK>
+__device__ __forceinline__ void load8(const void* y, int64_t off, float v[8]) {
+  if (YK == OUT_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(y) + off);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) + off);
+    const u32 w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (YK == OUT_BF16) {
+        v[2 * j] = bf16_bits_to_f32(w[j] & 0xffffu);
+        v[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+      } else {
+        v[2 * j] = f16_bits_to_f32((uint16_t)(w[j] & 0xffffu));
+        v[2 * j + 1] = f16_bits_to_f32((uint16_t)(w[j] >> 16));
+      }
+    }
+  }
+}
+
+template <int OK>
+__device__ __forceinline__ void store8(void* out, int64_t off, const float v[8]) {
+  if (OK == OUT_F32) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + off);
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    u32 w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (u32)OutT<OK>::from(v[2 * j]) | ((u32)OutT<OK>::from(v[2 * j + 1]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + off) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+template <int YK, int OK>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restrict__ y,
+                                                           const int* __restrict__ p2s,
+                                                           const float* __restrict__ tw, int T,
+                                                           int topk, int N, int64_t P,
+                                                           void* __restrict__ out) {
+  const int cblocks = (N / 8 + kThreads - 1) / kThreads;
+  const int t = blockIdx.x / cblocks;
+  const int c = ((blockIdx.x - t * cblocks) * kThreads + threadIdx.x) * 8;
+  if (c >= N) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < topk; ++j) {
+    const int s = p2s[(int64_t)t * topk + j];
+    if (s < 0 || s >= P) continue;
+    const float w = tw[(int64_t)t * topk + j];
+    float v[8];
+    load8<YK>(y, (int64_t)s * N + c, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(w, v[q], acc[q]);
+  }
+  store8<OK>(out, (int64_t)t * N + c, acc);
+}
+
+template <int YK>
+hipError_t launch_y(const void* y, const int* p2s, const float* tw, int T, int topk, int N,
+                    int64_t P, int out_kind, void* out, hipStream_t stream) {
+  const dim3 grid(((N / 8 + kThreads - 1) / kThreads) * T);
+  switch (out_kind) {
+    case OUT_F16:
+      hipLaunchKernelGGL((combine_kernel<YK, OUT_F16>), grid, dim3(kThreads), 0, stream, y, p2s, tw,
+                         T, topk, N, P, out);
+      break;
+    case OUT_BF16:
+      hipLaunchKernelGGL((combine_kernel<YK, OUT_BF16>), grid, dim3(kThreads), 0, stream, y, p2s,
+                         tw, T, topk, N, P, out);
+      break;
+    default:
+      hipLaunchKernelGGL((combine_kernel<YK, OUT_F32>), grid, dim3(kThreads), 0, stream, y, p2s, tw,
+                         T, topk, N, P, out);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* y, int y_kind, const int* p2s, const float* tw, int T,
+                          int topk, int N, int64_t P, int out_kind, void* out,
+                          hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  switch (y_kind) {
+    case OUT_F16: return launch_y<OUT_F16>(y, p2s, tw, T, topk, N, P, out_kind, out, stream);
+    case OUT_BF16: return launch_y<OUT_BF16>(y, p2s, tw, T, topk, N, P, out_kind, out, stream);
+    default: return launch_y<OUT_F32>(y, p2s, tw, T, topk, N, P, out_kind, out, stream);
+  }
+}
+
+}  // namespace moeq

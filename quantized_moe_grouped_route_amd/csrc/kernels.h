@@ -1,0 +1,46 @@
+// Internal launchers (host side of each kernel file).  Arguments are
+// validated by the C-ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moeq {
+
+// Route prep.
+size_t route_workspace_bytes(int64_t P, int E);
+size_t route_lds_bytes(int E);
+hipError_t launch_route(const int* ids, int P, int E, int* offsets, int* sorted_ids,
+                        int* pair_to_sorted, int* n_invalid, void* ws, hipStream_t stream);
+
+// Combine.  y_kind / out_kind are OutKind values.
+hipError_t launch_combine(const void* y, int y_kind, const int* p2s, const float* tw, int T,
+                          int topk, int N, int64_t P, int out_kind, void* out, hipStream_t stream);
+
+// Arguments common to the grouped GEMMs.
+struct GroupedArgs {
+  const int* offsets;       // [E+1]
+  const int* sorted_ids;    // [P] or null (identity rows)
+  int64_t rows_a;           // rows of the activation operand
+  int a_sorted;             // 1: row = s, 0: row = sorted_ids[s] / topk
+  int topk;
+  int E;
+  int64_t P;
+  int N;                    // GEMM columns (2I for SILU_MUL)
+  int K;
+  int silu_mul;             // 1: write I = N/2 columns silu(gate) * up
+  int out_kind;             // OutKind
+  void* out;
+  int sched;                // 0 auto, 1 decode, 2 prefill
+  int num_cus;              // compute units of the current device
+};
+
+hipError_t launch_gemm_int4(const GroupedArgs& g, const uint8_t* a, const float* a_scale,
+                            const uint8_t* w, const float* w_scale, hipStream_t stream);
+hipError_t launch_gemm_fp8(const GroupedArgs& g, const uint8_t* a, const float* a_scale,
+                           const uint8_t* w, const float* w_scale, hipStream_t stream);
+hipError_t launch_gemm_nvfp4(const GroupedArgs& g, const uint16_t* x, const uint8_t* w,
+                             const uint8_t* w_sf, const float* w_gscale, hipStream_t stream);
+
+}  // namespace moeq

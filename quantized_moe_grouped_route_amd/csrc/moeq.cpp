@@ -1,0 +1,221 @@
+// C ABI of the library: host-side validation and asynchronous launch on the
+// caller's stream.  Nothing here allocates device memory, synchronizes, or
+// copies between host and device.  The argument checks mirror the pages'
+// conventions (CUTLASS discussion #2855 rejects K or N not multiples of 32
+// before launching; megamoe_rm.cu checks every shape before its launches),
+// reported as status codes because the boundary is C.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moeq.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moeq_status fail(moeq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxTopk = 64;
+
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+moeq_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOEQ_OK;
+  return fail(MOEQ_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+// Checks shared by the three grouped GEMMs.
+moeq_status check_grouped(const char* fn, const void* a, int64_t rows_a, int a_row, const void* w,
+                          const int32_t* offsets, int64_t P, int32_t topk, int32_t E, int64_t N,
+                          int64_t K, const void* out) {
+  if (E < 1 || E > kMaxE) return fail(MOEQ_EINVAL, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  if (topk < 1 || topk > kMaxTopk) return fail(MOEQ_EINVAL, "%s: topk=%d outside [1, %d]", fn, topk, kMaxTopk);
+  if (P < 0 || P >= (int64_t(1) << 31)) return fail(MOEQ_EINVAL, "%s: P=%lld out of range", fn, (long long)P);
+  if (rows_a < 0 || rows_a >= (int64_t(1) << 31)) return fail(MOEQ_EINVAL, "%s: rows_a=%lld out of range", fn, (long long)rows_a);
+  if (P > 0 && rows_a == 0) return fail(MOEQ_EINVAL, "%s: rows_a=0 with P>0", fn);
+  if (N <= 0 || K <= 0 || N > (1 << 20) || K > (1 << 17))
+    return fail(MOEQ_EINVAL, "%s: N=%lld K=%lld out of range", fn, (long long)N, (long long)K);
+  if (K % 128 != 0) return fail(MOEQ_EALIGN, "%s: K=%lld must be a multiple of 128", fn, (long long)K);
+  if (N % 128 != 0) return fail(MOEQ_EALIGN, "%s: N=%lld must be a multiple of 128", fn, (long long)N);
+  if (a_row != MOEQ_AROW_TOKEN && a_row != MOEQ_AROW_SORTED) return fail(MOEQ_EINVAL, "%s: bad a_row %d", fn, a_row);
+  if (!a || !w || !offsets || !out) return fail(MOEQ_EINVAL, "%s: null pointer", fn);
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(out, 16) || !aligned(offsets, 4))
+    return fail(MOEQ_EALIGN, "%s: pointers must be 16-byte aligned", fn);
+  return MOEQ_OK;
+}
+
+moeq::GroupedArgs make_args(const int32_t* offsets, const int32_t* sorted, int64_t rows_a,
+                            moeq_arow a_row, int64_t P, int32_t topk, int32_t E, int64_t N,
+                            int64_t K, bool silu, moeq_dtype od, void* out, moeq_sched sched) {
+  moeq::GroupedArgs g;
+  g.offsets = offsets;
+  g.sorted_ids = sorted;
+  g.rows_a = rows_a;
+  g.a_sorted = (a_row == MOEQ_AROW_SORTED) ? 1 : 0;
+  g.topk = topk;
+  g.E = E;
+  g.P = P;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.silu_mul = silu ? 1 : 0;
+  g.out_kind = (int)od;
+  g.out = out;
+  g.sched = (int)sched;
+  g.num_cus = device_cus();
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moeq_last_error(void) { return g_err.c_str(); }
+
+int32_t moeq_abi_version(void) { return 1; }
+
+size_t moe_route_prep_workspace_bytes(int64_t T, int32_t topk, int32_t E) {
+  if (T < 0 || topk < 1 || E < 1) return 0;
+  return moeq::route_workspace_bytes(T * (int64_t)topk, E);
+}
+
+moeq_status moe_route_prep(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
+                           int32_t* expert_offsets, int32_t* sorted_pair_ids,
+                           int32_t* pair_to_sorted, int32_t* n_invalid, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_route_prep";
+  if (T < 0) return fail(MOEQ_EINVAL, "%s: T=%lld < 0", fn, (long long)T);
+  if (topk < 1 || topk > kMaxTopk) return fail(MOEQ_EINVAL, "%s: topk=%d outside [1, %d]", fn, topk, kMaxTopk);
+  if (E < 1 || E > kMaxE) return fail(MOEQ_EINVAL, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  const int64_t P = T * (int64_t)topk;
+  if (P >= (int64_t(1) << 31)) return fail(MOEQ_EINVAL, "%s: T*topk too large", fn);
+  if (!expert_offsets || !n_invalid || (P > 0 && (!topk_ids || !sorted_pair_ids || !pair_to_sorted)))
+    return fail(MOEQ_EINVAL, "%s: null pointer", fn);
+  if (!aligned(topk_ids, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_pair_ids, 4) ||
+      !aligned(pair_to_sorted, 4) || !aligned(n_invalid, 4) || !aligned(workspace, 4))
+    return fail(MOEQ_EALIGN, "%s: int32 arrays must be 4-byte aligned", fn);
+  const size_t need = moeq::route_workspace_bytes(P, E);
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(MOEQ_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
+  return hip_status(moeq::launch_route(topk_ids, (int)P, E, expert_offsets, sorted_pair_ids,
+                                       pair_to_sorted, n_invalid, workspace, (hipStream_t)stream),
+                    fn);
+}
+
+moeq_status grouped_gemm_qint4(const uint8_t* a, const float* a_scale, int64_t rows_a,
+                               moeq_arow a_row, const uint8_t* w, const float* w_scale,
+                               const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
+                               int64_t P, int32_t topk, int32_t E, int64_t N, int64_t K,
+                               moeq_act act, moeq_dtype out_dtype, void* out, moeq_sched sched,
+                               void* stream) {
+  const char* fn = "grouped_gemm_qint4";
+  moeq_status st = check_grouped(fn, a, rows_a, a_row, w, expert_offsets, P, topk, E, N, K, out);
+  if (st != MOEQ_OK) return st;
+  if (!a_scale || !w_scale) return fail(MOEQ_EINVAL, "%s: null scale pointer", fn);
+  if (!aligned(a_scale, 4) || !aligned(w_scale, 4)) return fail(MOEQ_EALIGN, "%s: scales must be 4-byte aligned", fn);
+  if (act != MOEQ_ACT_NONE && act != MOEQ_ACT_SILU_MUL) return fail(MOEQ_EUNSUPPORTED, "%s: act %d", fn, act);
+  if (out_dtype != MOEQ_F16 && out_dtype != MOEQ_BF16 && out_dtype != MOEQ_F32 && out_dtype != MOEQ_I32)
+    return fail(MOEQ_EUNSUPPORTED, "%s: out dtype %d", fn, out_dtype);
+  if (out_dtype == MOEQ_I32 && act != MOEQ_ACT_NONE)
+    return fail(MOEQ_EUNSUPPORTED, "%s: I32 output needs act NONE", fn);
+  if (a_row == MOEQ_AROW_TOKEN && !sorted_pair_ids && rows_a < P)
+    return fail(MOEQ_EINVAL, "%s: identity rows need rows_a >= P", fn);
+  if (sched < MOEQ_SCHED_AUTO || sched > MOEQ_SCHED_PREFILL) return fail(MOEQ_EINVAL, "%s: sched %d", fn, sched);
+  moeq::GroupedArgs g = make_args(expert_offsets, sorted_pair_ids, rows_a, a_row, P, topk, E, N, K,
+                                  act == MOEQ_ACT_SILU_MUL, out_dtype, out, sched);
+  return hip_status(moeq::launch_gemm_int4(g, a, a_scale, w, w_scale, (hipStream_t)stream), fn);
+}
+
+moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int64_t rows_a,
+                                    moeq_arow a_row, const uint8_t* w, const float* w_scale,
+                                    const int32_t* expert_offsets,
+                                    const int32_t* sorted_pair_ids, int64_t P, int32_t topk,
+                                    int32_t E, int64_t N, int64_t K, moeq_dtype out_dtype,
+                                    void* out, moeq_sched sched, void* stream) {
+  const char* fn = "grouped_gemm_qfp8_block";
+  moeq_status st = check_grouped(fn, a, rows_a, a_row, w, expert_offsets, P, topk, E, N, K, out);
+  if (st != MOEQ_OK) return st;
+  if (!a_scale || !w_scale) return fail(MOEQ_EINVAL, "%s: null scale pointer", fn);
+  if (!aligned(a_scale, 4) || !aligned(w_scale, 4)) return fail(MOEQ_EALIGN, "%s: scales must be 4-byte aligned", fn);
+  if (out_dtype != MOEQ_F16 && out_dtype != MOEQ_BF16 && out_dtype != MOEQ_F32)
+    return fail(MOEQ_EUNSUPPORTED, "%s: out dtype %d", fn, out_dtype);
+  if (a_row == MOEQ_AROW_TOKEN && !sorted_pair_ids && rows_a < P)
+    return fail(MOEQ_EINVAL, "%s: identity rows need rows_a >= P", fn);
+  if (sched < MOEQ_SCHED_AUTO || sched > MOEQ_SCHED_PREFILL) return fail(MOEQ_EINVAL, "%s: sched %d", fn, sched);
+  moeq::GroupedArgs g = make_args(expert_offsets, sorted_pair_ids, rows_a, a_row, P, topk, E, N, K,
+                                  false, out_dtype, out, sched);
+  return hip_status(moeq::launch_gemm_fp8(g, a, a_scale, w, w_scale, (hipStream_t)stream), fn);
+}
+
+moeq_status grouped_gemm_qnvfp4(const void* x, int64_t rows_a, moeq_arow a_row, const uint8_t* w,
+                                const uint8_t* w_sf, const float* w_gscale,
+                                const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
+                                int64_t P, int32_t topk, int32_t E, int64_t N, int64_t K,
+                                moeq_act act, moeq_dtype out_dtype, void* out,
+                                moeq_sched sched, void* stream) {
+  const char* fn = "grouped_gemm_qnvfp4";
+  moeq_status st = check_grouped(fn, x, rows_a, a_row, w, expert_offsets, P, topk, E, N, K, out);
+  if (st != MOEQ_OK) return st;
+  if (!w_sf || !w_gscale) return fail(MOEQ_EINVAL, "%s: null scale pointer", fn);
+  if (!aligned(w_sf, 16) || !aligned(w_gscale, 4)) return fail(MOEQ_EALIGN, "%s: scales misaligned", fn);
+  if (act != MOEQ_ACT_NONE && act != MOEQ_ACT_SILU_MUL) return fail(MOEQ_EUNSUPPORTED, "%s: act %d", fn, act);
+  if (out_dtype != MOEQ_F16 && out_dtype != MOEQ_BF16 && out_dtype != MOEQ_F32)
+    return fail(MOEQ_EUNSUPPORTED, "%s: out dtype %d", fn, out_dtype);
+  if (a_row == MOEQ_AROW_TOKEN && !sorted_pair_ids && rows_a < P)
+    return fail(MOEQ_EINVAL, "%s: identity rows need rows_a >= P", fn);
+  if (sched < MOEQ_SCHED_AUTO || sched > MOEQ_SCHED_PREFILL) return fail(MOEQ_EINVAL, "%s: sched %d", fn, sched);
+  moeq::GroupedArgs g = make_args(expert_offsets, sorted_pair_ids, rows_a, a_row, P, topk, E, N, K,
+                                  act == MOEQ_ACT_SILU_MUL, out_dtype, out, sched);
+  return hip_status(moeq::launch_gemm_nvfp4(g, static_cast<const uint16_t*>(x), w, w_sf, w_gscale,
+                                            (hipStream_t)stream),
+                    fn);
+}
+
+moeq_status moe_scatter_combine(const void* y, moeq_dtype y_dtype, const int32_t* pair_to_sorted,
+                                const float* topk_weights, int64_t T, int32_t topk, int64_t N,
+                                moeq_dtype out_dtype, void* out, void* stream) {
+  const char* fn = "moe_scatter_combine";
+  if (T < 0) return fail(MOEQ_EINVAL, "%s: T=%lld < 0", fn, (long long)T);
+  if (topk < 1 || topk > kMaxTopk) return fail(MOEQ_EINVAL, "%s: topk=%d outside [1, %d]", fn, topk, kMaxTopk);
+  if (N <= 0 || N > (1 << 24)) return fail(MOEQ_EINVAL, "%s: N=%lld out of range", fn, (long long)N);
+  if (N % 8 != 0) return fail(MOEQ_EALIGN, "%s: N=%lld must be a multiple of 8", fn, (long long)N);
+  if (T * (int64_t)topk >= (int64_t(1) << 31)) return fail(MOEQ_EINVAL, "%s: T*topk too large", fn);
+  if (y_dtype != MOEQ_F16 && y_dtype != MOEQ_BF16 && y_dtype != MOEQ_F32)
+    return fail(MOEQ_EUNSUPPORTED, "%s: y dtype %d", fn, y_dtype);
+  if (out_dtype != MOEQ_F16 && out_dtype != MOEQ_BF16 && out_dtype != MOEQ_F32)
+    return fail(MOEQ_EUNSUPPORTED, "%s: out dtype %d", fn, out_dtype);
+  if (T > 0 && (!y || !pair_to_sorted || !topk_weights || !out)) return fail(MOEQ_EINVAL, "%s: null pointer", fn);
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(pair_to_sorted, 4) || !aligned(topk_weights, 4))
+    return fail(MOEQ_EALIGN, "%s: pointers misaligned", fn);
+  return hip_status(moeq::launch_combine(y, (int)y_dtype, pair_to_sorted, topk_weights, (int)T, topk,
+                                         (int)N, T * (int64_t)topk, (int)out_dtype, out,
+                                         (hipStream_t)stream),
+                    fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,34 @@
+// NVFP4 weight decode shared by the NVFP4 schedules.
+//
+// An E2M1 code times its UE4M3 block scale is always a bf16 value (every
+// product of the 16 E2M1 values and the 127 non-negative finite e4m3 values
+// fits in 8 significant bits), so dequantization is exact: each byte (two
+// E2M1 codes, element 2b in the low nibble) is widened to two fp32 values by
+// the gfx950 conversion (scale operand 2^0), multiplied by the block scale
+// in fp32 (exact) and packed to bf16 (exact, no rounding happens).
+#pragma once
+
+#include "common.h"
+
+namespace moeq {
+
+// Two E2M1 codes in byte `sel` of `word` -> fp32 pair (low nibble first).
+template <int SEL>
+__device__ __forceinline__ v2f e2m1x2_f32(u32 word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
+}
+
+__device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
+  return (u32)f32_to_bf16_bits(lo) | ((u32)f32_to_bf16_bits(hi) << 16);
+}
+
+// 8 E2M1 codes (one 32-bit word, elements 0..7) times `scale` -> 8 bf16 as
+// four packed 32-bit words, in element order.
+__device__ __forceinline__ uint4 dequant8_bf16(u32 word, float scale) {
+  const v2f p0 = e2m1x2_f32<0>(word), p1 = e2m1x2_f32<1>(word);
+  const v2f p2 = e2m1x2_f32<2>(word), p3 = e2m1x2_f32<3>(word);
+  return make_uint4(pack_bf16x2(p0.x * scale, p0.y * scale), pack_bf16x2(p1.x * scale, p1.y * scale),
+                    pack_bf16x2(p2.x * scale, p2.y * scale), pack_bf16x2(p3.x * scale, p3.y * scale));
+}
+
+}  // namespace moeq

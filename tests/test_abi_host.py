@@ -1,0 +1,153 @@
+"""C-ABI library: it loads, exports every function include/moeq.h declares,
+and rejects bad arguments on the host with the documented status before any
+HIP call (these tests need no GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import quantized_moe_grouped_route_amd as mq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moeq.h")
+
+# Fake device addresses: only their values are inspected on these paths.
+A16 = 0x10000
+ODD = 0x10001
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                          text, flags=re.M))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mq.LIB_PATH):
+        pytest.skip("libmoeq.so not built")
+    return mq.lib()
+
+
+def test_header_declares_the_five_entry_points():
+    fns = declared_functions()
+    for f in ("moe_route_prep", "grouped_gemm_qint4", "grouped_gemm_qfp8_block",
+              "grouped_gemm_qnvfp4", "moe_scatter_combine", "moeq_last_error",
+              "moe_route_prep_workspace_bytes", "moeq_abi_version"):
+        assert f in fns
+    assert set(mq.EXPORTS) == fns
+
+
+def test_library_exports_every_declared_symbol(L):
+    raw = C.CDLL(mq.LIB_PATH)
+    for f in declared_functions():
+        assert hasattr(raw, f), f
+    assert L.moeq_abi_version() == 1
+
+
+def test_workspace_bytes(L):
+    assert L.moe_route_prep_workspace_bytes(64, 2, 4) == 0          # one chunk: fused kernel
+    assert L.moe_route_prep_workspace_bytes(4096, 8, 256) == 32 * 257 * 4
+    assert L.moe_route_prep_workspace_bytes(-1, 2, 4) == 0
+
+
+def _route(L, T=4, topk=2, E=4, ids=A16, offs=A16, srt=A16, p2s=A16, ninv=A16, ws=None, wsb=0):
+    return L.moe_route_prep(ids, T, topk, E, offs, srt, p2s, ninv, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), mq.EINVAL), (dict(topk=0), mq.EINVAL), (dict(topk=65), mq.EINVAL),
+    (dict(E=0), mq.EINVAL), (dict(E=1025), mq.EINVAL), (dict(ids=None), mq.EINVAL),
+    (dict(offs=None), mq.EINVAL), (dict(srt=ODD), mq.EALIGN),
+    (dict(T=5000, topk=8, E=16), mq.EINVAL),            # needs a workspace
+    (dict(T=2 ** 28, topk=8), mq.EINVAL),               # T*topk >= 2^31
+])
+def test_route_prep_rejects(L, kw, status):
+    assert _route(L, **kw) == status
+    assert L.moeq_last_error()
+
+
+def _int4(L, **kw):
+    a = dict(a=A16, sa=A16, rows=16, arow=0, w=A16, sw=A16, off=A16, srt=A16, P=16, topk=2, E=4,
+             N=256, K=256, act=0, od=mq.F16, out=A16, sched=0)
+    a.update(kw)
+    return L.grouped_gemm_qint4(a["a"], a["sa"], a["rows"], a["arow"], a["w"], a["sw"], a["off"],
+                                a["srt"], a["P"], a["topk"], a["E"], a["N"], a["K"], a["act"],
+                                a["od"], a["out"], a["sched"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=192), mq.EALIGN), (dict(N=96), mq.EALIGN), (dict(E=0), mq.EINVAL),
+    (dict(E=2000), mq.EINVAL), (dict(topk=0), mq.EINVAL), (dict(P=-1), mq.EINVAL),
+    (dict(a=None), mq.EINVAL), (dict(w=ODD), mq.EALIGN), (dict(out=ODD), mq.EALIGN),
+    (dict(sa=None), mq.EINVAL), (dict(act=7), mq.EUNSUPPORTED), (dict(od=9), mq.EUNSUPPORTED),
+    (dict(od=mq.I32, act=1), mq.EUNSUPPORTED), (dict(arow=5), mq.EINVAL),
+    (dict(srt=None, rows=8, P=16), mq.EINVAL), (dict(sched=9), mq.EINVAL),
+    (dict(rows=0), mq.EINVAL), (dict(K=1 << 18), mq.EINVAL),
+])
+def test_int4_rejects(L, kw, status):
+    assert _int4(L, **kw) == status
+
+
+def _fp8(L, **kw):
+    a = dict(a=A16, sa=A16, rows=16, arow=0, w=A16, sw=A16, off=A16, srt=A16, P=16, topk=1, E=1,
+             N=256, K=256, od=mq.BF16, out=A16, sched=0)
+    a.update(kw)
+    return L.grouped_gemm_qfp8_block(a["a"], a["sa"], a["rows"], a["arow"], a["w"], a["sw"],
+                                     a["off"], a["srt"], a["P"], a["topk"], a["E"], a["N"], a["K"],
+                                     a["od"], a["out"], a["sched"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=64), mq.EALIGN), (dict(N=64), mq.EALIGN), (dict(od=mq.I32), mq.EUNSUPPORTED),
+    (dict(sw=None), mq.EINVAL), (dict(sa=ODD), mq.EALIGN), (dict(off=None), mq.EINVAL),
+])
+def test_fp8_rejects(L, kw, status):
+    assert _fp8(L, **kw) == status
+
+
+def _nvfp4(L, **kw):
+    a = dict(x=A16, rows=16, arow=0, w=A16, sf=A16, gs=A16, off=A16, srt=A16, P=16, topk=2, E=4,
+             N=256, K=256, act=0, od=mq.BF16, out=A16, sched=0)
+    a.update(kw)
+    return L.grouped_gemm_qnvfp4(a["x"], a["rows"], a["arow"], a["w"], a["sf"], a["gs"], a["off"],
+                                 a["srt"], a["P"], a["topk"], a["E"], a["N"], a["K"], a["act"],
+                                 a["od"], a["out"], a["sched"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=96), mq.EALIGN), (dict(N=32), mq.EALIGN), (dict(sf=ODD), mq.EALIGN),
+    (dict(gs=None), mq.EINVAL), (dict(od=mq.I32), mq.EUNSUPPORTED), (dict(act=3), mq.EUNSUPPORTED),
+    (dict(x=None), mq.EINVAL),
+])
+def test_nvfp4_rejects(L, kw, status):
+    assert _nvfp4(L, **kw) == status
+
+
+def _combine(L, **kw):
+    a = dict(y=A16, yd=mq.BF16, p2s=A16, tw=A16, T=8, topk=2, N=256, od=mq.BF16, out=A16)
+    a.update(kw)
+    return L.moe_scatter_combine(a["y"], a["yd"], a["p2s"], a["tw"], a["T"], a["topk"], a["N"],
+                                 a["od"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=12), mq.EALIGN), (dict(T=-2), mq.EINVAL), (dict(topk=0), mq.EINVAL),
+    (dict(yd=mq.I32), mq.EUNSUPPORTED), (dict(od=7), mq.EUNSUPPORTED), (dict(y=None), mq.EINVAL),
+    (dict(out=ODD), mq.EALIGN),
+])
+def test_combine_rejects(L, kw, status):
+    assert _combine(L, **kw) == status
+
+
+def test_error_text_names_the_call(L):
+    assert _int4(L, K=192) == mq.EALIGN
+    assert b"grouped_gemm_qint4" in L.moeq_last_error() and b"K=192" in L.moeq_last_error()
+
+
+def test_binding_raises_without_gpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        mq.moe_route_prep(torch.zeros(4, 2, dtype=torch.int32), 4)

@@ -1,0 +1,234 @@
+"""GPU parity: every entry point of the HIP library against the CPU oracle on
+the same seeded inputs.  Tables and integer accumulators must be equal;
+floating outputs must satisfy max_j |gpu - oracle| <= 2e-3 * ||oracle_row||_2
+per row."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import dev, host, bf16_bits, assert_rows_close
+
+pytestmark = pytest.mark.gpu
+
+mq = pytest.importorskip("quantized_moe_grouped_route_amd")
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mq.lib()
+
+
+def _route_gpu(ids, E):
+    offs, srt, p2s, ninv = mq.moe_route_prep(dev(ids.astype(np.int32)), E)
+    return host(offs), host(srt), host(p2s), int(host(ninv)[0])
+
+
+# ------------------------------------------------------------------ route
+ROUTE_CASES = [
+    ("tiny", lambda r: synth.distinct_uniform_ids(r, 5, 2, 4), 4),
+    ("repeats", lambda r: synth.uniform_ids_with_repeats(r, 300, 3, 7), 7),
+    ("minus1_and_invalid", lambda r: np.where(r.random((333, 3)) < 0.2, -1,
+                                              r.integers(-3, 12, size=(333, 3))).astype(np.int32), 9),
+    ("E1", lambda r: np.zeros((1024, 1), np.int32), 1),
+    ("T0", lambda r: np.zeros((0, 2), np.int32), 4),
+    ("all_minus1", lambda r: -np.ones((70, 2), np.int32), 3),
+    ("multi_chunk", lambda r: synth.uniform_ids_with_repeats(r, 1500, 4, 33), 33),
+    ("multi_chunk_ragged", lambda r: np.where(r.random((2049, 3)) < 0.1, -1,
+                                              synth.uniform_ids_with_repeats(r, 2049, 3, 5)), 5),
+    ("E1024", lambda r: synth.uniform_ids_with_repeats(r, 700, 8, 1024), 1024),
+    ("zipf_T4096", lambda r: synth.zipf_ids(r, 4096, 8, 256), 256),
+    ("mixtral_T8192", lambda r: synth.distinct_uniform_ids(r, 8192, 2, 8), 8),
+    ("decode_T8", lambda r: synth.distinct_uniform_ids(r, 8, 8, 256), 256),
+]
+
+
+@pytest.mark.parametrize("name,make,E", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+def test_route_prep_exact(name, make, E):
+    ids = make(np.random.default_rng(11)).astype(np.int32)
+    ref = oracle.route_prep(ids, E)
+    got = _route_gpu(ids, E) if ids.size else None
+    if ids.size == 0:
+        offs, srt, p2s, ninv = mq.moe_route_prep(torch.zeros((0, ids.shape[1]), dtype=torch.int32,
+                                                             device="cuda"), E)
+        assert host(offs).tolist() == [0] * (E + 1) and int(host(ninv)[0]) == 0
+        return
+    for g, r in zip(got[:3], ref[:3]):
+        assert np.array_equal(g, r)
+    assert got[3] == ref[3]
+
+
+# ------------------------------------------------------------------ combine
+@pytest.mark.parametrize("ydt,odt", [(torch.bfloat16, torch.bfloat16), (torch.float16, torch.float16),
+                                     (torch.float32, torch.float32), (torch.float32, torch.bfloat16)])
+def test_combine(ydt, odt):
+    rng = np.random.default_rng(5)
+    T, k, E, N = 97, 4, 6, 520
+    ids = synth.uniform_ids_with_repeats(rng, T, k, E)
+    ids[3] = -1
+    ids[10, 2] = -1
+    w = synth.softmax_weights(rng, T, k)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(ids), E)
+    y = torch.randn(T * k, N, device="cuda").to(ydt)
+    out = mq.moe_scatter_combine(y, p2s, dev(w), out_dtype=odt)
+    ref = oracle.scatter_combine(host(y), host(p2s), w)
+    assert_rows_close(host(out), ref, what="combine")
+    assert torch.all(out[3] == 0)
+
+
+# ------------------------------------------------------------------ INT4
+def _int4_case(seed, T, E, k, N, K, routing="distinct"):
+    d = synth.int4_moe(seed, T, E, k, N, K, routing=routing)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    return d, offs, srt, p2s
+
+
+@pytest.mark.parametrize("T,E,k,N,K", [(300, 5, 2, 384, 512), (64, 4, 2, 256, 256),
+                                       (37, 3, 3, 128, 128), (5, 8, 2, 256, 384)])
+def test_int4_raw_accumulator_bit_exact(T, E, k, N, K):
+    d, offs, srt, p2s = _int4_case(21, T, E, k, N, K, routing="repeat")
+    acc = mq.grouped_gemm_qint4(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]),
+                                offs, srt, k, out_dtype=torch.int32)
+    ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"],
+                                    host(offs), host(srt), k)
+    n = int(host(offs)[-1])
+    assert np.array_equal(host(acc)[:n], ref["acc"])
+
+
+@pytest.mark.parametrize("odt", [torch.float16, torch.bfloat16, torch.float32])
+def test_int4_scaled(odt):
+    d, offs, srt, p2s = _int4_case(22, 300, 5, 2, 384, 512)
+    y = mq.grouped_gemm_qint4(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]),
+                              offs, srt, 2, out_dtype=odt)
+    ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"],
+                                    host(offs), host(srt), 2)
+    assert_rows_close(host(y)[: ref["y"].shape[0]], ref["y"], what="int4")
+
+
+def test_int4_silu_mul_and_sorted_rows():
+    d, offs, srt, p2s = _int4_case(23, 200, 4, 2, 512, 256)
+    h = mq.grouped_gemm_qint4(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]),
+                              offs, srt, 2, act="silu_mul", out_dtype=torch.float16)
+    ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"],
+                                    host(offs), host(srt), 2, act="silu_mul")
+    assert_rows_close(host(h)[: ref["y"].shape[0]], ref["y"], what="int4 silu")
+    # SORTED rows: A already in sorted order
+    rng = np.random.default_rng(3)
+    P = 400
+    a2 = synth.uniform_bytes(rng, (P, 128))
+    s2 = synth.uniform_f32(rng, (P,), 0.005, 0.05)
+    y2 = mq.grouped_gemm_qint4(dev(a2), dev(s2), dev(d["w"][:, :, :128].copy()),
+                               dev(d["w_scale"]), offs, srt, 2, a_row="sorted",
+                               out_dtype=torch.int32)
+    ref2 = oracle.grouped_gemm_qint4(a2, s2, "sorted", d["w"][:, :, :128], d["w_scale"],
+                                     host(offs), host(srt), 2)
+    assert np.array_equal(host(y2)[: ref2["acc"].shape[0]], ref2["acc"])
+
+
+def test_int4_rows_past_offsets_untouched_and_empty_experts():
+    T, E, k, N, K = 50, 6, 2, 256, 256
+    d = synth.int4_moe(24, T, E, k, N, K)
+    d["topk_ids"][d["topk_ids"] >= 3] = -1          # experts 3..5 empty, some pairs skipped
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    n = int(host(offs)[-1])
+    out = torch.full((T * k, N), 12345, dtype=torch.int32, device="cuda")
+    mq.grouped_gemm_qint4(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]),
+                          offs, srt, k, out_dtype=torch.int32, out=out)
+    assert torch.all(out[n:] == 12345)
+    ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"],
+                                    host(offs), host(srt), k)
+    assert np.array_equal(host(out)[:n], ref["acc"])
+
+
+def test_int4_extreme_codes():
+    # all codes -8: acc = 64*K per element, the largest magnitude
+    T, E, N, K = 40, 2, 128, 4096
+    ids = np.zeros((T, 1), np.int32)
+    ids[::2] = 1
+    a = np.full((T, K // 2), 0x88, np.uint8)
+    w = np.full((E, N, K // 2), 0x88, np.uint8)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(ids), E)
+    acc = mq.grouped_gemm_qint4(dev(a), dev(np.ones(T, np.float32)), dev(w),
+                                dev(np.ones((E, N), np.float32)), offs, srt, 1,
+                                out_dtype=torch.int32)
+    assert torch.all(acc == 64 * K)
+
+
+# ------------------------------------------------------------------ FP8
+@pytest.mark.parametrize("M,N,K", [(300, 256, 512), (128, 128, 128), (1, 384, 256)])
+def test_fp8_dense(M, N, K):
+    d = synth.fp8_block(31, M, N, K)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), 1)
+    y = mq.grouped_gemm_qfp8_block(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]),
+                                   offs, srt, 1, out_dtype=torch.float32)
+    ref = oracle.fp8_dense(d)
+    assert_rows_close(host(y), ref, what="fp8")
+
+
+def test_fp8_routed_scales_vary_on_every_index():
+    rng = np.random.default_rng(9)
+    d = synth.fp8_block(32, 0, 256, 384, E=3, T=150, k=2)
+    d["a_scale"] = synth.uniform_f32(rng, d["a_scale"].shape, 0.25, 4.0)
+    d["w_scale"] = synth.uniform_f32(rng, d["w_scale"].shape, 0.25, 4.0)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), 3)
+    y = mq.grouped_gemm_qfp8_block(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]),
+                                   offs, srt, 2, out_dtype=torch.bfloat16)
+    ref = oracle.grouped_gemm_qfp8_block(d["a"], d["a_scale"], "token", d["w"], d["w_scale"],
+                                         host(offs), host(srt), 2)["y"]
+    assert_rows_close(host(y)[: ref.shape[0]], ref, what="fp8 routed")
+
+
+# ------------------------------------------------------------------ NVFP4
+@pytest.mark.parametrize("sched", ["prefill", "decode"])
+@pytest.mark.parametrize("act", ["none", "silu_mul"])
+def test_nvfp4(sched, act):
+    T, E, k, H, I = 150, 5, 2, 256, 128
+    d = synth.nvfp4_moe(41, T, E, k, H, I, routing="repeat")
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    y = mq.grouped_gemm_qnvfp4(dev(d["x"]), dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k,
+                               act=act, out_dtype=torch.float32, sched=sched)
+    ref = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], host(offs),
+                                     host(srt), k, act=act)["y"]
+    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 {sched} {act}")
+
+
+@pytest.mark.parametrize("sched", ["prefill", "decode"])
+def test_nvfp4_sorted_rows_full_code_range(sched):
+    # every scale byte 0x00..0x7E occurs; SORTED activation rows
+    T, E, k, H, I = 64, 3, 2, 512, 128
+    d = synth.nvfp4_moe(42, T, E, k, H, I, scale_lo=0x00, scale_hi=0x7E)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    P = T * k
+    xs = synth.normal_bf16(np.random.default_rng(1), (P, I))
+    y = mq.grouped_gemm_qnvfp4(dev(xs), dev(d["w2"]), dev(d["s2"]), dev(d["g2"]), offs, srt, k,
+                               a_row="sorted", out_dtype=torch.float32, sched=sched)
+    ref = oracle.grouped_gemm_qnvfp4(xs, "sorted", d["w2"], d["s2"], d["g2"], host(offs),
+                                     host(srt), k)["y"]
+    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 sorted {sched}")
+
+
+def test_both_schedules_meet_tolerance():
+    # decode and prefill both sum exact bf16 products in fp32; they may round
+    # differently, but both must meet the tolerance on the same input.
+    T, E, k, H, I = 24, 4, 2, 256, 128
+    d = synth.nvfp4_moe(43, T, E, k, H, I)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    ys = [host(mq.grouped_gemm_qnvfp4(dev(d["x"]), dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs,
+                                      srt, k, out_dtype=torch.float32, sched=s))
+          for s in ("prefill", "decode")]
+    ref = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], host(offs),
+                                     host(srt), k)["y"]
+    for y in ys:
+        assert_rows_close(y[: ref.shape[0]], ref, what="nvfp4 schedules")
+
+
+def test_repeat_runs_bitwise_identical():
+    d = synth.nvfp4_moe(44, 100, 4, 2, 256, 128)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), 4)
+    args = (dev(d["x"]), dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, 2)
+    a = mq.grouped_gemm_qnvfp4(*args, act="silu_mul")
+    b = mq.grouped_gemm_qnvfp4(*args, act="silu_mul")
+    assert torch.equal(a, b)
