@@ -17,6 +17,12 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned u32;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte loads and stores through native vector types (arrays of these
+// stay in registers; arrays of HIP's uint4 struct can end up in scratch).
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 constexpr int kWave = 64;
 

@@ -16,7 +16,7 @@ namespace moeq {
 namespace {
 
 template <int OUT>
-__global__ __launch_bounds__(kThreadsT) void fp8_prefill(
+__global__ __launch_bounds__(kThreadsT, 1) void fp8_prefill(
     const uint8_t* __restrict__ a, const float* __restrict__ a_scale, int64_t rows_a, int a_sorted,
     const uint8_t* __restrict__ w, const float* __restrict__ w_scale,
     const int* __restrict__ offsets, const int* __restrict__ sorted_ids, int topk, int E, int P, int N,
@@ -59,12 +59,12 @@ __global__ __launch_bounds__(kThreadsT) void fp8_prefill(
 #pragma unroll
       for (int y = 0; y < 2; ++y) acc[x][y] = v16f{};
 
-    uint4 ra[4], rb[4];
+    u32x4 ra[4], rb[4];
     float rsa = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ra[i] = *reinterpret_cast<const uint4*>(pa[i]);
-      rb[i] = *reinterpret_cast<const uint4*>(pb[i]);
+      ra[i] = ld16(pa[i]);
+      rb[i] = ld16(pb[i]);
     }
     if (tid < kTileM) rsa = a_scale[sa_row];
 
@@ -72,8 +72,8 @@ __global__ __launch_bounds__(kThreadsT) void fp8_prefill(
       __syncthreads();  // previous step's fragment reads are done
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<uint4*>(lds_a + (lrow + 32 * i) * kPitch + lchunk) = ra[i];
-        *reinterpret_cast<uint4*>(lds_b + (lrow + 32 * i) * kPitch + lchunk) = rb[i];
+        st16(lds_a + (lrow + 32 * i) * kPitch + lchunk, ra[i]);
+        st16(lds_b + (lrow + 32 * i) * kPitch + lchunk, rb[i]);
       }
       if (tid < kTileM) lds_sa[tid] = rsa;
       const float sb = sb_ptr[g];
@@ -82,8 +82,8 @@ __global__ __launch_bounds__(kThreadsT) void fp8_prefill(
         const int64_t off = (int64_t)(g + 1) * 128;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          ra[i] = *reinterpret_cast<const uint4*>(pa[i] + off);
-          rb[i] = *reinterpret_cast<const uint4*>(pb[i] + off);
+          ra[i] = ld16(pa[i] + off);
+          rb[i] = ld16(pb[i] + off);
         }
         if (tid < kTileM) rsa = a_scale[(int64_t)(g + 1) * rows_a + sa_row];
       }
@@ -100,16 +100,12 @@ __global__ __launch_bounds__(kThreadsT) void fp8_prefill(
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
           const uint8_t* p = lds_a + (64 * wm + 32 * x + (lane & 31)) * kPitch + koff;
-          const uint4 lo = *reinterpret_cast<const uint4*>(p);
-          const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
-          fa[x] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          fa[x] = *reinterpret_cast<const v8i*>(p);
         }
 #pragma unroll
         for (int y = 0; y < 2; ++y) {
           const uint8_t* p = lds_b + (b_lds_row(false, wn, y) + (lane & 31)) * kPitch + koff;
-          const uint4 lo = *reinterpret_cast<const uint4*>(p);
-          const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
-          fb[y] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          fb[y] = *reinterpret_cast<const v8i*>(p);
         }
 #pragma unroll
         for (int x = 0; x < 2; ++x)

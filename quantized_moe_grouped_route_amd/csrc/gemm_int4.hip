@@ -17,10 +17,9 @@
 namespace moeq {
 namespace {
 
-__device__ __forceinline__ void split_nibbles(uint4 p, uint4& lo, uint4& hi) {
-  lo = make_uint4((p.x << 4) & 0xF0F0F0F0u, (p.y << 4) & 0xF0F0F0F0u, (p.z << 4) & 0xF0F0F0F0u,
-                  (p.w << 4) & 0xF0F0F0F0u);
-  hi = make_uint4(p.x & 0xF0F0F0F0u, p.y & 0xF0F0F0F0u, p.z & 0xF0F0F0F0u, p.w & 0xF0F0F0F0u);
+__device__ __forceinline__ void split_nibbles(u32x4 p, u32x4& lo, u32x4& hi) {
+  lo = (p << 4) & 0xF0F0F0F0u;
+  hi = p & 0xF0F0F0F0u;
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
@@ -29,7 +28,7 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g));
 // memory (thread t: row t/4 + 64i, bytes (t%4)*16, i = 0, 1), widened to
 // 128 int8 bytes per row in LDS.
 template <int OUT, bool SILU>
-__global__ __launch_bounds__(kThreadsT) void int4_prefill(
+__global__ __launch_bounds__(kThreadsT, 1) void int4_prefill(
     const uint8_t* __restrict__ a, const float* __restrict__ a_scale, int64_t rows_a, int a_sorted,
     const uint8_t* __restrict__ w, const float* __restrict__ w_scale,
     const int* __restrict__ offsets, const int* __restrict__ sorted_ids, int topk, int E, int P, int N,
@@ -72,33 +71,33 @@ __global__ __launch_bounds__(kThreadsT) void int4_prefill(
 #pragma unroll
       for (int y = 0; y < 2; ++y) acc[x][y] = v16i{};
 
-    uint4 ra[2], rb[2];
+    u32x4 ra[2], rb[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      ra[i] = *reinterpret_cast<const uint4*>(pa[i]);
-      rb[i] = *reinterpret_cast<const uint4*>(pb[i]);
+      ra[i] = ld16(pa[i]);
+      rb[i] = ld16(pb[i]);
     }
     for (int st = 0; st < steps; ++st) {
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        uint4 lo, hi;
+        u32x4 lo, hi;
         uint8_t* da = lds_a + (lrow + 64 * i) * kPitch + 2 * lchunk;
         split_nibbles(ra[i], lo, hi);
-        *reinterpret_cast<uint4*>(da) = lo;
-        *reinterpret_cast<uint4*>(da + 16) = hi;
+        st16(da, lo);
+        st16(da + 16, hi);
         uint8_t* db = lds_b + (lrow + 64 * i) * kPitch + 2 * lchunk;
         split_nibbles(rb[i], lo, hi);
-        *reinterpret_cast<uint4*>(db) = lo;
-        *reinterpret_cast<uint4*>(db + 16) = hi;
+        st16(db, lo);
+        st16(db + 16, hi);
       }
       __syncthreads();
       if (st + 1 < steps) {
         const int64_t off = (int64_t)(st + 1) * 64;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          ra[i] = *reinterpret_cast<const uint4*>(pa[i] + off);
-          rb[i] = *reinterpret_cast<const uint4*>(pb[i] + off);
+          ra[i] = ld16(pa[i] + off);
+          rb[i] = ld16(pb[i] + off);
         }
       }
 #pragma unroll
@@ -107,13 +106,11 @@ __global__ __launch_bounds__(kThreadsT) void int4_prefill(
         v4i fa[2], fb[2];
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-          const uint4 v = *reinterpret_cast<const uint4*>(lds_a + (64 * wm + 32 * x + (lane & 31)) * kPitch + koff);
-          fa[x] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+          fa[x] = *reinterpret_cast<const v4i*>(lds_a + (64 * wm + 32 * x + (lane & 31)) * kPitch + koff);
         }
 #pragma unroll
         for (int y = 0; y < 2; ++y) {
-          const uint4 v = *reinterpret_cast<const uint4*>(lds_b + (b_lds_row(SILU, wn, y) + (lane & 31)) * kPitch + koff);
-          fb[y] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+          fb[y] = *reinterpret_cast<const v4i*>(lds_b + (b_lds_row(SILU, wn, y) + (lane & 31)) * kPitch + koff);
         }
 #pragma unroll
         for (int x = 0; x < 2; ++x)

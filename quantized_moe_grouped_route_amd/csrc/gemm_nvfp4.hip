@@ -29,7 +29,7 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g));
 // t/2, packed bytes (t%2)*16 = 32 codes = 2 scale blocks), dequantized to
 // 128 bytes of bf16 per row in LDS.
 template <int OUT, bool SILU>
-__global__ __launch_bounds__(kThreadsT) void nvfp4_prefill(
+__global__ __launch_bounds__(kThreadsT, 1) void nvfp4_prefill(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale,
     const int* __restrict__ offsets, const int* __restrict__ sorted_ids, int topk, int E, int P, int N,
@@ -70,32 +70,32 @@ __global__ __launch_bounds__(kThreadsT) void nvfp4_prefill(
 #pragma unroll
       for (int q = 0; q < 2; ++q) acc[p][q] = v16f{};
 
-    uint4 ra[4], rw;
+    u32x4 ra[4], rw;
     uint32_t rs;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const uint4*>(pa[i]);
-    rw = *reinterpret_cast<const uint4*>(pw);
+    for (int i = 0; i < 4; ++i) ra[i] = ld16(pa[i]);
+    rw = ld16(pw);
     rs = *reinterpret_cast<const uint16_t*>(ps);
 
     for (int st = 0; st < steps; ++st) {
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint4*>(lds_a + (arow + 32 * i) * kPitch + achunk) = ra[i];
+        st16(lds_a + (arow + 32 * i) * kPitch + achunk, ra[i]);
       {
         const float s0 = e4m3_to_f32(rs & 0xffu), s1 = e4m3_to_f32((rs >> 8) & 0xffu);
         uint8_t* db = lds_b + brow * kPitch + bhalf * 64;
-        *reinterpret_cast<uint4*>(db) = dequant8_bf16(rw.x, s0);
-        *reinterpret_cast<uint4*>(db + 16) = dequant8_bf16(rw.y, s0);
-        *reinterpret_cast<uint4*>(db + 32) = dequant8_bf16(rw.z, s1);
-        *reinterpret_cast<uint4*>(db + 48) = dequant8_bf16(rw.w, s1);
+        st16(db, dequant8_bf16(rw.x, s0));
+        st16(db + 16, dequant8_bf16(rw.y, s0));
+        st16(db + 32, dequant8_bf16(rw.z, s1));
+        st16(db + 48, dequant8_bf16(rw.w, s1));
       }
       __syncthreads();
       if (st + 1 < steps) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          ra[i] = *reinterpret_cast<const uint4*>(pa[i] + (int64_t)(st + 1) * 128);
-        rw = *reinterpret_cast<const uint4*>(pw + (int64_t)(st + 1) * 32);
+          ra[i] = ld16(pa[i] + (int64_t)(st + 1) * 128);
+        rw = ld16(pw + (int64_t)(st + 1) * 32);
         rs = *reinterpret_cast<const uint16_t*>(ps + (int64_t)(st + 1) * 4);
       }
 #pragma unroll
@@ -196,18 +196,16 @@ __global__ __launch_bounds__(256) void nvfp4_decode(
 
     v4f acc = v4f{};
     for (int c = 0; c < chunks; ++c) {
-      const v4i wv4 = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(pw + (int64_t)c * 64));
-      const uint4 wq = make_uint4((u32)wv4[0], (u32)wv4[1], (u32)wv4[2], (u32)wv4[3]);
+      const u32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pw + (int64_t)c * 64));
       const uint32_t sq = *reinterpret_cast<const uint16_t*>(ps + (int64_t)c * 8);
       const float s0 = e4m3_to_f32(sq & 0xffu), s1 = e4m3_to_f32(sq >> 8);
-      uint4 xa[4];
+      u32x4 xa[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        xa[i] = has_row ? *reinterpret_cast<const uint4*>(px + (int64_t)c * 256 + i * 16) : make_uint4(0, 0, 0, 0);
-      const u32 wq4[4] = {wq.x, wq.y, wq.z, wq.w};
+        xa[i] = has_row ? ld16(px + (int64_t)c * 256 + i * 16) : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint4 wd = dequant8_bf16(wq4[i], i < 2 ? s0 : s1);
+        const u32x4 wd = dequant8_bf16(wq[i], i < 2 ? s0 : s1);
         acc = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, wd), __builtin_bit_cast(v8bf, xa[i]), acc);
       }
     }

@@ -24,11 +24,11 @@ __device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
 
 // 8 E2M1 codes (one 32-bit word, elements 0..7) times `scale` -> 8 bf16 as
 // four packed 32-bit words, in element order.
-__device__ __forceinline__ uint4 dequant8_bf16(u32 word, float scale) {
+__device__ __forceinline__ u32x4 dequant8_bf16(u32 word, float scale) {
   const v2f p0 = e2m1x2_f32<0>(word), p1 = e2m1x2_f32<1>(word);
   const v2f p2 = e2m1x2_f32<2>(word), p3 = e2m1x2_f32<3>(word);
-  return make_uint4(pack_bf16x2(p0.x * scale, p0.y * scale), pack_bf16x2(p1.x * scale, p1.y * scale),
-                    pack_bf16x2(p2.x * scale, p2.y * scale), pack_bf16x2(p3.x * scale, p3.y * scale));
+  return u32x4{pack_bf16x2(p0.x * scale, p0.y * scale), pack_bf16x2(p1.x * scale, p1.y * scale),
+               pack_bf16x2(p2.x * scale, p2.y * scale), pack_bf16x2(p3.x * scale, p3.y * scale)};
 }
 
 }  // namespace moeq

@@ -1,0 +1,120 @@
+"""Parity at the five workloads' full sizes, in the launch configuration the
+benchmark times (bench.Workload issues the calls).  Route tables must be
+equal; expert outputs are checked on sampled rows that the oracle computes
+one by one; the combine is checked in full against the oracle applied to the
+GPU's own expert rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import host, bf16_bits, assert_rows_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run(idx):
+    import bench
+    wl = bench.Workload(idx)
+    wl.step()
+    torch.cuda.synchronize()
+    return wl
+
+
+def _check_route(wl):
+    offs, srt, p2s, ninv = (host(t) for t in wl.route_out)
+    ref = oracle.route_prep(wl.d["topk_ids"], wl.E)
+    assert np.array_equal(offs, ref[0]) and np.array_equal(srt, ref[1]) and np.array_equal(p2s, ref[2])
+    assert int(ninv[0]) == ref[3] == 0
+    return ref
+
+
+def _sample_rows(offs, n_per=2, max_experts=6, seed=0):
+    """A few sorted rows from the largest, the smallest and random non-empty experts."""
+    rng = np.random.default_rng(seed)
+    sizes = np.diff(offs)
+    ne = np.nonzero(sizes)[0]
+    order = ne[np.argsort(sizes[ne])]
+    pick = list(dict.fromkeys([order[-1], order[0]] + list(rng.permutation(ne)[: max_experts - 2])))
+    rows = []
+    for e in pick[:max_experts]:
+        lo, hi = offs[e], offs[e + 1]
+        rows += list(rng.choice(np.arange(lo, hi), size=min(n_per, hi - lo), replace=False))
+        rows.append(hi - 1)
+    return np.unique(np.array(rows, np.int64))
+
+
+def test_workload0_w4a4_tiny_end_to_end():
+    wl = _run(0)
+    off, srt, p2s, _ = _check_route(wl)
+    d = wl.d
+    ref = oracle.int4_layer(d)
+    assert_rows_close(host(wl.y), ref["y"], what="y")
+    assert_rows_close(host(wl.out), oracle.scatter_combine(host(wl.y), p2s, d["topk_weights"]),
+                      what="combine (GPU y)")
+    assert_rows_close(host(wl.out), ref["out"], what="layer")
+    acc = wl.mq.grouped_gemm_qint4(wl.a, wl.sa, wl.w, wl.sw, wl.route_out[0], wl.route_out[1], wl.k,
+                                   out_dtype=torch.int32)
+    assert np.array_equal(host(acc), ref["acc"])
+
+
+def test_workload1_fp8_dense_sampled_rows():
+    wl = _run(1)
+    _check_route(wl)
+    d = wl.d
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 511, 1023],
+                                     np.random.default_rng(1).choice(1024, 40, replace=False)]))
+    ref = oracle.grouped_gemm_qfp8_block(d["a"], d["a_scale"], "token", d["w"], d["w_scale"],
+                                         host(wl.route_out[0]), host(wl.route_out[1]), 1, rows=rows)["y"]
+    assert_rows_close(host(wl.y)[rows], ref, what="fp8 full size")
+
+
+def _nvfp4_checks(wl, n_per):
+    off, srt, p2s, _ = _check_route(wl)
+    d = wl.d
+    rows = _sample_rows(off, n_per=n_per)
+    h_ref = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], off, srt, d["k"],
+                                       act="silu_mul", rows=rows)["y"]
+    assert_rows_close(host(wl.h)[rows], h_ref, what="FC1 h")
+    hb = bf16_bits(wl.h)      # FC2 consumes the GPU's h (per-call parity)
+    y_ref = oracle.grouped_gemm_qnvfp4(hb, "sorted", d["w2"], d["s2"], d["g2"], off, srt, d["k"],
+                                       rows=rows)["y"]
+    assert_rows_close(host(wl.y)[rows], y_ref, what="FC2 y")
+    out_ref = oracle.scatter_combine(host(wl.y), p2s, d["topk_weights"])
+    assert_rows_close(host(wl.out), out_ref, what="combine")
+
+
+def test_workload2_nvfp4_decode():
+    _nvfp4_checks(_run(2), n_per=1)
+
+
+def test_workload3_nvfp4_prefill_zipf():
+    wl = _run(3)
+    sizes = np.diff(host(wl.route_out[0]))
+    assert sizes.min() == 0 and sizes.max() > 1000      # skewed, with empty experts
+    _nvfp4_checks(wl, n_per=2)
+
+
+def test_workload4_w4a4_mixtral():
+    wl = _run(4)
+    off, srt, p2s, _ = _check_route(wl)
+    d = wl.d
+    rows = _sample_rows(off, n_per=2, max_experts=3)
+    h_ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], off, srt,
+                                      d["k"], act="silu_mul", rows=rows)["y"]
+    assert_rows_close(host(wl.h)[rows], h_ref, what="FC1 h")
+    # FC2 raw accumulators at full size, bit-exact on the sampled rows
+    acc = wl.mq.grouped_gemm_qint4(wl.a2, wl.sa2, wl.w2, wl.sw2, wl.route_out[0], wl.route_out[1],
+                                   wl.k, a_row="sorted", out_dtype=torch.int32)
+    ref2 = oracle.grouped_gemm_qint4(d["a2"], d["a2_scale"], "sorted", d["w2"], d["w2_scale"], off,
+                                     srt, d["k"], rows=rows)
+    assert np.array_equal(host(acc)[rows], ref2["acc"])
+    assert_rows_close(host(wl.y)[rows], ref2["y"], what="FC2 y")
+    assert_rows_close(host(wl.out), oracle.scatter_combine(host(wl.y), p2s, d["topk_weights"]),
+                      what="combine")
