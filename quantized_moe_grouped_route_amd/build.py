@@ -24,6 +24,8 @@ COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Wno-unused-variable", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: epilogue / promotion arithmetic reads them directly
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 
