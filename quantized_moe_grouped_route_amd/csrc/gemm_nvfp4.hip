@@ -16,6 +16,7 @@
 
 #include "kernels.h"
 #include "nvfp4.h"
+#include "pipeline.h"
 #include "tile.h"
 
 namespace moeq {
@@ -24,121 +25,204 @@ namespace {
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 // ------------------------------------------------------------------ prefill
-// K step = 64 values: A rows 128 bytes of bf16 (thread t: row t/8 + 32i,
-// bytes (t%8)*16), B rows 32 packed bytes + 4 scale bytes (thread t: row
-// t/2, packed bytes (t%2)*16 = 32 codes = 2 scale blocks), dequantized to
-// 128 bytes of bf16 per row in LDS.
+// CU work unit: a workgroup of 4 waves owns a 128 (activation rows) x 256
+// (weight rows; for SILU_MUL 128 gate rows + the 128 matching up rows)
+// tile and walks K in steps of 64 through a 3-stage LDS ring (75 KB), so
+// two workgroups share a CU and their phases (dequantization on the VALU,
+// MFMAs) interleave.  Stage layout (25 KB):
+//   A  128 rows x 128 bytes (64 bf16), 16-byte chunks swizzled as in the
+//      FP8 kernel;
+//   B  256 rows x 32 packed bytes (64 E2M1 codes), the 16-byte chunk c of
+//      row r at position c ^ ((r >> 3) & 1);
+//   S  256 rows x 4 scale bytes.
+// Wave wn owns 64 weight rows (two 32-row MFMA operands) against all 128
+// activation rows, so every weight code is dequantized once per tile.
+//
+// K slots: in a K step, MFMA lane l (slice l/32) takes the codes
+// [32*slice, +32) of its weight row - one 16-byte LDS read, two scale bytes
+// - and sub-step s uses codes [32*slice + 8s, +8).  The activation operand
+// uses the same slots: slice `slice`, sub-step s = logical chunk 4*slice+s
+// of the row's 128 bytes.
+namespace pf {
+constexpr int kM = 128, kN = 256;
+constexpr int kStages = 3;
+constexpr int kABytes = kM * 128;
+constexpr int kBBytes = kN * 32;
+constexpr int kSBytes = kN * 4;
+constexpr int kStageBytes = kABytes + kBBytes + kSBytes;
+constexpr int kThreads = 256;
+}  // namespace pf
+
 template <int OUT, bool SILU>
-__global__ __launch_bounds__(kThreadsT, 1) void nvfp4_prefill(
+__global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale,
     const int* __restrict__ offsets, const int* __restrict__ sorted_ids, int topk, int E, int P, int N,
     int K, void* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[kTileM * kPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[kTileN * kPitch];
+  using namespace pf;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
   __shared__ int tile_start[kMaxExperts + 1];
   __shared__ int sched_scratch[2 * kMaxWaves];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-  const int n_tiles = N / kTileN;
+  const int tid = threadIdx.x, lane = tid & 63, wn = tid >> 6;
   const int I = N / 2;
-  const int steps = K / 64;
-  const int64_t wrow_bytes = K / 2, srow_bytes = K / 16;
-  sched_build(tile_start, sched_scratch, offsets, E, P, kTileM, n_tiles);
+  const int n_tiles = SILU ? I / 128 : N / kN;
+  const int G = K / 64;
+  const int64_t xrow_bytes = (int64_t)K * 2, wrow_bytes = K / 2, srow_bytes = K / 16;
+  sched_build(tile_start, sched_scratch, offsets, E, P, kM, n_tiles);
   const int total = tile_start[E];
 
-  const int arow = tid >> 3, achunk = (tid & 7) * 16;  // A: bytes of bf16
-  const int brow = tid >> 1, bhalf = tid & 1;          // B: 16 packed bytes
+  const int slice = lane >> 5, l32 = lane & 31;
+  const int key = frag_key(lane);
+  // Weight rows of this lane's two operands (row index in the B tile).
+  const int brow0 = SILU ? 32 * wn + l32 : 64 * wn + l32;
+  const int brow1 = SILU ? 128 + 32 * wn + l32 : 64 * wn + 32 + l32;
+  const int boff0 = kABytes + brow0 * 32 + ((slice ^ ((brow0 >> 3) & 1)) << 4);
+  const int boff1 = kABytes + brow1 * 32 + ((slice ^ ((brow1 >> 3) & 1)) << 4);
+  const int soff0 = kABytes + kBBytes + brow0 * 4 + slice * 2;
+  const int soff1 = kABytes + kBBytes + brow1 * 4 + slice * 2;
+  int aoff[4];  // activation chunk offsets for sub-step s (logical chunk 4*slice + s)
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aoff[s] = (((4 * slice + s) ^ key) << 4);
 
   for (int item = xcd_logical_id(blockIdx.x, gridDim.x); item < total; item += gridDim.x) {
-    const Tile t = sched_tile<4>(tile_start, offsets, E, P, kTileM, n_tiles, item);
+    const Tile t = sched_tile<4>(tile_start, offsets, E, P, kM, n_tiles, item);
+    // DMA sources.  A: wave wn moves rows 8q + lane/8 for q = 4wn + j.
     const uint8_t* pa[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = t.row0 + min(arow + 32 * i, t.rows - 1);
-      pa[i] = reinterpret_cast<const uint8_t*>(x) +
-              a_row_of(s, sorted_ids, a_sorted, topk, rows_a) * (int64_t)K * 2 + achunk;
+    for (int j = 0; j < 4; ++j) {
+      const int q = 4 * wn + j;
+      const int r = 8 * q + (lane >> 3);
+      const int s = t.row0 + min(r, t.rows - 1);
+      pa[j] = reinterpret_cast<const uint8_t*>(x) + a_row_of(s, sorted_ids, a_sorted, topk, rows_a) * xrow_bytes +
+              dma_chunk(lane, q);
     }
-    const int64_t wr = (int64_t)t.e * N + b_global_row(SILU, t.nt, brow, I);
-    const uint8_t* pw = w + wr * wrow_bytes + bhalf * 16;
-    const uint8_t* ps = w_sf + wr * srow_bytes + bhalf * 2;
-
-    v16f acc[2][2];
+    auto grow = [&](int r) __attribute__((always_inline)) {
+      if (!SILU) return (int64_t)t.e * N + (int64_t)t.nt * kN + r;
+      return (int64_t)t.e * N + (r < 128 ? (int64_t)t.nt * 128 + r : (int64_t)I + t.nt * 128 + (r - 128));
+    };
+    // B: wave wn moves rows 64wn + 32j + lane/2 (chunk position lane%2);
+    // S: rows 64wn + lane.
+    const uint8_t* pb[2];
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) acc[p][q] = v16f{};
-
-    u32x4 ra[4], rw;
-    uint32_t rs;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = ld16(pa[i]);
-    rw = ld16(pw);
-    rs = *reinterpret_cast<const uint16_t*>(ps);
-
-    for (int st = 0; st < steps; ++st) {
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        st16(lds_a + (arow + 32 * i) * kPitch + achunk, ra[i]);
-      {
-        const float s0 = e4m3_to_f32(rs & 0xffu), s1 = e4m3_to_f32((rs >> 8) & 0xffu);
-        uint8_t* db = lds_b + brow * kPitch + bhalf * 64;
-        st16(db, dequant8_bf16(rw.x, s0));
-        st16(db + 16, dequant8_bf16(rw.y, s0));
-        st16(db + 32, dequant8_bf16(rw.z, s1));
-        st16(db + 48, dequant8_bf16(rw.w, s1));
-      }
-      __syncthreads();
-      if (st + 1 < steps) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ra[i] = ld16(pa[i] + (int64_t)(st + 1) * 128);
-        rw = ld16(pw + (int64_t)(st + 1) * 32);
-        rs = *reinterpret_cast<const uint16_t*>(ps + (int64_t)(st + 1) * 4);
-      }
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq) {
-        const int koff = kq * 32 + (lane >> 5) * 16;
-        v8bf fa[2], fb[2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-          fa[p] = *reinterpret_cast<const v8bf*>(lds_a + (64 * wm + 32 * p + (lane & 31)) * kPitch + koff);
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-          fb[q] = *reinterpret_cast<const v8bf*>(lds_b + (b_lds_row(SILU, wn, q) + (lane & 31)) * kPitch + koff);
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-          for (int q = 0; q < 2; ++q) acc[p][q] = mfma_bf16_32x32x16(fa[p], fb[q], acc[p][q]);
-      }
+    for (int j = 0; j < 2; ++j) {
+      const int rb = 64 * wn + 32 * j + (lane >> 1);
+      pb[j] = w + grow(rb) * wrow_bytes + (((lane & 1) ^ ((rb >> 3) & 1)) << 4);
     }
+    const uint8_t* ps = w_sf + grow(64 * wn + lane) * srow_bytes;
+    const uint32_t lds_a = lds_addr(smem + wn * 4096);
+    const uint32_t lds_b = lds_addr(smem + kABytes + wn * 2048);
+    const uint32_t lds_s = lds_addr(smem + kABytes + kBBytes + wn * 256);
+    auto issue = [&](int g) __attribute__((always_inline)) {
+      const uint32_t st = (uint32_t)((g % kStages) * kStageBytes);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16(pa[j] + (int64_t)g * 128, lds_a + st + j * 1024);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) dma16(pb[j] + (int64_t)g * 32, lds_b + st + j * 1024);
+      dma4(ps + (int64_t)g * 4, lds_s + st);
+    };
+    constexpr int kPer = 7;  // loads per wave per stage
 
-    const float gs = w_gscale[t.e];
-    typedef typename OutT<OUT>::T T;
-    T* o = static_cast<T*>(out);
-    if (SILU) {
-      const int col = t.nt * 64 + 32 * wn + (lane & 31);
+    v16f acc[2][4];
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+    for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int rr = 64 * wm + 32 * p + c32_row(i, lane);
-          const float g = gs * acc[p][0][i], u = gs * acc[p][1][i];
-          if (rr < t.rows) o[(int64_t)(t.row0 + rr) * I + col] = OutT<OUT>::from(silu(g) * u);
+      for (int y = 0; y < 4; ++y) acc[a2][y] = v16f{};
+
+    raw_barrier();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+      if (s < G) issue(s);
+    int last_issued = min(G, kStages - 1) - 1;
+
+    for (int g = 0; g < G; ++g) {
+      if (last_issued - g >= 1) wait_vmcnt<kPer>();
+      else wait_vmcnt<0>();
+      raw_barrier();  // stage g visible to all waves; stage g-1 is free
+      if (g + kStages - 1 < G) {
+        issue(g + kStages - 1);
+        last_issued = g + kStages - 1;
+      }
+      const uint8_t* st = smem + (g % kStages) * kStageBytes;
+      // Dequantize this lane's 2 x 32 weight codes (exact in bf16).
+      const u32x4 q0 = ld16(st + boff0), q1 = ld16(st + boff1);
+      const uint32_t sc0 = *reinterpret_cast<const uint16_t*>(st + soff0);
+      const uint32_t sc1 = *reinterpret_cast<const uint16_t*>(st + soff1);
+      const float s00 = e4m3_to_f32(sc0 & 0xffu), s01 = e4m3_to_f32(sc0 >> 8);
+      const float s10 = e4m3_to_f32(sc1 & 0xffu), s11 = e4m3_to_f32(sc1 >> 8);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const v8bf wf0 = __builtin_bit_cast(v8bf, dequant8_bf16(q0[s], s < 2 ? s00 : s01));
+        const v8bf wf1 = __builtin_bit_cast(v8bf, dequant8_bf16(q1[s], s < 2 ? s10 : s11));
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const v8bf xf = *reinterpret_cast<const v8bf*>(st + (32 * y + l32) * 128 + aoff[s]);
+          acc[0][y] = mfma_bf16_32x32x16(wf0, xf, acc[0][y]);
+          acc[1][y] = mfma_bf16_32x32x16(wf1, xf, acc[1][y]);
         }
-    } else {
+      }
+    }
+
+    // Epilogue: global scale (and the SiLU-gated product), output tile
+    // through LDS, then 16-byte stores along output rows.
+    typedef typename OutT<OUT>::T T;
+    constexpr int kCols = SILU ? 128 : 256;
+    constexpr int kOutPitch = kCols * (int)sizeof(T) + 16;
+    constexpr bool kStaged = kM * kOutPitch <= kStages * kStageBytes;  // else: f32, direct stores
+    raw_barrier();  // all waves are done with the ring
+    uint8_t* otile = smem;
+    const float gs = w_gscale[t.e];
+    const int ldo = SILU ? I : N;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int col = t.nt * kTileN + b_lds_row(false, wn, q) + (lane & 31);
+    for (int y = 0; y < 4; ++y) {
+      uint8_t* orow = otile + (32 * y + l32) * kOutPitch;
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
+      for (int q = 0; q < 4; ++q) {
+        float v[2][4];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int rr = 64 * wm + 32 * p + c32_row(i, lane);
-            if (rr < t.rows) o[(int64_t)(t.row0 + rr) * N + col] = OutT<OUT>::from(gs * acc[p][q][i]);
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * q + r;
+          if (SILU) {
+            v[0][r] = silu(gs * acc[0][y][i]) * (gs * acc[1][y][i]);
+            v[1][r] = 0.f;
+          } else {
+            v[0][r] = gs * acc[0][y][i];
+            v[1][r] = gs * acc[1][y][i];
           }
+        }
+        // weight columns 8q + 4*slice + r of the lane's 32-row operand(s)
+        const int col0 = (SILU ? 32 * wn : 64 * wn) + 8 * q + 4 * slice;
+#pragma unroll
+        for (int a2 = 0; a2 < (SILU ? 1 : 2); ++a2) {
+          if constexpr (!kStaged) {
+            const int rr = 32 * y + l32;
+            if (rr < t.rows)
+              *reinterpret_cast<float4*>(static_cast<float*>(out) + (int64_t)(t.row0 + rr) * ldo +
+                                         (int64_t)t.nt * kCols + col0 + 32 * a2) =
+                  make_float4(v[a2][0], v[a2][1], v[a2][2], v[a2][3]);
+            continue;
+          }
+          uint8_t* dst = orow + (col0 + 32 * a2) * (int)sizeof(T);
+          if (sizeof(T) == 2) {
+            const u32 lo = pack2<OUT>(v[a2][0], v[a2][1]);
+            const u32 hi = pack2<OUT>(v[a2][2], v[a2][3]);
+            *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+          } else {
+            *reinterpret_cast<float4*>(dst) = make_float4(v[a2][0], v[a2][1], v[a2][2], v[a2][3]);
+          }
+        }
+      }
+    }
+    raw_barrier();
+    if constexpr (kStaged) {
+      constexpr int kChunksPerRow = kCols * (int)sizeof(T) / 16;
+      uint8_t* obase = static_cast<uint8_t*>(out) + ((int64_t)t.row0 * ldo + (int64_t)t.nt * kCols) * (int)sizeof(T);
+#pragma unroll 4
+      for (int i = 0; i < kM * kChunksPerRow / kThreads; ++i) {
+        const int ci = tid + kThreads * i;
+        const int r = ci / kChunksPerRow, c = ci % kChunksPerRow;
+        if (r < t.rows)
+          st16(obase + (int64_t)r * ldo * (int)sizeof(T) + c * 16, ld16(otile + r * kOutPitch + c * 16));
       }
     }
   }
@@ -248,10 +332,10 @@ hipError_t go(const GroupedArgs& g, bool decode, const uint16_t* x, const uint8_
                        g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N, g.K,
                        g.out);
   } else {
-    const int64_t mt_ub = (g.P + kTileM - 1) / kTileM + std::min<int64_t>(g.E, g.P);
-    const int64_t items_ub = mt_ub * (g.N / kTileN);
+    const int64_t mt_ub = (g.P + pf::kM - 1) / pf::kM + std::min<int64_t>(g.E, g.P);
+    const int64_t items_ub = mt_ub * (g.N / pf::kN);
     const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus * 2);
-    hipLaunchKernelGGL((nvfp4_prefill<OUT, SILU>), dim3(grid), dim3(kThreadsT), 0, stream, x,
+    hipLaunchKernelGGL((nvfp4_prefill<OUT, SILU>), dim3(grid), dim3(pf::kThreads), 0, stream, x,
                        g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P,
                        g.N, g.K, g.out);
   }
@@ -263,8 +347,9 @@ hipError_t go(const GroupedArgs& g, bool decode, const uint16_t* x, const uint8_
 hipError_t launch_gemm_nvfp4(const GroupedArgs& g, const uint16_t* x, const uint8_t* w,
                              const uint8_t* w_sf, const float* w_gscale, hipStream_t stream) {
   if (g.P == 0) return hipSuccess;
-  // AUTO: the streaming schedule while experts average fewer than 16 rows.
-  const bool decode = g.sched == 1 || (g.sched == 0 && g.P < (int64_t)16 * g.E);
+  // AUTO: the streaming schedule while experts average fewer than 16 rows,
+  // and whenever N is not a multiple of the prefill tile (256).
+  const bool decode = g.sched == 1 || (g.sched == 0 && (g.P < (int64_t)16 * g.E || g.N % pf::kN != 0));
   if (g.silu_mul) {
     switch (g.out_kind) {
       case OUT_F16: return go<OUT_F16, true>(g, decode, x, w, w_sf, w_gscale, stream);

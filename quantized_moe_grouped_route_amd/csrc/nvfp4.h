@@ -18,8 +18,9 @@ __device__ __forceinline__ v2f e2m1x2_f32(u32 word) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
 }
 
+// Two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32, nearest even).
 __device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
-  return (u32)f32_to_bf16_bits(lo) | ((u32)f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(u32, __builtin_convertvector(v2f{lo, hi}, v2bf));
 }
 
 // 8 E2M1 codes (one 32-bit word, elements 0..7) times `scale` -> 8 bf16 as
@@ -29,6 +30,13 @@ __device__ __forceinline__ u32x4 dequant8_bf16(u32 word, float scale) {
   const v2f p2 = e2m1x2_f32<2>(word), p3 = e2m1x2_f32<3>(word);
   return u32x4{pack_bf16x2(p0.x * scale, p0.y * scale), pack_bf16x2(p1.x * scale, p1.y * scale),
                pack_bf16x2(p2.x * scale, p2.y * scale), pack_bf16x2(p3.x * scale, p3.y * scale)};
+}
+
+// Packed pair of output elements of kind KIND (bf16 or f16) from two floats.
+template <int KIND>
+__device__ __forceinline__ u32 pack2(float lo, float hi) {
+  if (KIND == OUT_BF16) return pack_bf16x2(lo, hi);
+  return (u32)f32_to_f16_bits(lo) | ((u32)f32_to_f16_bits(hi) << 16);
 }
 
 }  // namespace moeq
