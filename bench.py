@@ -100,7 +100,8 @@ class Workload:
             self.flops = 2.0 * P * d["N"] * d["K"]
             self.weight_bytes = float(self.w.numel() + self.sw.numel() * 4)
             self.dtype = "fp8_e4m3"
-            self.dom = ("fp8_prefill", ["gemm_fp8.hip", "common.h", "tile.h"], "mfma", PEAK["fp8"])
+            self.dom = ("fp8_prefill", ["gemm_fp8.hip", "common.h", "tile.h", "pipeline.h"], "mfma",
+                        PEAK["fp8"])
         elif kind == "int4":
             self.a, self.sa = _dev(d["a"]), _dev(d["a_scale"])
             self.w, self.sw = _dev(d["w"]), _dev(d["w_scale"])
@@ -136,10 +137,10 @@ class Workload:
             self.flops = 2.0 * valid.size * (2 * I * H + H * I)
             self.dtype = "bf16_x_nvfp4"
             if idx == 2:
-                self.dom = ("nvfp4_decode", ["gemm_nvfp4.hip", "nvfp4.h", "common.h", "tile.h"], "hbm",
+                self.dom = ("nvfp4_decode", ["gemm_nvfp4.hip", "nvfp4.h", "common.h", "tile.h", "pipeline.h"], "hbm",
                             PEAK["hbm_GBps"])
             else:
-                self.dom = ("nvfp4_prefill", ["gemm_nvfp4.hip", "nvfp4.h", "common.h", "tile.h"], "mfma",
+                self.dom = ("nvfp4_prefill", ["gemm_nvfp4.hip", "nvfp4.h", "common.h", "tile.h", "pipeline.h"], "mfma",
                             PEAK["bf16"])
 
     def step(self, ev=None):
@@ -174,6 +175,25 @@ class Workload:
             mq.grouped_gemm_qnvfp4(self.h, self.w2, self.s2, self.g2, offs, srt, self.k,
                                    a_row="sorted", out=self.y)
             mq.moe_scatter_combine(self.y, p2s, self.tw, out=self.out)
+
+    def dominant_launches(self):
+        """(launches of the dominant kernel per step, index of the timed one)."""
+        return (1, 0) if self.cfg["kind"] == "fp8" or self.idx == 0 else (2, 0)
+
+    def dominant_bytes(self):
+        """Fewest HBM bytes one launch of the dominant kernel can move: every
+        operand read once, every output written once."""
+        d, P = self.d, self.T * self.k
+        kind = self.cfg["kind"]
+        if kind == "fp8":
+            N, K = d["N"], d["K"]
+            return float(P * K + d["w"].size + d["a_scale"].size * 4 + d["w_scale"].size * 4 + P * N * 2)
+        if kind == "int4":
+            N, K = d["N"], d["K"]
+            out = N * 2 if self.idx == 0 else N  # f16 y, or f16 h = N/2 columns
+            return float(P * K // 2 + P * 4 + d["w"].size + d["w_scale"].size * 4 + P * out)
+        H, I = d["H"], d["I"]
+        return float(self.fc1_bytes + P * H * 2 + P * I * 2)
 
     def dominant_work(self):
         """Algorithmic work of one launch of the dominant kernel:
@@ -241,6 +261,132 @@ def cpu_baseline(idx: int, d, budget_s: float = 10.0):
                 kind="oracle", sample=f"FC1 of {len(experts)} experts ({rows.size} rows)")
 
 
+# ------------------------------------------------------- profile summaries
+def profile_commands(idx: int, pdir: str):
+    """The rocprofv3 runs whose outputs --summarize-profiles reduces."""
+    run = f"python3 bench.py --workload {idx}"
+    short = f"{run} --steps 3 --warmup 1 --no-cpu-baseline"
+    copy = "python3 bench.py --copy-calibration"
+    pmc = "rocprofv3 --pmc {c} -d {d} -o run --output-format csv -- {r}"
+    return {
+        "trace": f"rocprofv3 --kernel-trace --stats -d {pdir}/trace_w{idx} -o run --output-format csv -- {run}",
+        "fetch": pmc.format(c="FETCH_SIZE", d=f"{pdir}/fetch_w{idx}", r=short),
+        "write": pmc.format(c="WRITE_SIZE", d=f"{pdir}/write_w{idx}", r=short),
+        "copy_fetch": pmc.format(c="FETCH_SIZE", d=f"{pdir}/fetch_copy", r=copy),
+        "copy_write": pmc.format(c="WRITE_SIZE", d=f"{pdir}/write_copy", r=copy),
+    }
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short_name(name):
+    """Kernel base name: no return type, namespaces, template or call arguments."""
+    base = name.split("(")[0] if not name.startswith("void ") else name[5:]
+    base = base.replace("(anonymous namespace)::", "").split("(")[0].split("<")[0]
+    return base.split("::")[-1]
+
+
+def summarize_profiles(idx: int, pdir: str, steps: int = 50, warmup: int = 10):
+    """Reduce the rocprofv3 outputs of profile_commands() to the text
+    summaries under profiles/: per-kernel duration statistics and, for the
+    dominant kernel, HBM traffic per launch scaled by a copy of known size."""
+    import synth
+    cfg = synth.WORKLOADS[idx]
+    wl = Workload.__new__(Workload)  # host-side fields only
+    wl.idx, wl.cfg, wl.d = idx, cfg, synth.workload(idx)
+    wl.T, wl.k, wl.E = wl.d["T"], wl.d["k"], wl.d["E"]
+    d = wl.d
+    tag = {"fp8": "fp8_prefill", "int4": "int4_prefill"}.get(cfg["kind"]) or \
+        ("nvfp4_decode" if idx == 2 else "nvfp4_prefill")
+    srcs = {"fp8_prefill": ["gemm_fp8.hip", "common.h", "tile.h", "pipeline.h"],
+            "int4_prefill": ["gemm_int4.hip", "common.h", "tile.h"]}.get(
+        tag, ["gemm_nvfp4.hip", "nvfp4.h", "common.h", "tile.h", "pipeline.h"])
+    if cfg["kind"] == "nvfp4":
+        H, I = d["H"], d["I"]
+        ids = d["topk_ids"].reshape(-1)
+        active = int(np.unique(ids[(ids >= 0) & (ids < wl.E)]).size)
+        wl.fc1_bytes = float(active * (2 * I * H // 2 + 2 * I * H // 16 + 4))
+    per_step, which = wl.dominant_launches()
+    cmds = profile_commands(idx, pdir)
+
+    def find(sub, suffix):
+        path = os.path.join(pdir, sub, f"run_{suffix}.csv")
+        if not os.path.exists(path):
+            raise SystemExit(f"missing {path}: run the rocprofv3 commands first")
+        return path
+
+    def dominant(rows, key):
+        rows = [r for r in rows if _short_name(r["Kernel_Name"]) == tag]
+        rows.sort(key=lambda r: int(r[key]))
+        return [r for i, r in enumerate(rows) if i % per_step == which]
+
+    # durations: stats over all launches, the timed launches from the trace
+    stats = _csv_rows(find(f"trace_w{idx}", "kernel_stats"))
+    trace = dominant(_csv_rows(find(f"trace_w{idx}", "kernel_trace")), "Start_Timestamp")
+    timed = trace[-steps:]
+    dur_us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
+    name = f"{tag}_{cfg['name']}"
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    lines = [f"# Kernel durations: {cfg['name']}", "",
+             "Command (from the repository root, TMPDIR=/tmp):", "", f"    {cmds['trace']}", "",
+             "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {_short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {r['Percentage']} |")
+    lines += ["", f"Dominant kernel `{tag}`: launch {which + 1} of {per_step} per step, last {len(timed)} "
+              f"launches of the trace (the timed steps): average {np.mean(dur_us):.2f} us, "
+              f"min {np.min(dur_us):.2f}, max {np.max(dur_us):.2f}."]
+    log = os.path.join(pdir, f"trace_w{idx}.log")
+    if os.path.exists(log):
+        for ln in open(log):
+            if ln.startswith("{"):
+                rec = json.loads(ln)
+                lines += ["", f"bench.py line of the same run: kernel_ms {rec['roofline']['kernel_ms']} "
+                          f"(HIP events), frac {rec['roofline']['frac']}, value {rec['value']} {rec['unit']}."]
+    with open(os.path.join(ROOT, "profiles", f"{name}_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # traffic
+    def counter(sub, ctr, rows_of):
+        rows = [r for r in _csv_rows(find(sub, "counter_collection")) if r["Counter_Name"] == ctr]
+        return [float(r["Counter_Value"]) for r in rows_of(rows)]
+    copy_bytes = float((1 << 28) * 4)
+    is_copy = lambda rows: [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+    cf = counter("fetch_copy", "FETCH_SIZE", is_copy)
+    cw = counter("write_copy", "WRITE_SIZE", is_copy)
+    f_fac = copy_bytes / (np.mean(cf) * 1024.0)
+    w_fac = copy_bytes / (np.mean(cw) * 1024.0)
+    dom = lambda rows: dominant(rows, "Dispatch_Id")
+    fk = counter(f"fetch_w{idx}", "FETCH_SIZE", dom)
+    wk = counter(f"write_w{idx}", "WRITE_SIZE", dom)
+    fetch_b = float(np.mean(fk)) * 1024.0 * f_fac
+    write_b = float(np.mean(wk)) * 1024.0 * w_fac
+    alg = wl.dominant_bytes()
+    txt = [f"kernel: {tag}", f"workload: {cfg['name']}",
+           f"kernel_sources: {' '.join(srcs)}",
+           f"kernel_sources_sha256_16: {_sources_digest(srcs)}",
+           f"launches_counted: {len(fk)} (FETCH_SIZE), {len(wk)} (WRITE_SIZE); launch {which + 1} of "
+           f"{per_step} per step",
+           f"fetch_size_kib_per_launch: {np.mean(fk):.1f}",
+           f"write_size_kib_per_launch: {np.mean(wk):.1f}",
+           f"copy_calibration: 1 GiB device copy reads FETCH_SIZE {np.mean(cf):.1f} KiB, "
+           f"WRITE_SIZE {np.mean(cw):.1f} KiB; factors fetch {f_fac:.4f}, write {w_fac:.4f}",
+           f"fetch_bytes_per_launch: {fetch_b:.0f}",
+           f"write_bytes_per_launch: {write_b:.0f}",
+           f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
+           f"algorithmic_bytes_per_launch: {alg:.0f}",
+           f"traffic_over_algorithmic: {(fetch_b + write_b) / alg:.3f}",
+           "commands (from the repository root, TMPDIR=/tmp):"]
+    txt += [f"  {cmds[k]}" for k in ("fetch", "write", "copy_fetch", "copy_write")]
+    with open(os.path.join(ROOT, "profiles", f"{name}_traffic.txt"), "w") as f:
+        f.write("\n".join(txt) + "\n")
+    print(f"wrote profiles/{name}_kernel_stats.md and profiles/{name}_traffic.txt")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,7 +397,19 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device 5 times (a kernel of known traffic "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--profile-commands", metavar="DIR",
+                    help="print the rocprofv3 commands (outputs under DIR) that "
+                         "--summarize-profiles reduces, one per line, and exit")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write the profiles/ summaries of --workload from the rocprofv3 "
+                         "outputs under DIR (host only) and exit")
     args = ap.parse_args()
+    if args.profile_commands:
+        print("\n".join(profile_commands(args.workload, args.profile_commands).values()))
+        return
+    if args.summarize_profiles:
+        summarize_profiles(args.workload, args.summarize_profiles, args.steps, args.warmup)
+        return
     if args.gpus != 1:
         print("bench.py measures one MI355X: the path runs on a single GPU; "
               "--gpus above 1 is not supported", file=sys.stderr)
@@ -270,15 +428,30 @@ def main():
         return
     wl = Workload(args.workload)
     torch.cuda.synchronize()
+    host_s = []
     for _ in range(args.warmup):
+        t = time.perf_counter()
         wl.step()
+        host_s.append(time.perf_counter() - t)
     torch.cuda.synchronize()
+    # The device must never wait for the host inside the timed region: a
+    # bounded spin kernel holds the stream while the host enqueues every
+    # timed step, so the events time the device's work, not the gaps of
+    # the Python launches.  The spin ends before t0 is recorded.
+    spin_ms = 2.0 + 1.5 * args.steps * 1e3 * float(np.median(host_s) if host_s else 1e-3)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    torch.cuda._sleep(1 << 20)
+    c1.record()
+    torch.cuda.synchronize()
+    cycles_per_ms = (1 << 20) / max(c0.elapsed_time(c1), 1e-3)
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    torch.cuda._sleep(int(min(spin_ms, 2000.0) * cycles_per_ms))
     wall = time.perf_counter()
     t0.record()
     for i in range(args.steps):
@@ -315,7 +488,8 @@ def main():
            "roofline": roof}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.workload, wl.d)
-    rec["host_wall_s_timed"] = round(wall, 4)
+    rec["host_wall_s_incl_spin"] = round(wall, 4)
+    rec["host_enqueue_ms_per_step"] = round(1e3 * float(np.median(host_s)) if host_s else 0.0, 4)
     print(json.dumps(rec), flush=True)
 
 

@@ -127,8 +127,8 @@ moeq_status moe_route_prep(const int32_t* topk_ids, int64_t T, int32_t topk, int
  *                I32: the raw accumulator acc (act NONE only), bit-exact
  * Computed exactly in integers (int8 MFMA on nibbles scaled by 16), then
  * scaled in fp32 and rounded to nearest even.
- * Requires K % 128 == 0, N % 64 == 0 (SILU_MUL: N % 128 == 0), all
- * pointers 16-byte aligned, E >= 1.
+ * Requires K % 128 == 0 and N % 128 == 0 (else MOEQ_EALIGN), all
+ * pointers 16-byte aligned, 1 <= E <= 1024, 1 <= topk <= 64.
  * ---------------------------------------------------------------------- */
 moeq_status grouped_gemm_qint4(const uint8_t* a, const float* a_scale, int64_t rows_a,
                                moeq_arow a_row, const uint8_t* w, const float* w_scale,
@@ -151,7 +151,8 @@ moeq_status grouped_gemm_qint4(const uint8_t* a, const float* a_scale, int64_t r
  *   out      [P][N] out_dtype (BF16 | F16 | F32)
  *   y[s][n] = sum_g a_scale[g][r] * w_scale[e][n/128][g]
  *                   * sum_{k in group g} a[r][k] * w[e][n][k]
- * Requires K % 128 == 0, N % 128 == 0, 16-byte aligned pointers.
+ * Requires K % 128 == 0 and N % 128 == 0 (else MOEQ_EALIGN), 16-byte
+ * aligned pointers, 1 <= E <= 1024, 1 <= topk <= 64.
  * ---------------------------------------------------------------------- */
 moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int64_t rows_a,
                                     moeq_arow a_row, const uint8_t* w, const float* w_scale,
@@ -175,8 +176,10 @@ moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int6
  *   out       [P][N] (NONE) or [P][N/2] (SILU_MUL), BF16 | F16 | F32
  *   y[s][n] = w_gscale[e] * sum_k x[r][k] * e2m1(w[e][n][k])
  *                                  * ue4m3(w_sf[e][n][k/16])
- * Requires K % 128 == 0, N % 64 == 0 (SILU_MUL: N % 128 == 0), 16-byte
- * aligned pointers.
+ * Requires K % 128 == 0 and N % 128 == 0 (else MOEQ_EALIGN), 16-byte
+ * aligned pointers, 1 <= E <= 1024, 1 <= topk <= 64.  sched AUTO takes the
+ * weight-streaming schedule when P < 16 * E or N % 256 != 0; PREFILL with
+ * N % 256 != 0 falls back to it as well.
  * ---------------------------------------------------------------------- */
 moeq_status grouped_gemm_qnvfp4(const void* x, int64_t rows_a, moeq_arow a_row,
                                 const uint8_t* w, const uint8_t* w_sf, const float* w_gscale,

@@ -240,8 +240,13 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
 // takes codes [8i, 8i+8) of every lane's 32, so its K slot (l/16, 0..7)
 // holds K index 128c + 32(l/16) + 8i + (0..7).  The activation operand uses
 // the same slots: lane l (routed row l % 16) loads x[row][that K range].
+//
+// The weight stream is what bounds this schedule: each lane keeps kPre
+// chunks (kPre x 16 bytes of codes, their scales) in flight in registers,
+// so a CU has enough bytes outstanding to cover the HBM latency.
 constexpr int kDecM = 16;
 constexpr int kDecNB = 64;  // weight rows per work item
+constexpr int kPre = 8;     // weight chunks in flight per lane
 
 template <int OUT, bool SILU>
 __global__ __launch_bounds__(256) void nvfp4_decode(
@@ -271,28 +276,73 @@ __global__ __launch_bounds__(256) void nvfp4_decode(
     const int g = lane >> 4;
     const uint8_t* pw = w + ((int64_t)t.e * N + wrow) * wrow_bytes + g * 16;
     const uint8_t* ps = w_sf + ((int64_t)t.e * N + wrow) * srow_bytes + g * 2;
-    // Activation row of this lane (routed row lane % 16), or none.
+    // Activation row of this lane (routed row lane % 16).  Lanes past the
+    // tile's rows read a valid row too: their MFMA columns are never stored.
     const int mr = lane & 15;
     const bool has_row = mr < t.rows;
     const uint8_t* px = reinterpret_cast<const uint8_t*>(x) +
                         a_row_of(t.row0 + (has_row ? mr : 0), sorted_ids, a_sorted, topk, rows_a) *
                             (int64_t)K * 2 + g * 64;
 
-    v4f acc = v4f{};
-    for (int c = 0; c < chunks; ++c) {
-      const u32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pw + (int64_t)c * 64));
-      const uint32_t sq = *reinterpret_cast<const uint16_t*>(ps + (int64_t)c * 8);
+    v4f acc0 = v4f{}, acc1 = v4f{};
+    // One K chunk: 32 codes of this lane's weight row against the matching
+    // activation values; two accumulators keep the MFMA chain short.
+    auto consume = [&](const u32x4& wq, uint32_t sq, int c) __attribute__((always_inline)) {
       const float s0 = e4m3_to_f32(sq & 0xffu), s1 = e4m3_to_f32(sq >> 8);
-      u32x4 xa[4];
+      const u32x4 x0 = ld16(px + (int64_t)c * 256), x1 = ld16(px + (int64_t)c * 256 + 16);
+      const u32x4 x2 = ld16(px + (int64_t)c * 256 + 32), x3 = ld16(px + (int64_t)c * 256 + 48);
+      acc0 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16(wq[0], s0)), __builtin_bit_cast(v8bf, x0), acc0);
+      acc1 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16(wq[1], s0)), __builtin_bit_cast(v8bf, x1), acc1);
+      acc0 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16(wq[2], s1)), __builtin_bit_cast(v8bf, x2), acc0);
+      acc1 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16(wq[3], s1)), __builtin_bit_cast(v8bf, x3), acc1);
+    };
+    auto wload = [&](int c) __attribute__((always_inline)) {
+      return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pw + (int64_t)c * 64));
+    };
+    auto sload = [&](int c) __attribute__((always_inline)) {
+      return (uint32_t)*reinterpret_cast<const uint16_t*>(ps + (int64_t)c * 8);
+    };
+
+    u32x4 wbuf[kPre];
+    uint32_t sbuf[kPre];
+    int c0 = 0;
+    if (chunks >= kPre) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        xa[i] = has_row ? ld16(px + (int64_t)c * 256 + i * 16) : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4 wd = dequant8_bf16(wq[i], i < 2 ? s0 : s1);
-        acc = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, wd), __builtin_bit_cast(v8bf, xa[i]), acc);
+      for (int i = 0; i < kPre; ++i) {
+        wbuf[i] = wload(i);
+        sbuf[i] = sload(i);
       }
+      // Steady state: every slot is consumed and refilled kPre chunks ahead.
+      for (; c0 + 2 * kPre <= chunks; c0 += kPre) {
+#pragma unroll
+        for (int i = 0; i < kPre; ++i) {
+          const u32x4 wq = wbuf[i];
+          const uint32_t sq = sbuf[i];
+          wbuf[i] = wload(c0 + kPre + i);
+          sbuf[i] = sload(c0 + kPre + i);
+          consume(wq, sq, c0 + i);
+        }
+      }
+      // Drain: chunks c0 .. c0+kPre-1 are in the slots; the rest (< kPre)
+      // is loaded as slots free up.
+#pragma unroll
+      for (int i = 0; i < kPre; ++i) {
+        const u32x4 wq = wbuf[i];
+        const uint32_t sq = sbuf[i];
+        if (c0 + kPre + i < chunks) {
+          wbuf[i] = wload(c0 + kPre + i);
+          sbuf[i] = sload(c0 + kPre + i);
+        }
+        consume(wq, sq, c0 + i);
+      }
+      c0 += kPre;
+#pragma unroll
+      for (int i = 0; i < kPre; ++i)
+        if (c0 + i < chunks) consume(wbuf[i], sbuf[i], c0 + i);
+    } else {
+      for (int c = 0; c < chunks; ++c) consume(wload(c), sload(c), c);
     }
+    const v4f acc = acc0 + acc1;
     // acc value i of lane l: weight row 4*(l/16) + i of the wave's 16, routed
     // row l % 16.
     const float gs = w_gscale[t.e];
@@ -327,7 +377,7 @@ hipError_t go(const GroupedArgs& g, bool decode, const uint16_t* x, const uint8_
   if (decode) {
     const int64_t mt_ub = (g.P + kDecM - 1) / kDecM + std::min<int64_t>(g.E, g.P);
     const int64_t items_ub = mt_ub * (SILU ? g.N / 64 : g.N / kDecNB);
-    const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus * 8);
+    const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus * 4);
     hipLaunchKernelGGL((nvfp4_decode<OUT, SILU>), dim3(grid), dim3(256), 0, stream, x, g.rows_a,
                        g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N, g.K,
                        g.out);
@@ -347,9 +397,10 @@ hipError_t go(const GroupedArgs& g, bool decode, const uint16_t* x, const uint8_
 hipError_t launch_gemm_nvfp4(const GroupedArgs& g, const uint16_t* x, const uint8_t* w,
                              const uint8_t* w_sf, const float* w_gscale, hipStream_t stream) {
   if (g.P == 0) return hipSuccess;
-  // AUTO: the streaming schedule while experts average fewer than 16 rows,
-  // and whenever N is not a multiple of the prefill tile (256).
-  const bool decode = g.sched == 1 || (g.sched == 0 && (g.P < (int64_t)16 * g.E || g.N % pf::kN != 0));
+  // The streaming schedule when asked for, under AUTO while experts average
+  // fewer than 16 rows, and whenever N is not a multiple of the prefill
+  // tile (256), which the prefill schedule cannot cover.
+  const bool decode = g.sched == 1 || g.N % pf::kN != 0 || (g.sched == 0 && g.P < (int64_t)16 * g.E);
   if (g.silu_mul) {
     switch (g.out_kind) {
       case OUT_F16: return go<OUT_F16, true>(g, decode, x, w, w_sf, w_gscale, stream);

@@ -210,6 +210,36 @@ def test_nvfp4_sorted_rows_full_code_range(sched):
     assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 sorted {sched}")
 
 
+@pytest.mark.parametrize("H", [1024, 1536, 2176, 3200])
+def test_nvfp4_decode_chunk_counts(H):
+    # K / 128 = 8, 12, 17, 25 weight chunks per lane: exactly the in-flight
+    # depth, a partial refill, one steady pass plus a tail, several passes
+    # plus a ragged tail.
+    T, E, k, I = 20, 3, 2, 128
+    d = synth.nvfp4_moe(45, T, E, k, H, I, routing="repeat")
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    y = mq.grouped_gemm_qnvfp4(dev(d["x"]), dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k,
+                               act="silu_mul", out_dtype=torch.float32, sched="decode")
+    ref = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], host(offs),
+                                     host(srt), k, act="silu_mul")["y"]
+    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 decode H={H}")
+
+
+@pytest.mark.parametrize("I", [64, 192])
+@pytest.mark.parametrize("sched", ["prefill", "auto"])
+def test_nvfp4_n_not_multiple_of_prefill_tile(I, sched):
+    # N = 2I = 128 or 384 is not a multiple of the 256-wide prefill tile:
+    # every column must still be computed.
+    T, E, k, H = 150, 5, 2, 256
+    d = synth.nvfp4_moe(46, T, E, k, H, I, routing="repeat")
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    y = mq.grouped_gemm_qnvfp4(dev(d["x"]), dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k,
+                               act="silu_mul", out_dtype=torch.float32, sched=sched)
+    ref = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], host(offs),
+                                     host(srt), k, act="silu_mul")["y"]
+    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 N={2 * I} {sched}")
+
+
 def test_both_schedules_meet_tolerance():
     # decode and prefill both sum exact bf16 products in fp32; they may round
     # differently, but both must meet the tolerance on the same input.
