@@ -8,10 +8,10 @@
 // kernel and for prefill:
 //   prefill  128x128 MFMA tiles; weights dequantized once per tile while
 //            they are staged into LDS, bf16 MFMA 32x32x16.
-//   decode   few rows per expert: each workgroup streams a block of weight
-//            rows in long contiguous runs and runs 16x16x32 bf16 MFMAs with
-//            the weights as the 16-row operand and the (at most 16) routed
-//            rows as the other, so no cross-lane reduction is needed.
+//   decode   few rows per expert: each wave streams 32 weight rows through
+//            a direct-to-LDS ring and runs 16x16x32 bf16 MFMAs with the
+//            weights as the 16-row operand and the (at most 4) routed rows
+//            as the other, so no cross-lane reduction is needed.
 #include <algorithm>
 
 #include "kernels.h"
@@ -229,144 +229,231 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
 }
 
 // ------------------------------------------------------------------ decode
-// Work item = (expert, 16-row m-tile, 64-column n-block); 4 waves, wave v
-// computes output columns [16v, 16v+16) of the block.  For SILU_MUL a block
-// covers 32 output columns: waves 0,1 the gate rows, waves 2,3 the up rows
-// of the same columns, met through LDS in the epilogue.
+// Weight streaming for few rows per expert.  The wave is the unit of work:
+// item = (tile of at most 4 routed rows of one expert, 16 output columns).
+// For SILU_MUL the wave's two 16-row weight groups are the gate rows
+// [16n, 16n+16) and the matching up rows [I+16n, ...), so both halves of an
+// output element meet in the same lane; without an activation the groups
+// are 32 consecutive weight rows.
 //
-// Weights are the MFMA's 16-row operand: lane l owns weight row (l % 16) of
-// the wave's 16 rows and, in K chunk c (128 values = 64 bytes per row), the
-// 16 bytes at (l / 16) * 16, i.e. 32 codes.  Those feed 4 MFMAs; MFMA i
-// takes codes [8i, 8i+8) of every lane's 32, so its K slot (l/16, 0..7)
-// holds K index 128c + 32(l/16) + 8i + (0..7).  The activation operand uses
-// the same slots: lane l (routed row l % 16) loads x[row][that K range].
+// Every operand reaches the wave through its own ring of LDS slots filled
+// by direct-to-LDS copies, issued kDepth chunks ahead and waited for with
+// hand-counted vmcnt waits (nothing the compiler must wait for sits in the
+// stream, so no wait drains it).  Per K chunk of 128:
+//   w0, w1  1 KB each: lane l copies bytes [16(l/16), +16) of row l%16's
+//           64-byte chunk, which is exactly what lane l feeds the MFMA;
+//   x       1 KB: 4 activation rows x 256 bytes, row r's 16-byte piece p
+//           stored at position p ^ r (the MFMA reads of 4 rows then hit
+//           distinct LDS banks);
+//   scales  per 4 chunks when K % 512 == 0 (32 rows x 32 bytes, double
+//           buffered), else per chunk (32 rows x 8 bytes).
+// The ring runs across item boundaries; tile lookups are wave-uniform
+// scalar loads, so they never wait on the vector memory counter.
 //
-// The weight stream is what bounds this schedule: each lane keeps kPre
-// chunks (kPre x 16 bytes of codes, their scales) in flight in registers,
-// so a CU has enough bytes outstanding to cover the HBM latency.
-constexpr int kDecM = 16;
-constexpr int kDecNB = 64;  // weight rows per work item
-constexpr int kPre = 8;     // weight chunks in flight per lane
+// MFMA 16x16x32 bf16 with the weights as the 16-row operand: lane l holds
+// weight row l%16, K slots [8(l/16), +8) of each sub-step; the activation
+// operand (16 columns, the tile's <=4 rows; other columns are discarded)
+// uses the same K slots.  Sub-step j of chunk c covers K = 128c + 32(l/16) +
+// 8j + (0..7), codes [8j, 8j+8) of the lane's 16 bytes.
+namespace dc {
+constexpr int kM = 4;         // routed rows per item
+constexpr int kDepth = 3;     // chunks in flight per wave
+constexpr int kWaves = 4;     // waves per workgroup (independent)
+constexpr int kSlotSuper = 3072;   // w0 | w1 | x
+constexpr int kSlotChunk = 3328;   // w0 | w1 | x | scales
+template <bool SUPER>
+constexpr int wave_bytes() { return SUPER ? kDepth * kSlotSuper + 2048 : kDepth * kSlotChunk; }
+}  // namespace dc
 
-template <int OUT, bool SILU>
-__global__ __launch_bounds__(256) void nvfp4_decode(
+typedef __attribute__((address_space(4))) const int cint_t;
+typedef __attribute__((address_space(4))) const float cfloat_t;
+// Wave-uniform reads through the constant address space: scalar loads.
+__device__ __forceinline__ int ld_uniform(const int* p, int i) { return ((cint_t*)(p))[i]; }
+__device__ __forceinline__ float ld_uniform(const float* p, int i) { return ((cfloat_t*)(p))[i]; }
+
+struct UTile {
+  int e, row0, rows, nt;
+};
+// Work item -> tile, every field wave-uniform (same numbering as sched_tile
+// with one m-tile per group: m-tile major, then n-blocks).
+__device__ __forceinline__ UTile uniform_tile(const int* tile_start, const int* __restrict__ offsets,
+                                              int E, int P, int bm, int n_tiles, int w) {
+  int bl = 0, bh = E - 1;
+  while (bl < bh) {
+    const int mid = (bl + bh + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane(tile_start[mid]) <= w) bl = mid; else bh = mid - 1;
+  }
+  const int e = __builtin_amdgcn_readfirstlane(bl);
+  const int local = w - __builtin_amdgcn_readfirstlane(tile_start[e]);
+  const int lo = min(max(ld_uniform(offsets, e), 0), P);
+  const int hi = min(max(ld_uniform(offsets, e + 1), lo), P);
+  const int mt = local / n_tiles;
+  UTile t;
+  t.e = e;
+  t.nt = local - mt * n_tiles;
+  t.row0 = lo + mt * bm;
+  t.rows = min(bm, hi - lo - mt * bm);
+  return t;
+}
+
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    default: wait_vmcnt<8>(); break;
+  }
+  asm volatile("" ::: "memory");
+}
+
+template <int OUT, bool SILU, bool SUPER>
+__global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
-    const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale,
-    const int* __restrict__ offsets, const int* __restrict__ sorted_ids, int topk, int E, int P, int N,
-    int K, void* __restrict__ out) {
+    const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale, const int* __restrict__ offsets,
+    const int* __restrict__ sorted_ids, int topk, int E, int P, int N, int K, void* __restrict__ out) {
+  constexpr int kSlot = SUPER ? dc::kSlotSuper : dc::kSlotChunk;
+  constexpr int kWave = dc::wave_bytes<SUPER>();
+  constexpr int D = dc::kDepth;
   __shared__ int tile_start[kMaxExperts + 1];
   __shared__ int sched_scratch[2 * kMaxWaves];
-  __shared__ float lds_up[2][kDecM][16 + 1];
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[dc::kWaves * kWave];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int I = N / 2;
-  // n-blocks: NONE covers 64 columns per item, SILU 32 output columns.
-  const int n_blocks = SILU ? (I / 32) : (N / kDecNB);
-  sched_build(tile_start, sched_scratch, offsets, E, P, kDecM, n_blocks);
+  const int n_blocks = SILU ? (I / 16) : (N / 32);
+  sched_build(tile_start, sched_scratch, offsets, E, P, dc::kM, n_blocks);
   const int total = tile_start[E];
-  const int64_t wrow_bytes = K / 2, srow_bytes = K / 16;
+  // Items are dealt to the fewest waves that still take the same number of
+  // rounds, so every active wave does the same number of items.
+  const int waves = gridDim.x * dc::kWaves;
+  const int rounds = (total + waves - 1) / waves;
+  const int active = rounds ? (total + rounds - 1) / rounds : 0;
+  const int wid = blockIdx.x * dc::kWaves + wv;
+  if (wid >= active) return;
   const int chunks = K / 128;
+  const int nq = ((total - wid + active - 1) / active) * chunks;  // (item, chunk) steps of this wave
+  const int64_t wrow = K / 2, srow = K / 16;
+  const int g = lane >> 4, l16 = lane & 15;
+  uint8_t* myring = ring + wv * kWave;
+  const uint32_t lb = lds_addr(myring);
+  const uint8_t* sbuf = myring + D * kSlot;  // SUPER: two 1 KB scale buffers
+  const uint32_t lsb = lb + D * kSlot;
 
-  for (int item = xcd_logical_id(blockIdx.x, gridDim.x); item < total; item += gridDim.x) {
-    const Tile t = sched_tile<1>(tile_start, offsets, E, P, kDecM, n_blocks, item);
-    // Weight row of this lane.
-    int wrow;
-    if (SILU) wrow = (wv < 2 ? 0 : I) + t.nt * 32 + (wv & 1) * 16 + (lane & 15);
-    else wrow = t.nt * kDecNB + wv * 16 + (lane & 15);
-    const int g = lane >> 4;
-    const uint8_t* pw = w + ((int64_t)t.e * N + wrow) * wrow_bytes + g * 16;
-    const uint8_t* ps = w_sf + ((int64_t)t.e * N + wrow) * srow_bytes + g * 2;
-    // Activation row of this lane (routed row lane % 16).  Lanes past the
-    // tile's rows read a valid row too: their MFMA columns are never stored.
-    const int mr = lane & 15;
-    const bool has_row = mr < t.rows;
-    const uint8_t* px = reinterpret_cast<const uint8_t*>(x) +
-                        a_row_of(t.row0 + (has_row ? mr : 0), sorted_ids, a_sorted, topk, rows_a) *
-                            (int64_t)K * 2 + g * 64;
-
-    v4f acc0 = v4f{}, acc1 = v4f{};
-    // One K chunk: 32 codes of this lane's weight row against the matching
-    // activation values; two accumulators keep the MFMA chain short.
-    auto consume = [&](const u32x4& wq, uint32_t sq, int c) __attribute__((always_inline)) {
-      const float s0 = e4m3_to_f32(sq & 0xffu), s1 = e4m3_to_f32(sq >> 8);
-      const u32x4 x0 = ld16(px + (int64_t)c * 256), x1 = ld16(px + (int64_t)c * 256 + 16);
-      const u32x4 x2 = ld16(px + (int64_t)c * 256 + 32), x3 = ld16(px + (int64_t)c * 256 + 48);
-      acc0 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16(wq[0], s0)), __builtin_bit_cast(v8bf, x0), acc0);
-      acc1 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16(wq[1], s0)), __builtin_bit_cast(v8bf, x1), acc1);
-      acc0 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16(wq[2], s1)), __builtin_bit_cast(v8bf, x2), acc0);
-      acc1 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16(wq[3], s1)), __builtin_bit_cast(v8bf, x3), acc1);
-    };
-    auto wload = [&](int c) __attribute__((always_inline)) {
-      return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pw + (int64_t)c * 64));
-    };
-    auto sload = [&](int c) __attribute__((always_inline)) {
-      return (uint32_t)*reinterpret_cast<const uint16_t*>(ps + (int64_t)c * 8);
-    };
-
-    u32x4 wbuf[kPre];
-    uint32_t sbuf[kPre];
-    int c0 = 0;
-    if (chunks >= kPre) {
+  // ---- copy cursor: sources of the next (item, chunk) to copy
+  int is_item = wid, is_c = 0;
+  const uint8_t *sw0 = nullptr, *sw1 = nullptr, *sx = nullptr, *ss = nullptr;
+  auto set_sources = [&](int item) __attribute__((always_inline)) {
+    const UTile t = uniform_tile(tile_start, offsets, E, P, dc::kM, n_blocks, item);
+    const int b0 = SILU ? t.nt * 16 : t.nt * 32;
+    const int b1 = SILU ? I + t.nt * 16 : t.nt * 32 + 16;
+    const int64_t e0 = (int64_t)t.e * N;
+    sw0 = w + (e0 + b0 + l16) * wrow + g * 16;
+    sw1 = w + (e0 + b1 + l16) * wrow + g * 16;
+    // activation slot row r = lane / 16 (rows past the tile repeat its last row)
+    int ar[dc::kM];
 #pragma unroll
-      for (int i = 0; i < kPre; ++i) {
-        wbuf[i] = wload(i);
-        sbuf[i] = sload(i);
-      }
-      // Steady state: every slot is consumed and refilled kPre chunks ahead.
-      for (; c0 + 2 * kPre <= chunks; c0 += kPre) {
-#pragma unroll
-        for (int i = 0; i < kPre; ++i) {
-          const u32x4 wq = wbuf[i];
-          const uint32_t sq = sbuf[i];
-          wbuf[i] = wload(c0 + kPre + i);
-          sbuf[i] = sload(c0 + kPre + i);
-          consume(wq, sq, c0 + i);
-        }
-      }
-      // Drain: chunks c0 .. c0+kPre-1 are in the slots; the rest (< kPre)
-      // is loaded as slots free up.
-#pragma unroll
-      for (int i = 0; i < kPre; ++i) {
-        const u32x4 wq = wbuf[i];
-        const uint32_t sq = sbuf[i];
-        if (c0 + kPre + i < chunks) {
-          wbuf[i] = wload(c0 + kPre + i);
-          sbuf[i] = sload(c0 + kPre + i);
-        }
-        consume(wq, sq, c0 + i);
-      }
-      c0 += kPre;
-#pragma unroll
-      for (int i = 0; i < kPre; ++i)
-        if (c0 + i < chunks) consume(wbuf[i], sbuf[i], c0 + i);
-    } else {
-      for (int c = 0; c < chunks; ++c) consume(wload(c), sload(c), c);
+    for (int r = 0; r < dc::kM; ++r) {
+      const int sp = t.row0 + (r < t.rows ? r : t.rows - 1);
+      const int64_t a = (a_sorted || sorted_ids == nullptr) ? (int64_t)sp
+                                                            : (int64_t)(ld_uniform(sorted_ids, sp) / topk);
+      ar[r] = (a < 0 || a >= rows_a) ? 0 : (int)a;
     }
-    const v4f acc = acc0 + acc1;
-    // acc value i of lane l: weight row 4*(l/16) + i of the wave's 16, routed
-    // row l % 16.
-    const float gs = w_gscale[t.e];
-    typedef typename OutT<OUT>::T T;
-    T* o = static_cast<T*>(out);
-    if (SILU) {
-      __syncthreads();
-      if (wv >= 2)
+    const int r = lane >> 4;
+    const int arow = r == 0 ? ar[0] : r == 1 ? ar[1] : r == 2 ? ar[2] : ar[3];
+    sx = reinterpret_cast<const uint8_t*>(x) + (int64_t)arow * K * 2 + (((lane & 15) ^ r) << 4);
+    // scales: lane -> weight group lane/32, row (lane/2)%16, half lane%2
+    const int sr = (lane >> 1) & 15;
+    ss = w_sf + (e0 + ((lane >> 5) ? b1 : b0) + sr) * srow + (lane & 1) * (SUPER ? 16 : 4);
+  };
+  auto ops_of = [&](int c) { return SUPER ? ((c & 3) == 0 ? 4 : 3) : 4; };
+  auto issue = [&](int slot) __attribute__((always_inline)) {
+    const uint32_t l = lb + slot * kSlot;
+    if (SUPER && (is_c & 3) == 0) dma16(ss + (int64_t)(is_c >> 2) * 32, lsb + ((is_c >> 2) & 1) * 1024);
+    dma16(sw0 + (int64_t)is_c * 64, l);
+    dma16(sw1 + (int64_t)is_c * 64, l + 1024);
+    dma16(sx + (int64_t)is_c * 256, l + 2048);
+    if (!SUPER) dma4(ss + (int64_t)is_c * 8, l + 3072);
+    if (++is_c == chunks) {
+      is_c = 0;
+      is_item += active;
+      if (is_item < total) set_sources(is_item);
+    }
+  };
+
+  set_sources(is_item);
+  const int npre = nq < D ? nq : D;
+  for (int i = 0; i < npre; ++i) issue(i);
+
+  // ---- compute cursor
+  int cs_item = wid, c = 0;
+  v4f acc0 = v4f{}, acc1 = v4f{};
+  const int xr = l16 & 3;  // activation slot row of MFMA column l16
+  for (int q = 0; q < nq; ++q) {
+    // copies issued after chunk q's: those of chunks q+1 .. min(q+D-1, nq-1)
+    int after = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_up[wv - 2][lane & 15][4 * (lane >> 4) + i] = gs * acc[i];
-      __syncthreads();
-      if (wv < 2 && has_row)
+    for (int j = 1; j < D; ++j)
+      if (q + j < nq) after += ops_of((c + j) % chunks);
+    wait_vm(after);
+    const int slot = q % D;
+    const uint8_t* sp = myring + slot * kSlot;
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(sp + lane * 16);
+    const u32x4 w1 = *reinterpret_cast<const u32x4*>(sp + 1024 + lane * 16);
+    u32x4 xv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int col = t.nt * 32 + wv * 16 + 4 * (lane >> 4) + i;
-          const float gv = gs * acc[i], uv = lds_up[wv][lane & 15][4 * (lane >> 4) + i];
-          o[(int64_t)(t.row0 + mr) * I + col] = OutT<OUT>::from(silu(gv) * uv);
+    for (int j = 0; j < 4; ++j)
+      xv[j] = *reinterpret_cast<const u32x4*>(sp + 2048 + xr * 256 + (((4 * g + j) ^ xr) << 4));
+    uint32_t q0, q1;
+    if (SUPER) {
+      const uint8_t* sb = sbuf + ((c >> 2) & 1) * 1024 + l16 * 32 + (c & 3) * 8 + 2 * g;
+      q0 = *reinterpret_cast<const uint16_t*>(sb);
+      q1 = *reinterpret_cast<const uint16_t*>(sb + 512);
+    } else {
+      q0 = *reinterpret_cast<const uint16_t*>(sp + 3072 + l16 * 8 + 2 * g);
+      q1 = *reinterpret_cast<const uint16_t*>(sp + 3072 + 128 + l16 * 8 + 2 * g);
+    }
+    // the slot is refilled once its reads have landed
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (q + D < nq) issue(slot);
+    const float a0 = e4m3_to_f32(q0 & 0xffu), a1 = e4m3_to_f32(q0 >> 8);
+    const float b0 = e4m3_to_f32(q1 & 0xffu), b1 = e4m3_to_f32(q1 >> 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc0 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16_hi(w0[j], j < 2 ? a0 : a1)),
+                                __builtin_bit_cast(v8bf, xv[j]), acc0);
+      acc1 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16_hi(w1[j], j < 2 ? b0 : b1)),
+                                __builtin_bit_cast(v8bf, xv[j]), acc1);
+    }
+    if (++c == chunks) {
+      // acc value i of lane l: weight row 4(l/16)+i of each 16-row group,
+      // routed row l%16 of the tile.
+      const UTile t = uniform_tile(tile_start, offsets, E, P, dc::kM, n_blocks, cs_item);
+      const float gs = ld_uniform(w_gscale, t.e);
+      typedef typename OutT<OUT>::T T;
+      T* o = static_cast<T*>(out);
+      if (l16 < t.rows) {
+        const int64_t row = t.row0 + l16;
+        if (SILU) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            o[row * I + t.nt * 16 + 4 * g + i] = OutT<OUT>::from(silu(gs * acc0[i]) * (gs * acc1[i]));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            o[row * N + t.nt * 32 + 4 * g + i] = OutT<OUT>::from(gs * acc0[i]);
+            o[row * N + t.nt * 32 + 16 + 4 * g + i] = OutT<OUT>::from(gs * acc1[i]);
+          }
         }
-    } else if (has_row) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int col = t.nt * kDecNB + wv * 16 + 4 * (lane >> 4) + i;
-        o[(int64_t)(t.row0 + mr) * N + col] = OutT<OUT>::from(gs * acc[i]);
       }
+      acc0 = v4f{};
+      acc1 = v4f{};
+      c = 0;
+      cs_item += active;
     }
   }
 }
@@ -375,12 +462,17 @@ template <int OUT, bool SILU>
 hipError_t go(const GroupedArgs& g, bool decode, const uint16_t* x, const uint8_t* w,
               const uint8_t* sf, const float* gsc, hipStream_t stream) {
   if (decode) {
-    const int64_t mt_ub = (g.P + kDecM - 1) / kDecM + std::min<int64_t>(g.E, g.P);
-    const int64_t items_ub = mt_ub * (SILU ? g.N / 64 : g.N / kDecNB);
-    const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus * 4);
-    hipLaunchKernelGGL((nvfp4_decode<OUT, SILU>), dim3(grid), dim3(256), 0, stream, x, g.rows_a,
-                       g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N, g.K,
-                       g.out);
+    // two workgroups (8 independent waves) per CU; the kernel deals the
+    // items over the waves itself
+    const int grid = g.num_cus * 2;
+    if (g.K % 512 == 0)
+      hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, true>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
+                         g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N,
+                         g.K, g.out);
+    else
+      hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, false>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
+                         g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N,
+                         g.K, g.out);
   } else {
     const int64_t mt_ub = (g.P + pf::kM - 1) / pf::kM + std::min<int64_t>(g.E, g.P);
     const int64_t items_ub = mt_ub * (g.N / pf::kN);

@@ -32,6 +32,22 @@ __device__ __forceinline__ u32x4 dequant8_bf16(u32 word, float scale) {
                pack_bf16x2(p2.x * scale, p2.y * scale), pack_bf16x2(p3.x * scale, p3.y * scale)};
 }
 
+// The same 8 bf16 values packed by taking the high halves of the fp32
+// products with one byte permute per pair: the products are exact bf16
+// values, so their low halves are zero and no rounding is skipped.  The
+// products are formed element by element (a two-float vector times a scalar
+// is not used on the conversion result).
+__device__ __forceinline__ u32 hi_halves(float lo, float hi) {
+  // v_perm_b32: selector bytes 0-3 pick from the second operand
+  return __builtin_amdgcn_perm(__builtin_bit_cast(u32, hi), __builtin_bit_cast(u32, lo), 0x07060302u);
+}
+__device__ __forceinline__ u32x4 dequant8_bf16_hi(u32 word, float scale) {
+  const v2f p0 = e2m1x2_f32<0>(word), p1 = e2m1x2_f32<1>(word);
+  const v2f p2 = e2m1x2_f32<2>(word), p3 = e2m1x2_f32<3>(word);
+  return u32x4{hi_halves(p0.x * scale, p0.y * scale), hi_halves(p1.x * scale, p1.y * scale),
+               hi_halves(p2.x * scale, p2.y * scale), hi_halves(p3.x * scale, p3.y * scale)};
+}
+
 // Packed pair of output elements of kind KIND (bf16 or f16) from two floats.
 template <int KIND>
 __device__ __forceinline__ u32 pack2(float lo, float hi) {
