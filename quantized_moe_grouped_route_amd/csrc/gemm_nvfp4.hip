@@ -236,33 +236,42 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
 // output element meet in the same lane; without an activation the groups
 // are 32 consecutive weight rows.
 //
-// Every operand reaches the wave through its own ring of LDS slots filled
-// by direct-to-LDS copies, issued kDepth chunks ahead and waited for with
-// hand-counted vmcnt waits (nothing the compiler must wait for sits in the
-// stream, so no wait drains it).  Per K chunk of 128:
-//   w0, w1  1 KB each: lane l copies bytes [16(l/16), +16) of row l%16's
-//           64-byte chunk, which is exactly what lane l feeds the MFMA;
-//   x       1 KB: 4 activation rows x 256 bytes, row r's 16-byte piece p
-//           stored at position p ^ r (the MFMA reads of 4 rows then hit
-//           distinct LDS banks);
-//   scales  per 4 chunks when K % 512 == 0 (32 rows x 32 bytes, double
-//           buffered), else per chunk (32 rows x 8 bytes).
-// The ring runs across item boundaries; tile lookups are wave-uniform
+// Every operand reaches the wave through LDS buffers filled by
+// direct-to-LDS copies issued kDepth steps ahead and waited for with vmcnt
+// waits counted from the copies actually issued: nothing the compiler waits
+// for sits in the stream, so no wait drains it.  The number of memory
+// requests in flight per CU is what bounds this stream, so copies read
+// whole 128-byte lines where the layout allows.
+//   WIDE (K % 512 == 0), a step is 2 chunks of K = 128:
+//     weights      per step and group, two copies of 8 rows x 128 bytes;
+//                  16-byte piece p of row r stored at position
+//                  p ^ ((r >> 1) & 7), so the 16 rows read by one MFMA
+//                  operand fall in distinct LDS banks;
+//     activations  per 4 chunks ("superchunk", double buffered, parity from
+//                  a running count so it alternates across items too): one
+//                  1 KB copy per routed row of the tile, piece p of row r at
+//                  position p ^ r;
+//     scales       per superchunk, one 1 KB copy of 32 rows x 32 bytes.
+//   otherwise, a step is one chunk: 16 rows x 64 weight bytes per group,
+//     4 rows x 256 activation bytes (rows past the tile repeat its last
+//     row), 32 rows x 8 scale bytes.
+// The stream runs across item boundaries; tile lookups are wave-uniform
 // scalar loads, so they never wait on the vector memory counter.
 //
 // MFMA 16x16x32 bf16 with the weights as the 16-row operand: lane l holds
 // weight row l%16, K slots [8(l/16), +8) of each sub-step; the activation
-// operand (16 columns, the tile's <=4 rows; other columns are discarded)
-// uses the same K slots.  Sub-step j of chunk c covers K = 128c + 32(l/16) +
-// 8j + (0..7), codes [8j, 8j+8) of the lane's 16 bytes.
+// operand (16 columns, the tile's <= 4 rows; other columns are discarded)
+// uses the same K slots.  Sub-step j of chunk c covers K = 128c + 32(l/16)
+// + 8j + (0..7), codes [8j, 8j+8) of the lane's 16 bytes of that chunk.
 namespace dc {
-constexpr int kM = 4;         // routed rows per item
-constexpr int kDepth = 3;     // chunks in flight per wave
-constexpr int kWaves = 4;     // waves per workgroup (independent)
-constexpr int kSlotSuper = 3072;   // w0 | w1 | x
-constexpr int kSlotChunk = 3328;   // w0 | w1 | x | scales
-template <bool SUPER>
-constexpr int wave_bytes() { return SUPER ? kDepth * kSlotSuper + 2048 : kDepth * kSlotChunk; }
+constexpr int kM = 4;          // routed rows per item
+constexpr int kWaves = 4;      // waves per workgroup (independent)
+template <bool WIDE> constexpr int cps() { return WIDE ? 2 : 1; }            // chunks per step
+template <bool WIDE> constexpr int depth() { return WIDE ? 2 : 3; }          // steps in flight
+template <bool WIDE> constexpr int slot_bytes() { return WIDE ? 4096 : 3328; }
+// WIDE: + activation buffers [2][4 rows][1 KB] + scale buffers [2][1 KB]
+template <bool WIDE>
+constexpr int wave_bytes() { return depth<WIDE>() * slot_bytes<WIDE>() + (WIDE ? 8192 + 2048 : 0); }
 }  // namespace dc
 
 typedef __attribute__((address_space(4))) const int cint_t;
@@ -296,6 +305,7 @@ __device__ __forceinline__ UTile uniform_tile(const int* tile_start, const int* 
   return t;
 }
 
+// s_waitcnt vmcnt(n) for a run-time n in [0, 15]
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
     case 0: wait_vmcnt<0>(); break;
@@ -306,19 +316,30 @@ __device__ __forceinline__ void wait_vm(int n) {
     case 5: wait_vmcnt<5>(); break;
     case 6: wait_vmcnt<6>(); break;
     case 7: wait_vmcnt<7>(); break;
-    default: wait_vmcnt<8>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    default: wait_vmcnt<15>(); break;
   }
   asm volatile("" ::: "memory");
 }
 
-template <int OUT, bool SILU, bool SUPER>
+template <int OUT, bool SILU, bool WIDE>
 __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale, const int* __restrict__ offsets,
     const int* __restrict__ sorted_ids, int topk, int E, int P, int N, int K, void* __restrict__ out) {
-  constexpr int kSlot = SUPER ? dc::kSlotSuper : dc::kSlotChunk;
-  constexpr int kWave = dc::wave_bytes<SUPER>();
-  constexpr int D = dc::kDepth;
+  constexpr int CPS = dc::cps<WIDE>();
+  constexpr int D = dc::depth<WIDE>();
+  constexpr int kSlot = dc::slot_bytes<WIDE>();
+  constexpr int kWave = dc::wave_bytes<WIDE>();
+  // a superchunk buffer is refilled D steps before its next use; the
+  // previous superchunk (2 steps) must be consumed by then
+  static_assert(!WIDE || D <= 2, "superchunk double buffer");
   __shared__ int tile_start[kMaxExperts + 1];
   __shared__ int sched_scratch[2 * kMaxWaves];
   __shared__ __attribute__((aligned(1024))) uint8_t ring[dc::kWaves * kWave];
@@ -335,26 +356,40 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
   const int active = rounds ? (total + rounds - 1) / rounds : 0;
   const int wid = blockIdx.x * dc::kWaves + wv;
   if (wid >= active) return;
-  const int chunks = K / 128;
-  const int nq = ((total - wid + active - 1) / active) * chunks;  // (item, chunk) steps of this wave
+  const int steps = K / (128 * CPS);                                 // per item
+  const int nq = ((total - wid + active - 1) / active) * steps;     // steps of this wave
   const int64_t wrow = K / 2, srow = K / 16;
   const int g = lane >> 4, l16 = lane & 15;
   uint8_t* myring = ring + wv * kWave;
   const uint32_t lb = lds_addr(myring);
-  const uint8_t* sbuf = myring + D * kSlot;  // SUPER: two 1 KB scale buffers
-  const uint32_t lsb = lb + D * kSlot;
+  const uint8_t* xbuf = myring + D * kSlot;  // WIDE: [2][4 rows][1 KB]
+  const uint8_t* sbuf = xbuf + 8192;          // WIDE: [2][1 KB]
+  const uint32_t lxb = lb + D * kSlot, lsb = lxb + 8192;
 
-  // ---- copy cursor: sources of the next (item, chunk) to copy
-  int is_item = wid, is_c = 0;
-  const uint8_t *sw0 = nullptr, *sw1 = nullptr, *sx = nullptr, *ss = nullptr;
+  // ---- copy cursor: sources of the next (item, step) to copy
+  int is_item = wid, is_st = 0, is_rows = 0, is_sc = 0;
+  // WIDE: weight row base of group grp, half h at wsrc[2 grp + h]
+  const uint8_t* wsrc[4];
+  const uint8_t *sx = nullptr, *ss = nullptr;
+  int64_t xrow[dc::kM];
   auto set_sources = [&](int item) __attribute__((always_inline)) {
     const UTile t = uniform_tile(tile_start, offsets, E, P, dc::kM, n_blocks, item);
     const int b0 = SILU ? t.nt * 16 : t.nt * 32;
     const int b1 = SILU ? I + t.nt * 16 : t.nt * 32 + 16;
     const int64_t e0 = (int64_t)t.e * N;
-    sw0 = w + (e0 + b0 + l16) * wrow + g * 16;
-    sw1 = w + (e0 + b1 + l16) * wrow + g * 16;
-    // activation slot row r = lane / 16 (rows past the tile repeat its last row)
+    if (WIDE) {
+      // copy h of a group: lane l -> row 8h + l/8, piece (l%8) ^ ((row >> 1) & 7)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 8 * h + (lane >> 3);
+        const int off = (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+        wsrc[h] = w + (e0 + b0 + r) * wrow + off;
+        wsrc[2 + h] = w + (e0 + b1 + r) * wrow + off;
+      }
+    } else {
+      wsrc[0] = w + (e0 + b0 + l16) * wrow + g * 16;
+      wsrc[2] = w + (e0 + b1 + l16) * wrow + g * 16;
+    }
     int ar[dc::kM];
 #pragma unroll
     for (int r = 0; r < dc::kM; ++r) {
@@ -363,23 +398,50 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
                                                             : (int64_t)(ld_uniform(sorted_ids, sp) / topk);
       ar[r] = (a < 0 || a >= rows_a) ? 0 : (int)a;
     }
-    const int r = lane >> 4;
-    const int arow = r == 0 ? ar[0] : r == 1 ? ar[1] : r == 2 ? ar[2] : ar[3];
-    sx = reinterpret_cast<const uint8_t*>(x) + (int64_t)arow * K * 2 + (((lane & 15) ^ r) << 4);
+    is_rows = t.rows;
+    if (WIDE) {
+#pragma unroll
+      for (int r = 0; r < dc::kM; ++r) xrow[r] = (int64_t)ar[r] * K * 2 + ((lane ^ r) << 4);
+    } else {
+      const int r = lane >> 4;
+      const int arow = r == 0 ? ar[0] : r == 1 ? ar[1] : r == 2 ? ar[2] : ar[3];
+      sx = reinterpret_cast<const uint8_t*>(x) + (int64_t)arow * K * 2 + (((lane & 15) ^ r) << 4);
+    }
     // scales: lane -> weight group lane/32, row (lane/2)%16, half lane%2
     const int sr = (lane >> 1) & 15;
-    ss = w_sf + (e0 + ((lane >> 5) ? b1 : b0) + sr) * srow + (lane & 1) * (SUPER ? 16 : 4);
+    ss = w_sf + (e0 + ((lane >> 5) ? b1 : b0) + sr) * srow + (lane & 1) * (WIDE ? 16 : 4);
   };
-  auto ops_of = [&](int c) { return SUPER ? ((c & 3) == 0 ? 4 : 3) : 4; };
+  uint32_t ops_ring = 0;  // copies issued per slot, 4 bits each
   auto issue = [&](int slot) __attribute__((always_inline)) {
     const uint32_t l = lb + slot * kSlot;
-    if (SUPER && (is_c & 3) == 0) dma16(ss + (int64_t)(is_c >> 2) * 32, lsb + ((is_c >> 2) & 1) * 1024);
-    dma16(sw0 + (int64_t)is_c * 64, l);
-    dma16(sw1 + (int64_t)is_c * 64, l + 1024);
-    dma16(sx + (int64_t)is_c * 256, l + 2048);
-    if (!SUPER) dma4(ss + (int64_t)is_c * 8, l + 3072);
-    if (++is_c == chunks) {
-      is_c = 0;
+    int ops;
+    if (WIDE) {
+      ops = 4;
+      if ((is_st & 1) == 0) {  // first step of a superchunk
+        const int bsel = is_sc & 1;
+        const int64_t sc = is_st >> 1;
+        dma16(ss + sc * 32, lsb + bsel * 1024);
+        const uint8_t* xs = reinterpret_cast<const uint8_t*>(x) + sc * 1024;
+        for (int r = 0; r < is_rows; ++r) dma16(xs + xrow[r], lxb + bsel * 4096 + r * 1024);
+        ops += 1 + is_rows;
+        ++is_sc;
+      }
+      const int64_t o = (int64_t)is_st * 128;
+      dma16(wsrc[0] + o, l);
+      dma16(wsrc[1] + o, l + 1024);
+      dma16(wsrc[2] + o, l + 2048);
+      dma16(wsrc[3] + o, l + 3072);
+    } else {
+      ops = 4;
+      const int64_t o = (int64_t)is_st * 64;
+      dma16(wsrc[0] + o, l);
+      dma16(wsrc[2] + o, l + 1024);
+      dma16(sx + (int64_t)is_st * 256, l + 2048);
+      dma4(ss + (int64_t)is_st * 8, l + 3072);
+    }
+    ops_ring = (ops_ring & ~(15u << (4 * slot))) | ((uint32_t)ops << (4 * slot));
+    if (++is_st == steps) {
+      is_st = 0;
       is_item += active;
       if (is_item < total) set_sources(is_item);
     }
@@ -390,46 +452,62 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
   for (int i = 0; i < npre; ++i) issue(i);
 
   // ---- compute cursor
-  int cs_item = wid, c = 0;
+  int cs_item = wid, st = 0, cs_sc = 0, cbuf = 0;
   v4f acc0 = v4f{}, acc1 = v4f{};
-  const int xr = l16 & 3;  // activation slot row of MFMA column l16
+  const int xr = l16 & 3;                 // activation row of MFMA column l16
+  const int wkey = (l16 >> 1) & 7;        // WIDE weight swizzle of row l16
   for (int q = 0; q < nq; ++q) {
-    // copies issued after chunk q's: those of chunks q+1 .. min(q+D-1, nq-1)
+    // copies issued after step q's: those of steps q+1 .. min(q+D-1, nq-1)
     int after = 0;
 #pragma unroll
     for (int j = 1; j < D; ++j)
-      if (q + j < nq) after += ops_of((c + j) % chunks);
+      if (q + j < nq) after += (ops_ring >> (4 * ((q + j) % D))) & 15;
     wait_vm(after);
     const int slot = q % D;
     const uint8_t* sp = myring + slot * kSlot;
-    const u32x4 w0 = *reinterpret_cast<const u32x4*>(sp + lane * 16);
-    const u32x4 w1 = *reinterpret_cast<const u32x4*>(sp + 1024 + lane * 16);
-    u32x4 xv[4];
+    u32x4 w0[CPS], w1[CPS], xv[CPS][4];
+    uint32_t q0[CPS], q1[CPS];
+    if (WIDE) {
+      if ((st & 1) == 0) cbuf = cs_sc++ & 1;
+      const uint8_t* xb = xbuf + cbuf * 4096 + xr * 1024;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      xv[j] = *reinterpret_cast<const u32x4*>(sp + 2048 + xr * 256 + (((4 * g + j) ^ xr) << 4));
-    uint32_t q0, q1;
-    if (SUPER) {
-      const uint8_t* sb = sbuf + ((c >> 2) & 1) * 1024 + l16 * 32 + (c & 3) * 8 + 2 * g;
-      q0 = *reinterpret_cast<const uint16_t*>(sb);
-      q1 = *reinterpret_cast<const uint16_t*>(sb + 512);
+      for (int cp = 0; cp < CPS; ++cp) {
+        const int pos = ((4 * cp + g) ^ wkey) << 4;
+        w0[cp] = *reinterpret_cast<const u32x4*>(sp + l16 * 128 + pos);
+        w1[cp] = *reinterpret_cast<const u32x4*>(sp + 2048 + l16 * 128 + pos);
+        const int cc = 2 * (st & 1) + cp;  // chunk within the superchunk
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xv[cp][j] = *reinterpret_cast<const u32x4*>(xb + (((16 * cc + 4 * g + j) ^ xr) << 4));
+        const uint8_t* sb = sbuf + cbuf * 1024 + l16 * 32 + cc * 8 + 2 * g;
+        q0[cp] = *reinterpret_cast<const uint16_t*>(sb);
+        q1[cp] = *reinterpret_cast<const uint16_t*>(sb + 512);
+      }
     } else {
-      q0 = *reinterpret_cast<const uint16_t*>(sp + 3072 + l16 * 8 + 2 * g);
-      q1 = *reinterpret_cast<const uint16_t*>(sp + 3072 + 128 + l16 * 8 + 2 * g);
+      w0[0] = *reinterpret_cast<const u32x4*>(sp + lane * 16);
+      w1[0] = *reinterpret_cast<const u32x4*>(sp + 1024 + lane * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xv[0][j] = *reinterpret_cast<const u32x4*>(sp + 2048 + xr * 256 + (((4 * g + j) ^ xr) << 4));
+      q0[0] = *reinterpret_cast<const uint16_t*>(sp + 3072 + l16 * 8 + 2 * g);
+      q1[0] = *reinterpret_cast<const uint16_t*>(sp + 3072 + 128 + l16 * 8 + 2 * g);
     }
     // the slot is refilled once its reads have landed
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (q + D < nq) issue(slot);
-    const float a0 = e4m3_to_f32(q0 & 0xffu), a1 = e4m3_to_f32(q0 >> 8);
-    const float b0 = e4m3_to_f32(q1 & 0xffu), b1 = e4m3_to_f32(q1 >> 8);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc0 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16_hi(w0[j], j < 2 ? a0 : a1)),
-                                __builtin_bit_cast(v8bf, xv[j]), acc0);
-      acc1 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16_hi(w1[j], j < 2 ? b0 : b1)),
-                                __builtin_bit_cast(v8bf, xv[j]), acc1);
+    for (int cp = 0; cp < CPS; ++cp) {
+      const float a0 = e4m3_to_f32(q0[cp] & 0xffu), a1 = e4m3_to_f32(q0[cp] >> 8);
+      const float b0 = e4m3_to_f32(q1[cp] & 0xffu), b1 = e4m3_to_f32(q1[cp] >> 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc0 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16_hi(w0[cp][j], j < 2 ? a0 : a1)),
+                                  __builtin_bit_cast(v8bf, xv[cp][j]), acc0);
+        acc1 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16_hi(w1[cp][j], j < 2 ? b0 : b1)),
+                                  __builtin_bit_cast(v8bf, xv[cp][j]), acc1);
+      }
     }
-    if (++c == chunks) {
+    if (++st == steps) {
       // acc value i of lane l: weight row 4(l/16)+i of each 16-row group,
       // routed row l%16 of the tile.
       const UTile t = uniform_tile(tile_start, offsets, E, P, dc::kM, n_blocks, cs_item);
@@ -452,7 +530,7 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
       }
       acc0 = v4f{};
       acc1 = v4f{};
-      c = 0;
+      st = 0;
       cs_item += active;
     }
   }

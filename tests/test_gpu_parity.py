@@ -240,6 +240,21 @@ def test_nvfp4_n_not_multiple_of_prefill_tile(I, sched):
     assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 N={2 * I} {sched}")
 
 
+@pytest.mark.parametrize("act", ["silu_mul", "none"])
+def test_nvfp4_decode_several_items_per_wave(act):
+    # More 4-row tiles x column blocks than the streaming schedule has waves,
+    # so each wave runs several items back to back, with K / 512 = 3 (an odd
+    # number of 4-chunk groups per item) and ragged last tiles.
+    T, E, k, H, I = 203, 4, 2, 1536, 512
+    d = synth.nvfp4_moe(47, T, E, k, H, I, routing="repeat")
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    y = mq.grouped_gemm_qnvfp4(dev(d["x"]), dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k,
+                               act=act, out_dtype=torch.float32, sched="decode")
+    ref = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], host(offs),
+                                     host(srt), k, act=act)["y"]
+    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 decode many items {act}")
+
+
 def test_both_schedules_meet_tolerance():
     # decode and prefill both sum exact bf16 products in fp32; they may round
     # differently, but both must meet the tolerance on the same input.
