@@ -16,6 +16,8 @@ reordering.  Sources, by page:
     scales and 128x128 B scales; the M-contiguous A-scale layout).
   * nvfp4-megamoe-kernel, tilelang_kernels.py, grouped_gemm_fp4 (NVFP4 routed
     grouped GEMM and weighted scatter-add).
+  * (CUTLASS discussion #2855 also fixes the per-token int4 quantization of
+    fp16 activations; its rule is a reading, see quant.py.)
   * megamoe_rm.cu (route_prep, fc1_rm, fc2_rm, combine kernels: stable
     per-expert ordering, -1 ids, per-expert global scale, SiLU-gated FC1,
     k-ordered fp32 combine).
@@ -32,5 +34,6 @@ from .gemm import (grouped_gemm_qint4, grouped_gemm_qfp8_block, grouped_gemm_qnv
                    gemm_rows)
 from .combine import scatter_combine
 from .layer import int4_layer, nvfp4_layer, fp8_dense
+from .quant import quantize_int4_rows
 
 __all__ = [n for n in dir() if not n.startswith("_")]
