@@ -12,6 +12,8 @@ synthetic input already resident in HBM:
   3  NVFP4 W4A16 prefill, 4096 tokens, Zipf(1.1) routing: as 2
   4  W4A4 INT4 Mixtral-like, 8192 tokens, E=8, top-2, H=4096 I=14336:
      route + FC1 (SiLU-gated) + FC2 (int4 rows in sorted order) + combine
+  5  per-row INT4 quantization of 16384 fp16 rows of 14336 (the FC2 input
+     of 4 in a full W4A4 chain)
 Prints ONE JSON line: whole-path throughput, the dominant kernel's roofline
 fraction (its launches timed with HIP events on the launch stream inside the
 timed region) and the CPU oracle's throughput on the host as a reported
@@ -82,9 +84,15 @@ class Workload:
         self.mq, self.idx = mq, idx
         self.cfg = synth.WORKLOADS[idx]
         self.d = d = synth.workload(idx)
-        self.E, self.k, self.T = d["E"], d["k"], d["T"]
+        if self.cfg["kind"] == "quant":
+            self.E, self.k, self.T = 1, 1, self.cfg["rows"]
+        else:
+            self.E, self.k, self.T = d["E"], d["k"], d["T"]
         T, k, E = self.T, self.k, self.E
         P = T * k
+        if self.cfg["kind"] == "quant":
+            self._init_quant(torch)
+            return
         self.ids = _dev(d["topk_ids"])
         self.tw = _dev(d["topk_weights"])
         i32 = dict(dtype=torch.int32, device="cuda")
@@ -143,12 +151,27 @@ class Workload:
                 self.dom = ("nvfp4_prefill", ["gemm_nvfp4.hip", "nvfp4.h", "common.h", "tile.h", "pipeline.h"], "mfma",
                             PEAK["bf16"])
 
+    def _init_quant(self, torch):
+        rows, K = self.cfg["rows"], self.cfg["K"]
+        self.x = _dev(self.d["x"])
+        self.q = torch.empty(rows, K // 2, dtype=torch.uint8, device="cuda")
+        self.qs = torch.empty(rows, dtype=torch.float32, device="cuda")
+        self.weight_bytes = float(rows * (2 * K + K // 2 + 4))
+        self.flops = 0.0
+        self.dtype = "f16_to_int4"
+        self.dom = ("quant_int4_rows", ["quant.hip", "common.h"], "hbm", PEAK["hbm_GBps"])
+
     def step(self, ev=None):
         """One pass of the path; `ev` = (start, end) events around the
         dominant kernel."""
         mq = self.mq
-        offs, srt, p2s, _ = mq.moe_route_prep(self.ids, self.E, out=self.route_out, workspace=self.ws)
         kind = self.cfg["kind"]
+        if kind == "quant":
+            if ev: ev[0].record()
+            mq.quantize_int4_rows(self.x, q=self.q, scale=self.qs)
+            if ev: ev[1].record()
+            return
+        offs, srt, p2s, _ = mq.moe_route_prep(self.ids, self.E, out=self.route_out, workspace=self.ws)
         if kind == "fp8":
             if ev: ev[0].record()
             mq.grouped_gemm_qfp8_block(self.a, self.sa, self.w, self.sw, offs, srt, self.k, out=self.y)
@@ -178,13 +201,15 @@ class Workload:
 
     def dominant_launches(self):
         """(launches of the dominant kernel per step, index of the timed one)."""
-        return (1, 0) if self.cfg["kind"] == "fp8" or self.idx == 0 else (2, 0)
+        return (1, 0) if self.cfg["kind"] in ("fp8", "quant") or self.idx == 0 else (2, 0)
 
     def dominant_bytes(self):
         """Fewest HBM bytes one launch of the dominant kernel can move: every
         operand read once, every output written once."""
         d, P = self.d, self.T * self.k
         kind = self.cfg["kind"]
+        if kind == "quant":
+            return self.weight_bytes
         if kind == "fp8":
             N, K = d["N"], d["K"]
             return float(P * K + d["w"].size + d["a_scale"].size * 4 + d["w_scale"].size * 4 + P * N * 2)
@@ -200,6 +225,8 @@ class Workload:
         (value, unit) in bytes (HBM-bound) or flops (MFMA-bound)."""
         d = self.d
         kind = self.cfg["kind"]
+        if kind == "quant":
+            return self.weight_bytes, "byte"
         if kind == "fp8":
             return 2.0 * self.T * self.k * d["N"] * d["K"], "flop"
         if kind == "int4":
@@ -219,10 +246,20 @@ def cpu_baseline(idx: int, d, budget_s: float = 10.0):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
     except Exception:
         cores = os.cpu_count()
-    kind = {0: "int4", 1: "fp8", 2: "nvfp4", 3: "nvfp4", 4: "int4"}[idx]
+    kind = {0: "int4", 1: "fp8", 2: "nvfp4", 3: "nvfp4", 4: "int4", 5: "quant"}[idx]
+    times = []
+    if kind == "quant":
+        x = d["x"]
+        rows = np.arange(0, x.shape[0], 64)
+        nbytes = rows.size * (2 * x.shape[1] + x.shape[1] // 2 + 4)
+        while sum(times) < budget_s and len(times) < 5:
+            t = time.perf_counter()
+            oracle.quantize_int4_rows(x[rows])
+            times.append(time.perf_counter() - t)
+        return dict(value=nbytes / float(np.median(times)) / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                    sample=f"{rows.size} of {x.shape[0]} rows, median of {len(times)} runs")
     off, srt, p2s, _ = oracle.route_prep(d["topk_ids"], d["E"])
     n = int(off[-1])
-    times = []
     if kind == "fp8":
         sample = "the whole workload (all rows)"
         work = 2.0 * n * d["N"] * d["K"]
@@ -297,13 +334,20 @@ def summarize_profiles(idx: int, pdir: str, steps: int = 50, warmup: int = 10):
     import synth
     cfg = synth.WORKLOADS[idx]
     wl = Workload.__new__(Workload)  # host-side fields only
-    wl.idx, wl.cfg, wl.d = idx, cfg, synth.workload(idx)
-    wl.T, wl.k, wl.E = wl.d["T"], wl.d["k"], wl.d["E"]
+    wl.idx, wl.cfg = idx, cfg
+    if cfg["kind"] == "quant":
+        wl.d = {}
+        wl.T, wl.k, wl.E = cfg["rows"], 1, 1
+        wl.weight_bytes = float(cfg["rows"] * (2 * cfg["K"] + cfg["K"] // 2 + 4))
+    else:
+        wl.d = synth.workload(idx)
+        wl.T, wl.k, wl.E = wl.d["T"], wl.d["k"], wl.d["E"]
     d = wl.d
-    tag = {"fp8": "fp8_prefill", "int4": "int4_prefill"}.get(cfg["kind"]) or \
+    tag = {"fp8": "fp8_prefill", "int4": "int4_prefill", "quant": "quant_int4_rows"}.get(cfg["kind"]) or \
         ("nvfp4_decode" if idx == 2 else "nvfp4_prefill")
     srcs = {"fp8_prefill": ["gemm_fp8.hip", "common.h", "tile.h", "pipeline.h"],
-            "int4_prefill": ["gemm_int4.hip", "common.h", "tile.h"]}.get(
+            "int4_prefill": ["gemm_int4.hip", "common.h", "tile.h"],
+            "quant_int4_rows": ["quant.hip", "common.h"]}.get(
         tag, ["gemm_nvfp4.hip", "nvfp4.h", "common.h", "tile.h", "pipeline.h"])
     if cfg["kind"] == "nvfp4":
         H, I = d["H"], d["I"]
@@ -392,7 +436,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device 5 times (a kernel of known traffic "
@@ -463,7 +507,7 @@ def main():
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     cfg = wl.cfg
-    if args.workload == 2:
+    if args.workload in (2, 5):
         value, unit = wl.weight_bytes / (ms * 1e-3) / 1e9, "GB/s"
     else:
         value, unit = wl.flops / (ms * 1e-3) / 1e12, "TFLOP/s"

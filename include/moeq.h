@@ -189,6 +189,26 @@ moeq_status grouped_gemm_qnvfp4(const void* x, int64_t rows_a, moeq_arow a_row,
                                 moeq_sched sched, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_quantize_int4 - per-row symmetric INT4 quantization of activations.
+ * [W4A4] quantizes the fp16 activations per token to int4 (the token scale
+ * is then applied with the channel scale in the GEMM epilogue); the page
+ * gives no rounding rule, the one used is:
+ *   amax = max_k |x[r][k]|,  scale[r] = amax / 7,
+ *   code = clamp(rne(x[r][k] * (7 / amax)), -8, 7)
+ * with each division and the product one fp32 operation; a row with
+ * amax < 2^-120 (an all-zero row included) gives zeros and scale 1.
+ *
+ *   x      [rows][K] x_dtype (F16 | BF16 | F32), rows contiguous
+ *   q      uint8 [rows][K/2]  two's-complement codes, element 2b in the
+ *          low nibble of byte b (grouped_gemm_qint4's activation layout)
+ *   scale  f32 [rows]
+ * Requires K % 16 == 0 (else MOEQ_EALIGN), x and q 16-byte aligned, scale
+ * 4-byte aligned.  NaN or infinite inputs give unspecified codes.
+ * ---------------------------------------------------------------------- */
+moeq_status moe_quantize_int4(const void* x, moeq_dtype x_dtype, int64_t rows, int64_t K, uint8_t* q,
+                              float* scale, void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_scatter_combine - weighted sum of each token's expert rows.
  * [MMRM] combine (a token's pairs that have an expert, summed in slot
  * order in fp32, one rounding); [TLK] zero output plus weighted

@@ -30,7 +30,7 @@ _DTYPE_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32, tor
 
 EXPORTS = ("moeq_last_error", "moeq_abi_version", "moe_route_prep_workspace_bytes",
            "moe_route_prep", "grouped_gemm_qint4", "grouped_gemm_qfp8_block",
-           "grouped_gemm_qnvfp4", "moe_scatter_combine")
+           "grouped_gemm_qnvfp4", "moe_scatter_combine", "moe_quantize_int4")
 
 
 class MoeqError(RuntimeError):
@@ -63,6 +63,7 @@ def lib():
         "grouped_gemm_qnvfp4": (i32, [vp, i64, i32, vp, vp, vp, vp, vp, i64, i32, i32, i64, i64,
                                       i32, i32, vp, i32, vp]),
         "moe_scatter_combine": (i32, [vp, i32, vp, vp, i64, i32, i64, i32, vp, vp]),
+        "moe_quantize_int4": (i32, [vp, i32, i64, i64, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -246,3 +247,22 @@ def moe_scatter_combine(y, pair_to_sorted, topk_weights, *, out_dtype=None, out=
                                    _stream())
     _check("moe_scatter_combine", st)
     return out
+
+
+def quantize_int4_rows(x, *, q=None, scale=None):
+    """Per-row symmetric int4 codes of x [rows][K] (f16/bf16/f32): returns
+    (q uint8 [rows][K/2], scale f32 [rows]), s = amax/7, codes
+    rne(x * 7/amax) clamped to [-8, 7], packed low nibble first."""
+    _need(x, "x", (torch.float16, torch.bfloat16, torch.float32), 2)
+    rows, K = x.shape
+    if q is None:
+        q = torch.empty(rows, K // 2, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _need(q, "q", (torch.uint8,), 2)
+    _need(scale, "scale", (torch.float32,), 1)
+    if tuple(q.shape) != (rows, K // 2) or tuple(scale.shape) != (rows,):
+        raise MoeqError("quantize_int4_rows: q must be [rows][K/2] and scale [rows]")
+    st = lib().moe_quantize_int4(_ptr(x), _DTYPE_CODE[x.dtype], rows, K, _ptr(q), _ptr(scale), _stream())
+    _check("moe_quantize_int4", st)
+    return q, scale

@@ -18,6 +18,10 @@ hipError_t launch_route(const int* ids, int P, int E, int* offsets, int* sorted_
 hipError_t launch_combine(const void* y, int y_kind, const int* p2s, const float* tw, int T,
                           int topk, int N, int64_t P, int out_kind, void* out, hipStream_t stream);
 
+// Per-row symmetric INT4 quantization (x_kind: OutKind of the input).
+hipError_t launch_quant_int4(const void* x, int x_kind, int64_t rows, int K, uint8_t* q, float* scale,
+                             int num_cus, hipStream_t stream);
+
 // Arguments common to the grouped GEMMs.
 struct GroupedArgs {
   const int* offsets;       // [E+1]

@@ -218,4 +218,18 @@ moeq_status moe_scatter_combine(const void* y, moeq_dtype y_dtype, const int32_t
                     fn);
 }
 
+moeq_status moe_quantize_int4(const void* x, moeq_dtype x_dtype, int64_t rows, int64_t K, uint8_t* q,
+                              float* scale, void* stream) {
+  const char* fn = "moe_quantize_int4";
+  if (rows < 0 || rows >= (int64_t(1) << 31)) return fail(MOEQ_EINVAL, "%s: rows=%lld out of range", fn, (long long)rows);
+  if (K <= 0 || K > (1 << 24)) return fail(MOEQ_EINVAL, "%s: K=%lld out of range", fn, (long long)K);
+  if (K % 16 != 0) return fail(MOEQ_EALIGN, "%s: K=%lld must be a multiple of 16", fn, (long long)K);
+  if (x_dtype != MOEQ_F16 && x_dtype != MOEQ_BF16 && x_dtype != MOEQ_F32)
+    return fail(MOEQ_EUNSUPPORTED, "%s: x dtype %d", fn, x_dtype);
+  if (rows > 0 && (!x || !q || !scale)) return fail(MOEQ_EINVAL, "%s: null pointer", fn);
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return fail(MOEQ_EALIGN, "%s: pointers misaligned", fn);
+  return hip_status(moeq::launch_quant_int4(x, (int)x_dtype, rows, (int)K, q, scale, device_cus(), (hipStream_t)stream),
+                    fn);
+}
+
 }  // extern "C"

@@ -35,8 +35,9 @@ __device__ __forceinline__ u32x4 dequant8_bf16(u32 word, float scale) {
 // The same 8 bf16 values packed by taking the high halves of the fp32
 // products with one byte permute per pair: the products are exact bf16
 // values, so their low halves are zero and no rounding is skipped.  The
-// products are formed element by element (a two-float vector times a scalar
-// is not used on the conversion result).
+// products are formed as scalars and only scalars are bit-cast: this
+// compiler keeps just element 0 when elements of a vector are bit-cast one
+// by one.
 __device__ __forceinline__ u32 hi_halves(float lo, float hi) {
   // v_perm_b32: selector bytes 0-3 pick from the second operand
   return __builtin_amdgcn_perm(__builtin_bit_cast(u32, hi), __builtin_bit_cast(u32, lo), 0x07060302u);

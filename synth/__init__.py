@@ -215,6 +215,8 @@ WORKLOADS = {
     3: dict(name="nvfp4_w4a16_prefill_T4096_zipf", kind="nvfp4", T=4096, E=256, k=8, H=7168,
             I=2048, routing="zipf"),
     4: dict(name="w4a4_int4_mixtral_T8192", kind="int4", T=8192, E=8, k=2, H=4096, I=14336),
+    # per-row int4 quantization of config 4's FC1 output h (T*k rows of I fp16)
+    5: dict(name="int4_quantize_rows_16384x14336_f16", kind="quant", rows=16384, K=14336),
 }
 
 
@@ -233,4 +235,9 @@ def workload(idx: int):
         # [T*k][I] with per-row scales x down [E][H][I].
         return int4_moe(seed, c["T"], c["E"], c["k"], 2 * c["I"], c["H"],
                         fc2_rows=c["T"] * c["k"], N2=c["H"], K2=c["I"])
+    if idx == 5:
+        r = streams(seed)
+        x = r[ROLE_ACT].standard_normal((c["rows"], c["K"]), dtype=np.float32)
+        x *= r[ROLE_ACT_SCALE].uniform(0.1, 10.0, (c["rows"], 1)).astype(np.float32)
+        return dict(x=x.astype(np.float16))
     raise KeyError(idx)

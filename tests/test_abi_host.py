@@ -35,7 +35,7 @@ def test_header_declares_the_five_entry_points():
     fns = declared_functions()
     for f in ("moe_route_prep", "grouped_gemm_qint4", "grouped_gemm_qfp8_block",
               "grouped_gemm_qnvfp4", "moe_scatter_combine", "moeq_last_error",
-              "moe_route_prep_workspace_bytes", "moeq_abi_version"):
+              "moe_route_prep_workspace_bytes", "moeq_abi_version", "moe_quantize_int4"):
         assert f in fns
     assert set(mq.EXPORTS) == fns
 
@@ -140,6 +140,21 @@ def _combine(L, **kw):
 ])
 def test_combine_rejects(L, kw, status):
     assert _combine(L, **kw) == status
+
+
+def _quant(L, **kw):
+    a = dict(x=A16, xd=mq.F16, rows=8, K=256, q=A16, sc=A16)
+    a.update(kw)
+    return L.moe_quantize_int4(a["x"], a["xd"], a["rows"], a["K"], a["q"], a["sc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=40), mq.EALIGN), (dict(K=0), mq.EINVAL), (dict(rows=-1), mq.EINVAL),
+    (dict(xd=mq.I32), mq.EUNSUPPORTED), (dict(x=None), mq.EINVAL), (dict(q=ODD), mq.EALIGN),
+    (dict(sc=ODD), mq.EALIGN),
+])
+def test_quantize_rejects(L, kw, status):
+    assert _quant(L, **kw) == status
 
 
 def test_error_text_names_the_call(L):

@@ -277,3 +277,68 @@ def test_repeat_runs_bitwise_identical():
     a = mq.grouped_gemm_qnvfp4(*args, act="silu_mul")
     b = mq.grouped_gemm_qnvfp4(*args, act="silu_mul")
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ INT4 activation quantizer
+def _quant_check(x_np, torch_dtype):
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).to(torch_dtype)
+    q, s = mq.quantize_int4_rows(x.cuda())
+    ref_q, ref_s = oracle.quantize_int4_rows(x.float().numpy())
+    assert np.array_equal(host(s), ref_s), "scales differ"
+    assert np.array_equal(host(q), ref_q), "codes differ"
+
+
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rows,K", [(1, 16), (33, 256), (7, 14336), (130, 528), (3, 32784)])
+def test_quantize_int4_bit_exact(dt, rows, K):
+    rng = np.random.default_rng(rows * 131 + K)
+    x = rng.standard_normal((rows, K)) * rng.uniform(1e-2, 1e2, (rows, 1))
+    _quant_check(x, dt)
+
+
+def test_quantize_int4_ties_zero_and_tiny_rows():
+    K = 64
+    x = np.zeros((4, K), np.float32)
+    # amax 7 -> multiplier 1: exact halves round to even
+    x[0, :8] = [7.0, -7.0, 2.5, 3.5, -0.5, 0.5, -2.5, 1.5]
+    x[1, 3] = 2.0 ** -125                      # below the tiny threshold
+    x[3, :] = np.linspace(-3.0, 3.0, K)        # every row value distinct
+    _quant_check(x, torch.float32)
+    q, s = mq.quantize_int4_rows(torch.from_numpy(x).cuda())
+    codes = oracle.int4_value(oracle.unpack_nibbles(host(q)))
+    assert list(codes[0, :8]) == [7, -7, 2, 4, 0, 0, -2, 2]
+    assert np.all(codes[1:3] == 0) and host(s)[1] == 1 and host(s)[2] == 1
+
+
+def test_w4a4_chain_with_quantized_activations():
+    # fp16 x -> per-token int4 -> FC1 (SiLU-gated, fp16 h) -> per-row int4
+    # of h -> FC2 on sorted rows -> combine; each GPU step checked against
+    # the oracle applied to the GPU's own inputs of that step, and the codes
+    # of both quantizations bit-exact.
+    T, E, k, H, I = 96, 4, 2, 256, 384
+    rng = np.random.default_rng(21)
+    d = synth.int4_moe(22, T, E, k, 2 * I, H, routing="distinct")
+    x = (rng.standard_normal((T, H)) * 2).astype(np.float16)
+    w2 = synth.uniform_bytes(np.random.default_rng(23), (E, H, I // 2))
+    sw2 = synth.uniform_f32(np.random.default_rng(24), (E, H), 0.005, 0.05)
+    ids = dev(d["topk_ids"])
+    offs, srt, p2s, _ = mq.moe_route_prep(ids, E)
+    qa, sa = mq.quantize_int4_rows(torch.from_numpy(x).cuda())
+    ref_qa, ref_sa = oracle.quantize_int4_rows(x)
+    assert np.array_equal(host(qa), ref_qa) and np.array_equal(host(sa), ref_sa)
+    h = mq.grouped_gemm_qint4(qa, sa, dev(d["w"]), dev(d["w_scale"]), offs, srt, k, act="silu_mul",
+                              out_dtype=torch.float16)
+    ref_h = oracle.grouped_gemm_qint4(ref_qa, ref_sa, "token", d["w"], d["w_scale"], host(offs),
+                                      host(srt), k, act="silu_mul")["y"]
+    n = ref_h.shape[0]
+    assert_rows_close(host(h)[:n].astype(np.float64), ref_h, what="chain FC1")
+    qh, sh = mq.quantize_int4_rows(h[:n].contiguous())
+    ref_qh, ref_sh = oracle.quantize_int4_rows(host(h)[:n])
+    assert np.array_equal(host(qh), ref_qh) and np.array_equal(host(sh), ref_sh)
+    y = mq.grouped_gemm_qint4(qh, sh, dev(w2), dev(sw2), offs, srt, k, a_row="sorted",
+                              out_dtype=torch.float16)
+    ref_y = oracle.grouped_gemm_qint4(ref_qh, ref_sh, "sorted", w2, sw2, host(offs), host(srt), k)["y"]
+    assert_rows_close(host(y)[:n].astype(np.float64), ref_y, what="chain FC2")
+    out = mq.moe_scatter_combine(y, p2s, dev(d["topk_weights"]), out_dtype=torch.float32)
+    ref_out = oracle.scatter_combine(host(y).astype(np.float64), host(p2s), d["topk_weights"])
+    assert_rows_close(host(out), ref_out, what="chain combine")

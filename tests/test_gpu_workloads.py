@@ -1,4 +1,4 @@
-"""Parity at the five workloads' full sizes, in the launch configuration the
+"""Parity at the workloads' full sizes, in the launch configuration the
 benchmark times (bench.Workload issues the calls).  Route tables must be
 equal; expert outputs are checked on sampled rows that the oracle computes
 one by one; the combine is checked in full against the oracle applied to the
@@ -118,3 +118,13 @@ def test_workload4_w4a4_mixtral():
     assert_rows_close(host(wl.y)[rows], ref2["y"], what="FC2 y")
     assert_rows_close(host(wl.out), oracle.scatter_combine(host(wl.y), p2s, d["topk_weights"]),
                       what="combine")
+
+
+def test_workload5_int4_quantizer_sampled_rows():
+    wl = _run(5)
+    x = wl.d["x"]
+    rows = np.unique(np.concatenate([[0, x.shape[0] - 1],
+                                     np.random.default_rng(5).integers(0, x.shape[0], 62)]))
+    ref_q, ref_s = oracle.quantize_int4_rows(x[rows])
+    assert np.array_equal(host(wl.qs)[rows], ref_s)
+    assert np.array_equal(host(wl.q)[rows], ref_q)
