@@ -159,7 +159,7 @@ class Workload:
         self.weight_bytes = float(rows * (2 * K + K // 2 + 4))
         self.flops = 0.0
         self.dtype = "f16_to_int4"
-        self.dom = ("quant_int4_rows", ["quant.hip", "common.h"], "hbm", PEAK["hbm_GBps"])
+        self.dom = ("quant_int4_rows_reg", ["quant.hip", "common.h"], "hbm", PEAK["hbm_GBps"])
 
     def step(self, ev=None):
         """One pass of the path; `ev` = (start, end) events around the
@@ -343,11 +343,11 @@ def summarize_profiles(idx: int, pdir: str, steps: int = 50, warmup: int = 10):
         wl.d = synth.workload(idx)
         wl.T, wl.k, wl.E = wl.d["T"], wl.d["k"], wl.d["E"]
     d = wl.d
-    tag = {"fp8": "fp8_prefill", "int4": "int4_prefill", "quant": "quant_int4_rows"}.get(cfg["kind"]) or \
+    tag = {"fp8": "fp8_prefill", "int4": "int4_prefill", "quant": "quant_int4_rows_reg"}.get(cfg["kind"]) or \
         ("nvfp4_decode" if idx == 2 else "nvfp4_prefill")
     srcs = {"fp8_prefill": ["gemm_fp8.hip", "common.h", "tile.h", "pipeline.h"],
             "int4_prefill": ["gemm_int4.hip", "common.h", "tile.h"],
-            "quant_int4_rows": ["quant.hip", "common.h"]}.get(
+            "quant_int4_rows_reg": ["quant.hip", "common.h"]}.get(
         tag, ["gemm_nvfp4.hip", "nvfp4.h", "common.h", "tile.h", "pipeline.h"])
     if cfg["kind"] == "nvfp4":
         H, I = d["H"], d["I"]
