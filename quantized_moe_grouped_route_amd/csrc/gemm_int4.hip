@@ -9,162 +9,224 @@
 // int8.  A and W get the same split, so the int8 MFMA sums the same
 // products, each scaled by 256; |acc| <= K * 64 * 256 < 2^31 for K <= 2^17,
 // and acc >> 8 is the exact int4 dot product.
+//
+// Data movement.  A workgroup of 8 waves owns a tile of 256 routed rows x
+// 256 weight rows.  K advances in stages of 128 int4 values (64 packed
+// bytes of every row), copied global -> LDS by the direct-to-LDS loads into
+// a ring of four stages that runs on across tiles: the next tile's first
+// stages load during this tile's last steps and its epilogue.  Nibbles stay
+// packed in LDS (half the bytes of int8) and each wave splits its fragments
+// after reading them; two waves per SIMD let one wave's LDS reads and
+// splits overlap the other's MFMAs.  A tile's first stage also copies the
+// tile's activation and weight scales into a per-tile LDS buffer for the
+// epilogue (one buffer per ring stage, so none is overwritten before its
+// epilogue).  Every global load of the main loop is one of these copies, so
+// waiting for a stage is an exact vmcnt count (pipeline.h); a tile's row
+// gather reads sorted_ids with scalar loads, counted in lgkmcnt instead.
+//
+// Wave (wm, wn) = (w / 4, w % 4) owns routed rows [128wm, +128) (four
+// 32-row MFMA B operands) and weight rows [64wn, +64) (two 32-row A
+// operands): 8 accumulators, 6 fragment reads per 16 MFMAs.  The MFMA's C
+// layout gives each lane one routed row (l % 32) and runs of 4 consecutive
+// weight rows, so the epilogue stores 4 adjacent outputs per lane.
+// SILU_MUL: tile rows [64wn, 64wn+32) are the gate rows and [64wn+32,
+// 64wn+64) the up rows of output columns [32wn, 32wn+32) of the tile, so
+// the gate and up values of one output meet in one lane.
 #include <algorithm>
 
 #include "kernels.h"
+#include "pipeline.h"
 #include "tile.h"
 
 namespace moeq {
 namespace {
 
-__device__ __forceinline__ void split_nibbles(u32x4 p, u32x4& lo, u32x4& hi) {
-  lo = (p << 4) & 0xF0F0F0F0u;
-  hi = p & 0xF0F0F0F0u;
-}
+constexpr int kBM = 256;                                     // routed rows per tile
+constexpr int kBN = 256;                                     // weight rows per tile
+constexpr int kWaves4 = 8;
+constexpr int kThreads4 = 64 * kWaves4;
+constexpr int kRowBytes = 64;                                // packed bytes per row per stage
+constexpr int kStages4 = 4;
+constexpr int kATileBytes = kBM * kRowBytes;                 // 16 KB
+constexpr int kStageBytes4 = kATileBytes + kBN * kRowBytes;  // 32 KB
+constexpr int kScaleBytes4 = 4096;  // [8 waves][64] activation scales | [8 waves][64] weight scales
+constexpr int kCopiesA = kATileBytes / 1024 / kWaves4;       // 1 KB copies per wave per stage
+constexpr int kCopiesB = kBN * kRowBytes / 1024 / kWaves4;
+constexpr int kCopiesStage = kCopiesA + kCopiesB;
+constexpr int kCopiesScale = 2;                              // extra, in a tile's first stage
+// Tile t's scales are read at its epilogue, which for half the waves comes
+// one stage after its last stage; tile t+5's first stage is issued later.
+constexpr int kScaleBufs = 5;
+constexpr int kGroupM = 4;                                   // m-tiles per n-tile sweep
+static_assert(kCopiesA == 2 && kCopiesB == 2, "copy mapping assumes 2 + 2 copies per wave");
+
+typedef __attribute__((address_space(4))) const int cint4_t;
+typedef int i32x16_a4 __attribute__((ext_vector_type(16), aligned(4)));
+typedef __attribute__((address_space(4))) const i32x16_a4 ci32x16_t;
+// Wave-uniform reads through the constant address space (scalar loads).
+__device__ __forceinline__ int ld_uniform_i32(const int* p, int i) { return ((cint4_t*)(p))[i]; }
+__device__ __forceinline__ i32x16_a4 ld_uniform_i32x16(const int* p) { return *(ci32x16_t*)(p); }
+
+__device__ __forceinline__ v4i lo_nibbles(u32x4 p) { return __builtin_bit_cast(v4i, (p << 4) & 0xF0F0F0F0u); }
+__device__ __forceinline__ v4i hi_nibbles(u32x4 p) { return __builtin_bit_cast(v4i, p & 0xF0F0F0F0u); }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-// Each K step covers 128 int4 values: 64 packed bytes per row from global
-// memory (thread t: row t/4 + 64i, bytes (t%4)*16, i = 0, 1), widened to
-// 128 int8 bytes per row in LDS.
+// LDS tiles: rows of 64 bytes (four 16-byte chunks), chunk c of row r at
+// position c ^ ((r >> 2) & 3).  The LDS serves 16 lanes of a 16-byte read
+// per pass from 256 bytes of banks (4 rows); 16 consecutive rows reading
+// one logical chunk then land on 16 distinct bank groups.  Fragment rows
+// are 32k + lane % 32, so the key is (lane >> 2) & 3.
+__device__ __forceinline__ int frag_off(int lane, int c) { return ((c ^ ((lane >> 2) & 3)) << 4); }
+// A 1 KB copy moves 16 rows: lane l lands at row l/4, position l%4, so it
+// fetches logical chunk (l % 4) ^ ((l / 16) % 4) of its row.
+__device__ __forceinline__ int copy_chunk(int lane) { return ((lane & 3) ^ ((lane >> 4) & 3)) << 4; }
+
+struct Tile4 {
+  int e, row0, rows, nt;
+};
+
+// Work item -> tile with every field wave-uniform.  Same numbering as
+// sched_tile: expert-major, and inside an expert kGroupM m-tiles are
+// visited for each n-tile before the next n-tile.
+__device__ __forceinline__ Tile4 tile_of(const int* tile_start, const int* __restrict__ offsets, int E, int P,
+                                         int n_tiles, int item) {
+  int bl = 0, bh = E - 1;
+  while (bl < bh) {
+    const int mid = (bl + bh + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane(tile_start[mid]) <= item) bl = mid; else bh = mid - 1;
+  }
+  const int e = __builtin_amdgcn_readfirstlane(bl);
+  const int local = item - __builtin_amdgcn_readfirstlane(tile_start[e]);
+  const int lo = min(max(ld_uniform_i32(offsets, e), 0), P);
+  const int hi = min(max(ld_uniform_i32(offsets, e + 1), lo), P);
+  const int m = hi - lo;
+  const int mtiles = (m + kBM - 1) / kBM;
+  const int group = local / (kGroupM * n_tiles);
+  const int in_group = local - group * kGroupM * n_tiles;
+  const int gm = min(kGroupM, mtiles - group * kGroupM);
+  const int mt = group * kGroupM + in_group % gm;
+  Tile4 t;
+  t.e = e;
+  t.row0 = lo + mt * kBM;
+  t.rows = min(kBM, m - mt * kBM);
+  t.nt = in_group / gm;
+  return t;
+}
+
+// Expert-local weight row of tile row rb (clamped into the matrix for the
+// columns past N of a partial last n-tile; those outputs are not stored).
+template <bool SILU>
+__device__ __forceinline__ int weight_row(const Tile4& t, int rb, int N) {
+  if (SILU) {
+    const int I = N / 2;
+    int col = t.nt * 128 + 32 * (rb >> 6) + (rb & 31);
+    if (col >= I) col = t.nt * 128;
+    return ((rb >> 5) & 1) * I + col;
+  }
+  const int r = t.nt * kBN + rb;
+  return r < N ? r : t.nt * kBN;
+}
+
+// Split fragments of one 32-K substep j of a stage (two per stage): lane
+// half h reads chunk 2j + h of its row; the chunk's low nibbles feed one
+// MFMA and its high nibbles another.
+struct Frag {
+  v4i w[2][2];  // [weight operand][low, high nibbles]
+  v4i x[4][2];  // [routed-row operand][low, high nibbles]
+};
+
+__device__ __forceinline__ Frag read_split(const uint8_t* As, const uint8_t* Bs, int wm, int wn, int lane, int j) {
+  const int off = frag_off(lane, 2 * j + (lane >> 5)), l32 = lane & 31;
+  u32x4 pw[2], px[4];
+#pragma unroll
+  for (int o = 0; o < 2; ++o) pw[o] = ld16(Bs + (64 * wn + 32 * o + l32) * kRowBytes + off);
+#pragma unroll
+  for (int o = 0; o < 4; ++o) px[o] = ld16(As + (128 * wm + 32 * o + l32) * kRowBytes + off);
+  Frag f;
+#pragma unroll
+  for (int o = 0; o < 2; ++o) {
+    f.w[o][0] = lo_nibbles(pw[o]);
+    f.w[o][1] = hi_nibbles(pw[o]);
+  }
+#pragma unroll
+  for (int o = 0; o < 4; ++o) {
+    f.x[o][0] = lo_nibbles(px[o]);
+    f.x[o][1] = hi_nibbles(px[o]);
+  }
+  return f;
+}
+
+// 16 MFMAs: the low-nibble pass over the 8 accumulators, then the high pass.
+__device__ __forceinline__ void mma_frag(const Frag& f, v16i (&acc)[2][4]) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int wo = 0; wo < 2; ++wo)
+#pragma unroll
+      for (int xo = 0; xo < 4; ++xo) acc[wo][xo] = mfma_i8_32x32x32(f.w[wo][p], f.x[xo][p], acc[wo][xo]);
+}
+
+template <int OUT>
+__device__ __forceinline__ void store4(void* out, int64_t idx, const float (&o)[4]) {
+  typedef typename OutT<OUT>::T T;
+  T* dst = static_cast<T*>(out) + idx;
+  if constexpr (sizeof(T) == 2) {
+    const u32 lo = (u32)OutT<OUT>::from(o[0]) | ((u32)OutT<OUT>::from(o[1]) << 16);
+    const u32 hi = (u32)OutT<OUT>::from(o[2]) | ((u32)OutT<OUT>::from(o[3]) << 16);
+    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+  } else {
+    *reinterpret_cast<v4f*>(dst) = v4f{o[0], o[1], o[2], o[3]};
+  }
+}
+
+// Epilogue of one tile: value i of accumulator [wo][xo] in lane l is
+// weight row 64wn + 32wo + 8(i/4) + 4(l/32) + i%4 and routed row
+// 128wm + 32xo + l%32 of the tile.  Scale tables: routed row r at
+// float (r / 32) * 64 + r % 32, weight row r at 512 + the same.
 template <int OUT, bool SILU>
-__global__ __launch_bounds__(kThreadsT, 1) void int4_prefill(
-    const uint8_t* __restrict__ a, const float* __restrict__ a_scale, int64_t rows_a, int a_sorted,
-    const uint8_t* __restrict__ w, const float* __restrict__ w_scale,
-    const int* __restrict__ offsets, const int* __restrict__ sorted_ids, int topk, int E, int P, int N,
-    int K, void* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[kTileM * kPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[kTileN * kPitch];
-  __shared__ __attribute__((aligned(16))) float lds_sa[kTileM];
-  __shared__ int tile_start[kMaxExperts + 1];
-  __shared__ int sched_scratch[2 * kMaxWaves];
-
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-  const int n_tiles = N / kTileN;
+__device__ __forceinline__ void epilogue(const Tile4& t, const float* sb, int wm, int wn, int lane, int N,
+                                         const v16i (&acc)[2][4], void* __restrict__ out) {
+  const int h = lane >> 5, l32 = lane & 31;
   const int I = N / 2;
-  const int steps = K / 128;
-  const int64_t row_bytes = K / 2;
-  sched_build(tile_start, sched_scratch, offsets, E, P, kTileM, n_tiles);
-  const int total = tile_start[E];
-
-  const int lrow = tid >> 2, lchunk = (tid & 3) * 16;
-
-  for (int item = xcd_logical_id(blockIdx.x, gridDim.x); item < total; item += gridDim.x) {
-    const Tile t = sched_tile<4>(tile_start, offsets, E, P, kTileM, n_tiles, item);
-    __syncthreads();  // the previous tile's epilogue has read lds_sa
-    const uint8_t* pa[2];
-    const uint8_t* pb[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int j = lrow + 64 * i;
-      const int s = t.row0 + min(j, t.rows - 1);
-      pa[i] = a + a_row_of(s, sorted_ids, a_sorted, topk, rows_a) * row_bytes + lchunk;
-      pb[i] = w + ((int64_t)t.e * N + b_global_row(SILU, t.nt, j, I)) * row_bytes + lchunk;
-    }
-    if (tid < kTileM)
-      lds_sa[tid] = a_scale[a_row_of(t.row0 + min(tid, t.rows - 1), sorted_ids, a_sorted, topk, rows_a)];
-
-    v16i acc[2][2];
+  for (int xo = 0; xo < 4; ++xo) {
+    const int r = 128 * wm + 32 * xo + l32;
+    if (r >= t.rows) continue;
+    const int64_t orow = t.row0 + r;
+    const float sa = sb[(4 * wm + xo) * 64 + l32];
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int qq = 0; qq < 4; ++qq) {
+      const int m0 = 8 * qq + 4 * h;  // operand row of values 4qq .. 4qq+3
+      if constexpr (SILU) {
+        const int col0 = t.nt * 128 + 32 * wn + m0;
+        if (col0 >= I) continue;
+        const v4f sg = *reinterpret_cast<const v4f*>(sb + 512 + (2 * wn) * 64 + m0);
+        const v4f su = *reinterpret_cast<const v4f*>(sb + 512 + (2 * wn + 1) * 64 + m0);
+        float o[4];
 #pragma unroll
-      for (int y = 0; y < 2; ++y) acc[x][y] = v16i{};
-
-    u32x4 ra[2], rb[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ra[i] = ld16(pa[i]);
-      rb[i] = ld16(pb[i]);
-    }
-    for (int st = 0; st < steps; ++st) {
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        u32x4 lo, hi;
-        uint8_t* da = lds_a + (lrow + 64 * i) * kPitch + 2 * lchunk;
-        split_nibbles(ra[i], lo, hi);
-        st16(da, lo);
-        st16(da + 16, hi);
-        uint8_t* db = lds_b + (lrow + 64 * i) * kPitch + 2 * lchunk;
-        split_nibbles(rb[i], lo, hi);
-        st16(db, lo);
-        st16(db + 16, hi);
-      }
-      __syncthreads();
-      if (st + 1 < steps) {
-        const int64_t off = (int64_t)(st + 1) * 64;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          ra[i] = ld16(pa[i] + off);
-          rb[i] = ld16(pb[i] + off);
+        for (int rr = 0; rr < 4; ++rr) {
+          const float g = sa * sg[rr] * (float)(acc[0][xo][4 * qq + rr] >> 8);
+          const float u = sa * su[rr] * (float)(acc[1][xo][4 * qq + rr] >> 8);
+          o[rr] = silu(g) * u;
         }
-      }
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq) {
-        const int koff = kq * 32 + (lane >> 5) * 16;
-        v4i fa[2], fb[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          fa[x] = *reinterpret_cast<const v4i*>(lds_a + (64 * wm + 32 * x + (lane & 31)) * kPitch + koff);
-        }
-#pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          fb[y] = *reinterpret_cast<const v4i*>(lds_b + (b_lds_row(SILU, wn, y) + (lane & 31)) * kPitch + koff);
-        }
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-          for (int y = 0; y < 2; ++y) acc[x][y] = mfma_i8_32x32x32(fa[x], fb[y], acc[x][y]);
-      }
-    }
-
-    // Epilogue.
-    if (OUT == OUT_I32) {
-      int* o = static_cast<int*>(out);
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          const int col = t.nt * kTileN + b_lds_row(false, wn, y) + (lane & 31);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int rr = 64 * wm + 32 * x + c32_row(i, lane);
-            if (rr < t.rows) o[(int64_t)(t.row0 + rr) * N + col] = acc[x][y][i] >> 8;
-          }
-        }
-    } else {
-      typedef typename OutT<(OUT == OUT_I32 ? OUT_F32 : OUT)>::T T;
-      T* o = static_cast<T*>(out);
-      if (SILU) {
-        const int col = t.nt * 64 + 32 * wn + (lane & 31);  // output column in [0, I)
-        const float swg = w_scale[(int64_t)t.e * N + col];
-        const float swu = w_scale[(int64_t)t.e * N + I + col];
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int rr = 64 * wm + 32 * x + c32_row(i, lane);
-            const float sa = lds_sa[rr];
-            const float g = sa * swg * (float)(acc[x][0][i] >> 8);
-            const float u = sa * swu * (float)(acc[x][1][i] >> 8);
-            if (rr < t.rows)
-              o[(int64_t)(t.row0 + rr) * I + col] = OutT<(OUT == OUT_I32 ? OUT_F32 : OUT)>::from(silu(g) * u);
-          }
+        store4<OUT>(out, orow * I + col0, o);
       } else {
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          const int col = t.nt * kTileN + b_lds_row(false, wn, y) + (lane & 31);
-          const float sw = w_scale[(int64_t)t.e * N + col];
+        for (int wo = 0; wo < 2; ++wo) {
+          const int col0 = t.nt * kBN + 64 * wn + 32 * wo + m0;
+          if (col0 >= N) continue;
+          if constexpr (OUT == OUT_I32) {
+            int* dst = static_cast<int*>(out) + orow * N + col0;
+            *reinterpret_cast<v4i*>(dst) = v4i{acc[wo][xo][4 * qq] >> 8, acc[wo][xo][4 * qq + 1] >> 8,
+                                               acc[wo][xo][4 * qq + 2] >> 8, acc[wo][xo][4 * qq + 3] >> 8};
+          } else {
+            const v4f sw = *reinterpret_cast<const v4f*>(sb + 512 + (2 * wn + wo) * 64 + m0);
+            float o[4];
 #pragma unroll
-          for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int rr = 64 * wm + 32 * x + c32_row(i, lane);
-              const float v = lds_sa[rr] * sw * (float)(acc[x][y][i] >> 8);
-              if (rr < t.rows)
-                o[(int64_t)(t.row0 + rr) * N + col] = OutT<(OUT == OUT_I32 ? OUT_F32 : OUT)>::from(v);
-            }
+            for (int rr = 0; rr < 4; ++rr) o[rr] = sa * sw[rr] * (float)(acc[wo][xo][4 * qq + rr] >> 8);
+            store4<OUT>(out, orow * N + col0, o);
+          }
         }
       }
     }
@@ -172,9 +234,168 @@ __global__ __launch_bounds__(kThreadsT, 1) void int4_prefill(
 }
 
 template <int OUT, bool SILU>
+__global__ __launch_bounds__(kThreads4, 1) void int4_prefill(
+    const uint8_t* __restrict__ a, const float* __restrict__ a_scale, int64_t rows_a, int a_sorted,
+    const uint8_t* __restrict__ w, const float* __restrict__ w_scale,
+    const int* __restrict__ offsets, const int* __restrict__ sorted_ids, int topk, int E, int P, int N,
+    int K, void* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages4 * kStageBytes4];
+  __shared__ __attribute__((aligned(16))) uint8_t sbuf[kScaleBufs * kScaleBytes4];
+  __shared__ int tile_start[kMaxExperts + 1];
+  __shared__ int sched_scratch[2 * kMaxWaves];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wid >> 2, wn = wid & 3;
+  const int l32 = lane & 31;
+  const int n_tiles = SILU ? (N / 2 + 127) / 128 : (N + kBN - 1) / kBN;
+  const int64_t rowb = K / 2;
+  const int steps = K / 128;
+  sched_build(tile_start, sched_scratch, offsets, E, P, kBM, n_tiles);
+  const int total = __builtin_amdgcn_readfirstlane(tile_start[E]);
+  const int G = gridDim.x;
+  const int first = xcd_logical_id(blockIdx.x, G);
+  if (first >= total) return;
+  const int nq = ((total - first + G - 1) / G) * steps;
+
+  // ---- issue cursor: sources of the next stage to copy.  Wave w copies
+  // tile rows [32w, 32w+32) of both operands: copy i moves rows
+  // 32w + 16i + lane/4.
+  const uint8_t* pa[kCopiesA];
+  const uint8_t* pb[kCopiesB];
+  const float* psa = a_scale;
+  const float* psw = w_scale;
+  const int cch = copy_chunk(lane);
+  int is_item = first, is_step = 0, is_sbuf = 0;
+  auto set_tile = [&](int item) __attribute__((always_inline)) {
+    const Tile4 t = tile_of(tile_start, offsets, E, P, n_tiles, item);
+    int arow[kCopiesA];
+#pragma unroll
+    for (int i = 0; i < kCopiesA; ++i) {
+      const int r0 = 32 * wid + 16 * i;
+      int r;
+      if (a_sorted || sorted_ids == nullptr) {
+        r = t.row0 + min(r0 + (lane >> 2), t.rows - 1);
+      } else {
+        // the copy's 16 sorted ids (one 64-byte scalar load when all 16
+        // rows are in the tile); each lane picks its own
+        i32x16_a4 ids;
+        if (r0 + 16 <= t.rows) {
+          ids = ld_uniform_i32x16(sorted_ids + t.row0 + r0);
+        } else {
+#pragma unroll
+          for (int g = 0; g < 16; ++g) ids[g] = ld_uniform_i32(sorted_ids, t.row0 + min(r0 + g, t.rows - 1));
+        }
+        int v = ids[0];
+#pragma unroll
+        for (int g = 1; g < 16; ++g) v = (lane >> 2) == g ? ids[g] : v;
+        r = v / topk;
+      }
+      arow[i] = (r < 0 || r >= rows_a) ? 0 : r;
+      pa[i] = a + (int64_t)arow[i] * rowb + cch;
+      pb[i] = w + ((int64_t)t.e * N + weight_row<SILU>(t, r0 + (lane >> 2), N)) * rowb + cch;
+    }
+    // scales of tile rows 32w + l32: copy l32 / 16 holds the routed row in
+    // lanes 4 (l32 % 16) .. +3
+    const int src = 4 * (l32 & 15);
+    const int s0 = __shfl(arow[0], src, 64), s1 = __shfl(arow[1], src, 64);
+    psa = a_scale + ((l32 >> 4) ? s1 : s0);
+    psw = w_scale + (int64_t)t.e * N + weight_row<SILU>(t, 32 * wid + l32, N);
+  };
+  const uint32_t ring_lds = lds_addr(ring), sbuf_lds = lds_addr(sbuf);
+  auto issue = [&](int slot) __attribute__((always_inline)) {
+    const uint32_t base = ring_lds + slot * kStageBytes4;
+    const int64_t ko = (int64_t)is_step * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < kCopiesA; ++i) dma16(pa[i] + ko, base + (kCopiesA * wid + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < kCopiesB; ++i) dma16(pb[i] + ko, base + kATileBytes + (kCopiesB * wid + i) * 1024);
+    if (is_step == 0) {
+      const uint32_t sb = sbuf_lds + is_sbuf * kScaleBytes4;
+      dma4(psa, sb + wid * 256);
+      dma4(psw, sb + 2048 + wid * 256);
+      is_sbuf = is_sbuf == kScaleBufs - 1 ? 0 : is_sbuf + 1;
+    }
+    if (++is_step == steps) {
+      is_step = 0;
+      is_item += G;
+      if (is_item < total) set_tile(is_item);
+    }
+  };
+
+  set_tile(first);
+#pragma nounroll
+  for (int s = 0; s < kStages4 && s < nq; ++s) issue(s);
+
+  v16i acc[2][4];
+#pragma unroll
+  for (int wo = 0; wo < 2; ++wo)
+#pragma unroll
+    for (int xo = 0; xo < 4; ++xo) acc[wo][xo] = v16i{};
+
+  // The two waves on a SIMD (w and w + 4, i.e. wm = 0 and 1) run half a
+  // stage apart: after a barrier a wave with wm = 0 reads and splits its
+  // first substep while its partner (wm = 1) runs the MFMAs of the substep
+  // it split before the barrier, so one wave's LDS reads and splits overlap
+  // the other's MFMAs instead of both waiting on the same phase.
+  int ep_item = first, ep_sbuf = 0;
+  auto finish_tile = [&]() __attribute__((always_inline)) {
+    const Tile4 t = tile_of(tile_start, offsets, E, P, n_tiles, ep_item);
+    epilogue<OUT, SILU>(t, reinterpret_cast<const float*>(sbuf + ep_sbuf * kScaleBytes4), wm, wn, lane, N, acc,
+                        out);
+#pragma unroll
+    for (int wo = 0; wo < 2; ++wo)
+#pragma unroll
+      for (int xo = 0; xo < 4; ++xo) acc[wo][xo] = v16i{};
+    ep_item += G;
+    ep_sbuf = ep_sbuf == kScaleBufs - 1 ? 0 : ep_sbuf + 1;
+  };
+  // Both loops pass the same nq barriers; they are separate so that the
+  // held substep is live only in the second.
+  auto stage_start = [&](int q) __attribute__((always_inline)) {
+    // Stage q must have landed.  The stages issued after it (q+1, q+2, and
+    // at q = 0 also q+3) may stay in flight: each is at least kCopiesStage
+    // copies (a tile's first stage has kCopiesScale more, which this count
+    // leaves out, so the wait is at most a little early-conservative).
+    if (q == 0 && nq > 3) wait_vmcnt<3 * kCopiesStage>();
+    else if (q + 2 < nq) wait_vmcnt<2 * kCopiesStage>();
+    else if (q + 1 < nq) wait_vmcnt<kCopiesStage>();
+    else wait_vmcnt<0>();
+    raw_barrier();  // every wave's part of stage q is in LDS; stage q-1's slot is free
+    if (q >= 1 && q + kStages4 - 1 < nq) issue((unsigned)(q + kStages4 - 1) % kStages4);
+    return ring + ((unsigned)q % kStages4) * kStageBytes4;
+  };
+  if (wm == 0) {
+    for (int q = 0, st = 0; q < nq; ++q) {
+      const uint8_t* As = stage_start(q);
+      mma_frag(read_split(As, As + kATileBytes, wm, wn, lane, 0), acc);
+      mma_frag(read_split(As, As + kATileBytes, wm, wn, lane, 1), acc);
+      if (++st == steps) {
+        st = 0;
+        finish_tile();
+      }
+    }
+  } else {
+    Frag held;
+    for (int q = 0, st = 0; q < nq; ++q) {
+      const uint8_t* As = stage_start(q);
+      if (q > 0) {
+        mma_frag(held, acc);
+        if (st == 0) finish_tile();
+      }
+      mma_frag(read_split(As, As + kATileBytes, wm, wn, lane, 0), acc);
+      held = read_split(As, As + kATileBytes, wm, wn, lane, 1);
+      if (++st == steps) st = 0;
+    }
+    mma_frag(held, acc);
+    finish_tile();
+  }
+}
+
+template <int OUT, bool SILU>
 hipError_t go(const GroupedArgs& g, int grid, const uint8_t* a, const float* a_scale,
               const uint8_t* w, const float* w_scale, hipStream_t stream) {
-  hipLaunchKernelGGL((int4_prefill<OUT, SILU>), dim3(grid), dim3(kThreadsT), 0, stream, a, a_scale,
+  hipLaunchKernelGGL((int4_prefill<OUT, SILU>), dim3(grid), dim3(kThreads4), 0, stream, a, a_scale,
                      g.rows_a, g.a_sorted, w, w_scale, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N,
                      g.K, g.out);
   return hipGetLastError();
@@ -184,10 +405,12 @@ hipError_t go(const GroupedArgs& g, int grid, const uint8_t* a, const float* a_s
 
 hipError_t launch_gemm_int4(const GroupedArgs& g, const uint8_t* a, const float* a_scale,
                             const uint8_t* w, const float* w_scale, hipStream_t stream) {
-  const int64_t mt_ub = (g.P + kTileM - 1) / kTileM + std::min<int64_t>(g.E, g.P);
-  const int64_t items_ub = mt_ub * (g.N / kTileN);
+  // Upper bound on tiles: every expert adds at most one partial m-tile.
+  const int64_t mt_ub = (g.P + kBM - 1) / kBM + std::min<int64_t>(g.E, g.P);
+  const int64_t n_tiles = g.silu_mul ? (g.N / 2 + 127) / 128 : (g.N + kBN - 1) / kBN;
+  const int64_t items_ub = mt_ub * n_tiles;
   if (items_ub == 0) return hipSuccess;
-  const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus * 2);
+  const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus);
   if (g.silu_mul) {
     switch (g.out_kind) {
       case OUT_F16: return go<OUT_F16, true>(g, grid, a, a_scale, w, w_scale, stream);
