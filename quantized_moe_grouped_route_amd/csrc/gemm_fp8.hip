@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kThreads8, 1) void fp8_prefill(
     int last_issued = min(G, kStages) - 1;
 
     const int steps = (G + 1) / 2;
-    for (int j = 0; j < steps; ++j) {
+    auto step_start = [&](int j) __attribute__((always_inline)) {
       // Stages 2j and 2j+1 must have landed; at most the stages after them
       // (issued one step ago) may be in flight.
       const int need = min(2 * j + 1, G - 1);
@@ -122,42 +122,78 @@ __global__ __launch_bounds__(kThreads8, 1) void fp8_prefill(
       else if (after == 1) wait_vmcnt<kDmaPerStage>();
       else wait_vmcnt<0>();
       raw_barrier();  // every wave's share is in LDS; stages 2j-2, 2j-1 are free
-      if (j > 0) {
-        for (int s = 2 * j + 2; s <= 2 * j + 3 && s < G; ++s) {
-          issue(s);
-          last_issued = s;
+      if (j > 0 && 2 * j + 2 < G) {
+        issue(2 * j + 2);
+        last_issued = 2 * j + 2;
+        if (2 * j + 3 < G) {
+          issue(2 * j + 3);
+          last_issued = 2 * j + 3;
         }
       }
-      const int g = 2 * j + kg;
-      if (g < G) {
-        const uint8_t* As = smem + (g % kStages) * kStageBytes;
-        const uint8_t* Bs = As + kTileBytes;
-        const float* Ss = reinterpret_cast<const float*>(As + 2 * kTileBytes);
+    };
+    // The 8 MFMAs of K group g into fresh partials, and the group's scales.
+    auto group_mma = [&](int g, v16f (&p)[2][2], float& sc0, float& sc1) __attribute__((always_inline)) {
+      const uint8_t* As = smem + (g % kStages) * kStageBytes;
+      const uint8_t* Bs = As + kTileBytes;
+      const float* Ss = reinterpret_cast<const float*>(As + 2 * kTileBytes);
 #define MOEQ_LD8(p, o0, o1) \
   __builtin_bit_cast(v8i, __builtin_shufflevector(ld16((p) + (o0)), ld16((p) + (o1)), 0, 1, 2, 3, 4, 5, 6, 7))
-        const v8i w00 = MOEQ_LD8(Bs + rw0, oa0, oa1), w01 = MOEQ_LD8(Bs + rw1, oa0, oa1);
-        const v8i x00 = MOEQ_LD8(As + rx0, oa0, oa1), x01 = MOEQ_LD8(As + rx1, oa0, oa1);
-        const v8i w10 = MOEQ_LD8(Bs + rw0, ob0, ob1), w11 = MOEQ_LD8(Bs + rw1, ob0, ob1);
-        const v8i x10 = MOEQ_LD8(As + rx0, ob0, ob1), x11 = MOEQ_LD8(As + rx1, ob0, ob1);
+      const v8i w00 = MOEQ_LD8(Bs + rw0, oa0, oa1), w01 = MOEQ_LD8(Bs + rw1, oa0, oa1);
+      const v8i x00 = MOEQ_LD8(As + rx0, oa0, oa1), x01 = MOEQ_LD8(As + rx1, oa0, oa1);
+      const v8i w10 = MOEQ_LD8(Bs + rw0, ob0, ob1), w11 = MOEQ_LD8(Bs + rw1, ob0, ob1);
+      const v8i x10 = MOEQ_LD8(As + rx0, ob0, ob1), x11 = MOEQ_LD8(As + rx1, ob0, ob1);
 #undef MOEQ_LD8
-        const float sb = Ss[16];
-        const float sc0 = Ss[sidx0] * sb, sc1 = Ss[sidx1] * sb;
-        v16f p00 = mfma_f8_32x32x64(w00, x00, v16f{});
-        v16f p01 = mfma_f8_32x32x64(w00, x01, v16f{});
-        v16f p10 = mfma_f8_32x32x64(w01, x00, v16f{});
-        v16f p11 = mfma_f8_32x32x64(w01, x01, v16f{});
-        p00 = mfma_f8_32x32x64(w10, x10, p00);
-        p01 = mfma_f8_32x32x64(w10, x11, p01);
-        p10 = mfma_f8_32x32x64(w11, x10, p10);
-        p11 = mfma_f8_32x32x64(w11, x11, p11);
+      const float sb = Ss[16];
+      sc0 = Ss[sidx0] * sb;
+      sc1 = Ss[sidx1] * sb;
+      p[0][0] = mfma_f8_32x32x64(w00, x00, v16f{});
+      p[0][1] = mfma_f8_32x32x64(w00, x01, v16f{});
+      p[1][0] = mfma_f8_32x32x64(w01, x00, v16f{});
+      p[1][1] = mfma_f8_32x32x64(w01, x01, v16f{});
+      p[0][0] = mfma_f8_32x32x64(w10, x10, p[0][0]);
+      p[0][1] = mfma_f8_32x32x64(w10, x11, p[0][1]);
+      p[1][0] = mfma_f8_32x32x64(w11, x10, p[1][0]);
+      p[1][1] = mfma_f8_32x32x64(w11, x11, p[1][1]);
+    };
+    // Promotion of a group's partials into the fp32 result.
+    auto promote = [&](const v16f (&p)[2][2], float sc0, float sc1) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          acc[0][0][i] = __builtin_fmaf(p00[i], sc0, acc[0][0][i]);
-          acc[0][1][i] = __builtin_fmaf(p01[i], sc1, acc[0][1][i]);
-          acc[1][0][i] = __builtin_fmaf(p10[i], sc0, acc[1][0][i]);
-          acc[1][1][i] = __builtin_fmaf(p11[i], sc1, acc[1][1][i]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        acc[0][0][i] = __builtin_fmaf(p[0][0][i], sc0, acc[0][0][i]);
+        acc[0][1][i] = __builtin_fmaf(p[0][1][i], sc1, acc[0][1][i]);
+        acc[1][0][i] = __builtin_fmaf(p[1][0][i], sc0, acc[1][0][i]);
+        acc[1][1][i] = __builtin_fmaf(p[1][1][i], sc1, acc[1][1][i]);
       }
+    };
+    // The two waves on a SIMD belong to different K groups (w and w + 4).
+    // Group 0 promotes each group's partials right after its MFMAs; group 1
+    // promotes them after the next barrier, before its next fragment reads,
+    // so one wave's promotion overlaps the other's reads and MFMAs instead
+    // of both leaving the MFMA unit idle at the same time.  The two loops
+    // pass the same barriers.
+    if (kg == 0) {
+      for (int j = 0; j < steps; ++j) {
+        step_start(j);
+        const int g = 2 * j;
+        v16f p[2][2];
+        float sc0, sc1;
+        group_mma(g, p, sc0, sc1);
+        promote(p, sc0, sc1);
+      }
+    } else {
+      v16f p[2][2];
+      float sc0 = 0.f, sc1 = 0.f;
+      bool held = false;
+      for (int j = 0; j < steps; ++j) {
+        step_start(j);
+        if (held) promote(p, sc0, sc1);
+        // keep the held partials' live range from overlapping the next ones
+        __builtin_amdgcn_sched_barrier(0);
+        const int g = 2 * j + 1;
+        held = g < G;
+        if (held) group_mma(g, p, sc0, sc1);
+      }
+      if (held) promote(p, sc0, sc1);
     }
 
     // Epilogue.  Group 1 parks its fp32 sums in LDS (the ring is idle now);
