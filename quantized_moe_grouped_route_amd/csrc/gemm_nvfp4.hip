@@ -13,6 +13,7 @@
 //            weights as the 16-row operand and the (at most 4) routed rows
 //            as the other, so no cross-lane reduction is needed.
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.h"
 #include "nvfp4.h"
@@ -135,32 +136,45 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
       if (s < G) issue(s);
     int last_issued = min(G, kStages - 1) - 1;
 
-    for (int g = 0; g < G; ++g) {
-      if (last_issued - g >= 1) wait_vmcnt<kPer>();
-      else wait_vmcnt<0>();
-      raw_barrier();  // stage g visible to all waves; stage g-1 is free
-      if (g + kStages - 1 < G) {
-        issue(g + kStages - 1);
-        last_issued = g + kStages - 1;
-      }
-      const uint8_t* st = smem + (g % kStages) * kStageBytes;
-      // Dequantize this lane's 2 x 32 weight codes (exact in bf16).
-      const u32x4 q0 = ld16(st + boff0), q1 = ld16(st + boff1);
-      const uint32_t sc0 = *reinterpret_cast<const uint16_t*>(st + soff0);
-      const uint32_t sc1 = *reinterpret_cast<const uint16_t*>(st + soff1);
-      const float s00 = e4m3_to_f32(sc0 & 0xffu), s01 = e4m3_to_f32(sc0 >> 8);
-      const float s10 = e4m3_to_f32(sc1 & 0xffu), s11 = e4m3_to_f32(sc1 >> 8);
+    // K loop over the tile's first NY 32-row groups of routed rows: the last
+    // m-tile of an expert is usually partial (with skewed routing most
+    // experts have fewer than 128 rows), and its MFMAs stop at the smallest
+    // multiple of 32 rows that covers it.
+    auto k_loop = [&](auto ny_c) __attribute__((always_inline)) {
+      constexpr int NY = decltype(ny_c)::value;
+      for (int g = 0; g < G; ++g) {
+        if (last_issued - g >= 1) wait_vmcnt<kPer>();
+        else wait_vmcnt<0>();
+        raw_barrier();  // stage g visible to all waves; stage g-1 is free
+        if (g + kStages - 1 < G) {
+          issue(g + kStages - 1);
+          last_issued = g + kStages - 1;
+        }
+        const uint8_t* st = smem + (g % kStages) * kStageBytes;
+        // Dequantize this lane's 2 x 32 weight codes (exact in bf16).
+        const u32x4 q0 = ld16(st + boff0), q1 = ld16(st + boff1);
+        const uint32_t sc0 = *reinterpret_cast<const uint16_t*>(st + soff0);
+        const uint32_t sc1 = *reinterpret_cast<const uint16_t*>(st + soff1);
+        const float s00 = e4m3_to_f32(sc0 & 0xffu), s01 = e4m3_to_f32(sc0 >> 8);
+        const float s10 = e4m3_to_f32(sc1 & 0xffu), s11 = e4m3_to_f32(sc1 >> 8);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const v8bf wf0 = __builtin_bit_cast(v8bf, dequant8_bf16(q0[s], s < 2 ? s00 : s01));
-        const v8bf wf1 = __builtin_bit_cast(v8bf, dequant8_bf16(q1[s], s < 2 ? s10 : s11));
+        for (int s = 0; s < 4; ++s) {
+          const v8bf wf0 = __builtin_bit_cast(v8bf, dequant8_bf16(q0[s], s < 2 ? s00 : s01));
+          const v8bf wf1 = __builtin_bit_cast(v8bf, dequant8_bf16(q1[s], s < 2 ? s10 : s11));
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          const v8bf xf = *reinterpret_cast<const v8bf*>(st + (32 * y + l32) * 128 + aoff[s]);
-          acc[0][y] = mfma_bf16_32x32x16(wf0, xf, acc[0][y]);
-          acc[1][y] = mfma_bf16_32x32x16(wf1, xf, acc[1][y]);
+          for (int y = 0; y < NY; ++y) {
+            const v8bf xf = *reinterpret_cast<const v8bf*>(st + (32 * y + l32) * 128 + aoff[s]);
+            acc[0][y] = mfma_bf16_32x32x16(wf0, xf, acc[0][y]);
+            acc[1][y] = mfma_bf16_32x32x16(wf1, xf, acc[1][y]);
+          }
         }
       }
+    };
+    switch ((t.rows + 31) >> 5) {
+      case 1: k_loop(std::integral_constant<int, 1>{}); break;
+      case 2: k_loop(std::integral_constant<int, 2>{}); break;
+      case 3: k_loop(std::integral_constant<int, 3>{}); break;
+      default: k_loop(std::integral_constant<int, 4>{}); break;
     }
 
     // Epilogue: global scale (and the SiLU-gated product), output tile
