@@ -257,10 +257,172 @@ __global__ __launch_bounds__(kThreads8, 1) void fp8_prefill(
   }
 }
 
+
+// ------------------------------------------------------------------ decode
+// Few routed rows per expert (decode): the weight stream is the whole cost,
+// so the wave is the unit of work and every operand arrives through a
+// per-wave direct-to-LDS ring, as in the NVFP4 decode schedule.
+//
+// Item = (tile of at most 4 routed rows of one expert, 16 weight rows).
+// Per 128-wide K group the ring slot holds the 16 weight rows (two whole-
+// line copies of 8 rows x 128 bytes, piece p of row r at position
+// p ^ ((r >> 1) & 7)), the tile's activation rows (one copy: 4 rows x 128
+// bytes; the upper 32 lanes repeat them) and the scales (one 4-byte copy:
+// lanes 0..3 the rows' activation scales of the group, lane 4 the weight
+// block scale).  One v_mfma_scale_f32_16x16x128_f8f6f4 per group takes the
+// weights as the 16-row operand (lane l: row l % 16, K bytes [32(l/16),
+// +32)) and the activation rows as the 16 columns (columns past the tile
+// are discarded); its partial is promoted with sa[g][row] * sw[e][n/128][g]
+// as in the prefill schedule.
+namespace fd {
+constexpr int kM = 4;                       // routed rows per item
+constexpr int kWaves = 4;                   // waves per workgroup, independent
+constexpr int kDepth = 4;                   // K groups in flight per wave
+constexpr int kW = 0, kX = 2048, kS = 3072;  // slot regions
+constexpr int kSlot = 3328;
+constexpr int kCopies = 4;                  // per K group: 2 weight, 1 activation, 1 scale
+}  // namespace fd
+
+typedef __attribute__((address_space(4))) const int cint8_t_;
+__device__ __forceinline__ int ld_uniform8(const int* p, int i) { return ((cint8_t_*)(p))[i]; }
+
+// vmcnt(n * fd::kCopies) for n in [0, kDepth - 1]
+__device__ __forceinline__ void wait_groups(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<fd::kCopies>(); break;
+    case 2: wait_vmcnt<2 * fd::kCopies>(); break;
+    default: wait_vmcnt<3 * fd::kCopies>(); break;
+  }
+  asm volatile("" ::: "memory");
+}
+
+template <int OUT>
+__global__ __launch_bounds__(64 * fd::kWaves) void fp8_decode(
+    const uint8_t* __restrict__ a, const float* __restrict__ a_scale, int64_t rows_a, int a_sorted,
+    const uint8_t* __restrict__ w, const float* __restrict__ w_scale,
+    const int* __restrict__ offsets, const int* __restrict__ sorted_ids, int topk, int E, int P, int N,
+    int K, void* __restrict__ out) {
+  __shared__ int tile_start[kMaxExperts + 1];
+  __shared__ int sched_scratch[2 * kMaxWaves];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[fd::kWaves][fd::kDepth][fd::kSlot];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_blocks = N / 16;
+  sched_build(tile_start, sched_scratch, offsets, E, P, fd::kM, n_blocks);
+  const int total = __builtin_amdgcn_readfirstlane(tile_start[E]);
+  // Items go to the fewest waves that still need the same number of rounds.
+  const int waves = gridDim.x * fd::kWaves;
+  const int rounds = (total + waves - 1) / waves;
+  const int active = rounds ? (total + rounds - 1) / rounds : 0;
+  const int wid = blockIdx.x * fd::kWaves + wv;
+  if (wid >= active) return;
+  const int G = K / 128;
+  uint8_t* myring = &ring[wv][0][0];
+  const uint32_t lb = lds_addr(myring);
+  const int l16 = lane & 15, quarter = lane >> 4;
+  // weight copy h: lane -> row 8h + lane/8, piece (lane % 8) ^ ((row >> 1) & 7)
+  const int wr0 = lane >> 3, wr1 = 8 + (lane >> 3);
+  const int wp0 = ((lane & 7) ^ ((wr0 >> 1) & 7)) << 4, wp1 = ((lane & 7) ^ ((wr1 >> 1) & 7)) << 4;
+  // fragment reads: row l16, pieces 2*quarter and 2*quarter + 1
+  const int wkey = (l16 >> 1) & 7;
+  const int wf0 = fd::kW + l16 * 128 + (((2 * quarter) ^ wkey) << 4);
+  const int wf1 = fd::kW + l16 * 128 + (((2 * quarter + 1) ^ wkey) << 4);
+  const int xslot = l16 < fd::kM ? l16 : 0;
+  const int xf0 = fd::kX + xslot * 128 + ((2 * quarter) << 4);
+  const int xf1 = xf0 + 16;
+
+  for (int item = wid; item < total; item += active) {
+    // Tile of the item, every field wave-uniform (m-tile major, then n-blocks).
+    int bl = 0, bh = E - 1;
+    while (bl < bh) {
+      const int mid = (bl + bh + 1) >> 1;
+      if (__builtin_amdgcn_readfirstlane(tile_start[mid]) <= item) bl = mid; else bh = mid - 1;
+    }
+    const int e = __builtin_amdgcn_readfirstlane(bl);
+    const int local = item - __builtin_amdgcn_readfirstlane(tile_start[e]);
+    const int lo = min(max(ld_uniform8(offsets, e), 0), P);
+    const int hi = min(max(ld_uniform8(offsets, e + 1), lo), P);
+    const int mt = local / n_blocks;
+    const int nb = local - mt * n_blocks;
+    const int row0 = lo + mt * fd::kM;
+    const int rows = min(fd::kM, hi - row0);
+    int arow[fd::kM];
+#pragma unroll
+    for (int j = 0; j < fd::kM; ++j) {
+      const int sp = row0 + min(j, rows - 1);
+      const int64_t r = (a_sorted || sorted_ids == nullptr) ? (int64_t)sp : (int64_t)(ld_uniform8(sorted_ids, sp) / topk);
+      arow[j] = (r < 0 || r >= rows_a) ? 0 : (int)r;
+    }
+    const int64_t wrow = (int64_t)e * N + (int64_t)nb * 16;
+    const uint8_t* sw0 = w + (wrow + wr0) * K + wp0;
+    const uint8_t* sw1 = w + (wrow + wr1) * K + wp1;
+    const int xr = (lane >> 3) & 3;
+    const int xrow = xr == 0 ? arow[0] : xr == 1 ? arow[1] : xr == 2 ? arow[2] : arow[3];
+    const uint8_t* sx = a + (int64_t)xrow * K + ((lane & 7) << 4);
+    const int srow = lane < fd::kM ? (lane == 0 ? arow[0] : lane == 1 ? arow[1] : lane == 2 ? arow[2] : arow[3]) : arow[0];
+    const float* ssa = a_scale + srow;                                          // + g * rows_a
+    const float* ssw = w_scale + ((int64_t)e * (N / 128) + (nb * 16) / 128) * G;  // + g
+    auto issue = [&](int g) __attribute__((always_inline)) {
+      const uint32_t sl = lb + (uint32_t)((g % fd::kDepth) * fd::kSlot);
+      const int64_t ko = (int64_t)g * 128;
+      dma16(sw0 + ko, sl + fd::kW);
+      dma16(sw1 + ko, sl + fd::kW + 1024);
+      dma16(sx + ko, sl + fd::kX);
+      dma4(lane == fd::kM ? ssw + g : ssa + (int64_t)g * rows_a, sl + fd::kS);
+    };
+    const int npre = G < fd::kDepth ? G : fd::kDepth;
+    for (int g = 0; g < npre; ++g) issue(g);
+    v4f acc = v4f{};
+    for (int g = 0; g < G; ++g) {
+      const int after = G - 1 - g;
+      wait_groups(after < fd::kDepth - 1 ? after : fd::kDepth - 1);
+      const uint8_t* sp = myring + (g % fd::kDepth) * fd::kSlot;
+      const v8i wfr = __builtin_bit_cast(v8i, __builtin_shufflevector(ld16(sp + wf0), ld16(sp + wf1), 0, 1, 2, 3, 4, 5, 6, 7));
+      const v8i xfr = __builtin_bit_cast(v8i, __builtin_shufflevector(ld16(sp + xf0), ld16(sp + xf1), 0, 1, 2, 3, 4, 5, 6, 7));
+      const float* ss = reinterpret_cast<const float*>(sp + fd::kS);
+      const float sc = ss[xslot] * ss[fd::kM];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot is read; it may be refilled
+      if (g + fd::kDepth < G) issue(g + fd::kDepth);
+      const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfr, xfr, v4f{}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(p[i], sc, acc[i]);
+    }
+    // value i of lane l: weight row 4 * quarter + i, routed row l16 of the tile
+    if (l16 < rows) {
+      typedef typename OutT<OUT>::T T;
+      T* o = static_cast<T*>(out) + (int64_t)(row0 + l16) * N + nb * 16 + 4 * quarter;
+      if constexpr (sizeof(T) == 2) {
+        const u32 v0 = (u32)OutT<OUT>::from(acc[0]) | ((u32)OutT<OUT>::from(acc[1]) << 16);
+        const u32 v1 = (u32)OutT<OUT>::from(acc[2]) | ((u32)OutT<OUT>::from(acc[3]) << 16);
+        *reinterpret_cast<uint2*>(o) = make_uint2(v0, v1);
+      } else {
+        *reinterpret_cast<v4f*>(o) = acc;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_fp8(const GroupedArgs& g, const uint8_t* a, const float* a_scale,
                            const uint8_t* w, const float* w_scale, hipStream_t stream) {
+  // AUTO takes the decode schedule when experts hold few rows on average.
+  const bool decode = g.sched == 1 || (g.sched == 0 && g.P < (int64_t)16 * g.E);
+  if (decode) {
+    if (g.P == 0) return hipSuccess;
+    const int grid = g.num_cus * 2;
+#define MOEQ_FD(OK)                                                                                              \
+  hipLaunchKernelGGL(fp8_decode<OK>, dim3(grid), dim3(64 * fd::kWaves), 0, stream, a, a_scale, g.rows_a,         \
+                     g.a_sorted, w, w_scale, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N, g.K, g.out)
+    switch (g.out_kind) {
+      case OUT_BF16: MOEQ_FD(OUT_BF16); break;
+      case OUT_F16: MOEQ_FD(OUT_F16); break;
+      default: MOEQ_FD(OUT_F32); break;
+    }
+#undef MOEQ_FD
+    return hipGetLastError();
+  }
   // Upper bound on tiles: every expert adds at most one partial m-tile.
   const int64_t mt_ub = (g.P + kTileM - 1) / kTileM + std::min<int64_t>(g.E, g.P);
   const int64_t items_ub = mt_ub * (g.N / kTileN);

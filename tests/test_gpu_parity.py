@@ -181,6 +181,43 @@ def test_fp8_routed_scales_vary_on_every_index():
     assert_rows_close(host(y)[: ref.shape[0]], ref, what="fp8 routed")
 
 
+@pytest.mark.parametrize("sched", ["auto", "decode", "prefill"])
+@pytest.mark.parametrize("T,E,k,N,K,odt", [(8, 16, 4, 256, 512, torch.bfloat16),
+                                           (37, 5, 2, 384, 128, torch.float32),
+                                           (3, 64, 8, 128, 1152, torch.float16)])
+def test_fp8_decode_schedule(sched, T, E, k, N, K, odt):
+    # AUTO picks the weight-streaming decode schedule for all three (P < 16 E);
+    # both forced schedules must agree with the oracle.  K = 128 is one K
+    # group, K = 1152 is nine (past the ring depth, not a multiple of it);
+    # tiles of 1..4 rows; rows past offsets[E] stay untouched.
+    d = synth.fp8_block(33, 0, N, K, E=E, T=T, k=k)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    P = T * k
+    out = torch.full((P + 5, N), 7.0, dtype=odt, device="cuda")
+    mq.grouped_gemm_qfp8_block(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]), offs, srt, k,
+                               out_dtype=odt, sched=sched, out=out[:P])
+    ref = oracle.grouped_gemm_qfp8_block(d["a"], d["a_scale"], "token", d["w"], d["w_scale"],
+                                         host(offs), host(srt), k)["y"]
+    n = ref.shape[0]
+    assert_rows_close(host(out)[:n].astype(np.float64), ref, what=f"fp8 {sched}")
+    assert (host(out)[P:] == 7.0).all()
+
+
+def test_fp8_decode_sorted_rows_and_empty_experts():
+    # SORTED A (row = sorted position), experts 0 and 3 empty, tiles with 1..4 rows.
+    rng = np.random.default_rng(34)
+    E, N, K = 5, 256, 640
+    counts = np.array([0, 3, 9, 0, 6])
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    P = int(offs[-1])
+    a, sa = synth.fp8_quant_1x128(rng.standard_normal((P, K)).astype(np.float32))
+    d = synth.fp8_block(35, 0, N, K, E=E, T=4, k=2)
+    y = mq.grouped_gemm_qfp8_block(dev(a), dev(sa), dev(d["w"]), dev(d["w_scale"]), dev(offs), None, 1,
+                                   a_row="sorted", out_dtype=torch.float32, sched="decode")
+    ref = oracle.grouped_gemm_qfp8_block(a, sa, "sorted", d["w"], d["w_scale"], offs, None, 1)["y"]
+    assert_rows_close(host(y), ref, what="fp8 decode sorted")
+
+
 # ------------------------------------------------------------------ NVFP4
 @pytest.mark.parametrize("sched", ["prefill", "decode"])
 @pytest.mark.parametrize("act", ["none", "silu_mul"])
