@@ -1,6 +1,6 @@
 """Throughput of the quantized MoE grouped-GEMM path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload {0,1,2,3,4}]
+    python bench.py [--steps K] [--warmup W] [--workload {0,1,2,3,4,5,6}]
 
 One step is one pass of the whole hot path over one batch of seeded
 synthetic input already resident in HBM:
@@ -14,6 +14,8 @@ synthetic input already resident in HBM:
      route + FC1 (SiLU-gated) + FC2 (int4 rows in sorted order) + combine
   5  per-row INT4 quantization of 16384 fp16 rows of 14336 (the FC2 input
      of 4 in a full W4A4 chain)
+  6  FP8 block-scaled MoE projection, decode: 8 tokens, E=256, top-8,
+     N=4096 K=7168: route + FP8 GEMM (weight-streaming schedule)
 Prints ONE JSON line: whole-path throughput, the dominant kernel's roofline
 fraction (its launches timed with HIP events on the launch stream inside the
 timed region) and the CPU oracle's throughput on the host as a reported
@@ -106,10 +108,16 @@ class Workload:
             self.w, self.sw = _dev(d["w"]), _dev(d["w_scale"])
             self.y = torch.empty(P, d["N"], dtype=torch.bfloat16, device="cuda")
             self.flops = 2.0 * P * d["N"] * d["K"]
-            self.weight_bytes = float(self.w.numel() + self.sw.numel() * 4)
+            ids = d["topk_ids"].reshape(-1)
+            self.active = int(np.unique(ids[(ids >= 0) & (ids < E)]).size)
+            self.weight_bytes = float(self.active * (d["N"] * d["K"] + (d["N"] // 128) * (d["K"] // 128) * 4))
             self.dtype = "fp8_e4m3"
-            self.dom = ("fp8_prefill", ["gemm_fp8.hip", "common.h", "tile.h", "pipeline.h"], "mfma",
-                        PEAK["fp8"])
+            if idx == 6:
+                self.dom = ("fp8_decode", ["gemm_fp8.hip", "common.h", "tile.h", "pipeline.h"], "hbm",
+                            PEAK["hbm_GBps"])
+            else:
+                self.dom = ("fp8_prefill", ["gemm_fp8.hip", "common.h", "tile.h", "pipeline.h"], "mfma",
+                            PEAK["fp8"])
         elif kind == "int4":
             self.a, self.sa = _dev(d["a"]), _dev(d["a_scale"])
             self.w, self.sw = _dev(d["w"]), _dev(d["w_scale"])
@@ -212,7 +220,7 @@ class Workload:
             return self.weight_bytes
         if kind == "fp8":
             N, K = d["N"], d["K"]
-            return float(P * K + d["w"].size + d["a_scale"].size * 4 + d["w_scale"].size * 4 + P * N * 2)
+            return float(P * K + self.weight_bytes + d["a_scale"].size * 4 + P * N * 2)
         if kind == "int4":
             N, K = d["N"], d["K"]
             out = N * 2 if self.idx == 0 else N  # f16 y, or f16 h = N/2 columns
@@ -226,6 +234,8 @@ class Workload:
         d = self.d
         kind = self.cfg["kind"]
         if kind == "quant":
+            return self.weight_bytes, "byte"
+        if kind == "fp8" and self.idx == 6:
             return self.weight_bytes, "byte"
         if kind == "fp8":
             return 2.0 * self.T * self.k * d["N"] * d["K"], "flop"
@@ -246,7 +256,7 @@ def cpu_baseline(idx: int, d, budget_s: float = 10.0):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
     except Exception:
         cores = os.cpu_count()
-    kind = {0: "int4", 1: "fp8", 2: "nvfp4", 3: "nvfp4", 4: "int4", 5: "quant"}[idx]
+    kind = {0: "int4", 1: "fp8", 2: "nvfp4", 3: "nvfp4", 4: "int4", 5: "quant", 6: "fp8"}[idx]
     times = []
     if kind == "quant":
         x = d["x"]
@@ -260,6 +270,18 @@ def cpu_baseline(idx: int, d, budget_s: float = 10.0):
                     sample=f"{rows.size} of {x.shape[0]} rows, median of {len(times)} runs")
     off, srt, p2s, _ = oracle.route_prep(d["topk_ids"], d["E"])
     n = int(off[-1])
+    if kind == "fp8" and idx == 6:
+        # the rows of 4 active experts; weight GB/s over their bytes
+        experts = [e for e in range(d["E"]) if off[e + 1] > off[e]][:4]
+        rows = np.concatenate([np.arange(off[e], off[e + 1]) for e in experts])
+        nbytes = len(experts) * d["N"] * d["K"]
+        while sum(times) < budget_s and len(times) < 5:
+            t = time.perf_counter()
+            oracle.grouped_gemm_qfp8_block(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], off, srt,
+                                           d["k"], rows=rows)
+            times.append(time.perf_counter() - t)
+        return dict(value=nbytes / float(np.median(times)) / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                    sample=f"{rows.size} rows of {len(experts)} active experts, median of {len(times)} runs")
     if kind == "fp8":
         sample = "the whole workload (all rows)"
         work = 2.0 * n * d["N"] * d["K"]
@@ -343,12 +365,18 @@ def summarize_profiles(idx: int, pdir: str, steps: int = 50, warmup: int = 10):
         wl.d = synth.workload(idx)
         wl.T, wl.k, wl.E = wl.d["T"], wl.d["k"], wl.d["E"]
     d = wl.d
-    tag = {"fp8": "fp8_prefill", "int4": "int4_prefill", "quant": "quant_int4_rows_reg"}.get(cfg["kind"]) or \
+    tag = ("fp8_decode" if idx == 6 else None) or \
+        {"fp8": "fp8_prefill", "int4": "int4_prefill", "quant": "quant_int4_rows_reg"}.get(cfg["kind"]) or \
         ("nvfp4_decode" if idx == 2 else "nvfp4_prefill")
     srcs = {"fp8_prefill": ["gemm_fp8.hip", "common.h", "tile.h", "pipeline.h"],
+            "fp8_decode": ["gemm_fp8.hip", "common.h", "tile.h", "pipeline.h"],
             "int4_prefill": ["gemm_int4.hip", "common.h", "tile.h"],
             "quant_int4_rows_reg": ["quant.hip", "common.h"]}.get(
         tag, ["gemm_nvfp4.hip", "nvfp4.h", "common.h", "tile.h", "pipeline.h"])
+    if cfg["kind"] == "fp8":
+        ids = d["topk_ids"].reshape(-1)
+        active = int(np.unique(ids[(ids >= 0) & (ids < wl.E)]).size)
+        wl.weight_bytes = float(active * (d["N"] * d["K"] + (d["N"] // 128) * (d["K"] // 128) * 4))
     if cfg["kind"] == "nvfp4":
         H, I = d["H"], d["I"]
         ids = d["topk_ids"].reshape(-1)
@@ -436,7 +464,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=1, choices=sorted(__import__("synth").WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device 5 times (a kernel of known traffic "
@@ -507,7 +535,7 @@ def main():
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     cfg = wl.cfg
-    if args.workload in (2, 5):
+    if args.workload in (2, 5, 6):
         value, unit = wl.weight_bytes / (ms * 1e-3) / 1e9, "GB/s"
     else:
         value, unit = wl.flops / (ms * 1e-3) / 1e12, "TFLOP/s"
@@ -522,7 +550,7 @@ def main():
             "kernel": tag, "kernel_ms": round(dom_ms, 5)}
     config = {"workload": cfg["name"]}
     config.update({k: v for k, v in cfg.items() if k not in ("name", "kind")})
-    if args.workload == 2:
+    if args.workload in (2, 6):
         config["active_experts"] = wl.active
         config["weight_bytes"] = wl.weight_bytes
     rec = {"metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,

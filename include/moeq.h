@@ -152,7 +152,10 @@ moeq_status grouped_gemm_qint4(const uint8_t* a, const float* a_scale, int64_t r
  *   y[s][n] = sum_g a_scale[g][r] * w_scale[e][n/128][g]
  *                   * sum_{k in group g} a[r][k] * w[e][n][k]
  * Requires K % 128 == 0 and N % 128 == 0 (else MOEQ_EALIGN), 16-byte
- * aligned pointers, 1 <= E <= 1024, 1 <= topk <= 64.
+ * aligned pointers, 1 <= E <= 1024, 1 <= topk <= 64.  sched AUTO takes the
+ * weight-streaming schedule (waves streaming 16 weight rows x at most 4
+ * routed rows) when P < 16 * E, the 128x128 MFMA tiles otherwise; both
+ * compute the same sums, grouped per 128-wide K block as above.
  * ---------------------------------------------------------------------- */
 moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int64_t rows_a,
                                     moeq_arow a_row, const uint8_t* w, const float* w_scale,

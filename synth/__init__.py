@@ -178,6 +178,25 @@ def fp8_block(seed: int, M: int, N: int, K: int, E: int = 1, *, T: int = 0, k: i
     return d
 
 
+def fp8_moe(seed: int, T: int, E: int, k: int, N: int, K: int):
+    """FP8 e4m3 block-scaled MoE projection for decode (DeepSeek-V3 style
+    scales): A [T][K] from N(0,1) quantized per 1x128; W [E][N][K] with e4m3
+    codes uniform over all non-NaN bytes, generated for the routed experts
+    only (the others are never read and stay zero); w_scale [E][N/128][K/128]
+    uniform in [0.5, 1.5] / 448; ids distinct uniform over E."""
+    r = streams(seed)
+    ids = distinct_uniform_ids(r[ROLE_ROUTING], T, k, E)
+    a, sa = fp8_quant_1x128(r[ROLE_ACT].standard_normal((T, K), dtype=np.float32))
+    w = np.zeros((E, N, K), np.uint8)
+    for e in np.unique(ids[(ids >= 0) & (ids < E)]):
+        codes = uniform_bytes(r[ROLE_W1], (N, K))
+        codes[(codes & 0x7F) == 0x7F] ^= 1          # no NaN codes
+        w[e] = codes
+    w_scale = (r[ROLE_S1].uniform(0.5, 1.5, (E, N // 128, K // 128)) / 448.0).astype(np.float32)
+    return dict(a=a, a_scale=sa, w=w, w_scale=w_scale, topk_ids=ids,
+                topk_weights=softmax_weights(r[ROLE_LOGITS], T, k), T=T, E=E, k=k, N=N, K=K, M=T)
+
+
 def nvfp4_moe(seed: int, T: int, E: int, k: int, H: int, I: int, *, routing="distinct",
               scale_lo: int = 0x30, scale_hi: int = 0x47):
     """NVFP4 W4A16 MoE layer: x [T][H] bf16 from N(0,1); w1 (gate rows [0,I) then
@@ -217,6 +236,9 @@ WORKLOADS = {
     4: dict(name="w4a4_int4_mixtral_T8192", kind="int4", T=8192, E=8, k=2, H=4096, I=14336),
     # per-row int4 quantization of config 4's FC1 output h (T*k rows of I fp16)
     5: dict(name="int4_quantize_rows_16384x14336_f16", kind="quant", rows=16384, K=14336),
+    # the FP8 block-scaled kernel under routing: one 8-token decode step of a
+    # DeepSeek-V3-shaped expert projection (gate+up, N = 2I = 4096, K = H)
+    6: dict(name="fp8_block_moe_decode_T8", kind="fp8", T=8, E=256, k=8, N=4096, K=7168),
 }
 
 
@@ -240,4 +262,6 @@ def workload(idx: int):
         x = r[ROLE_ACT].standard_normal((c["rows"], c["K"]), dtype=np.float32)
         x *= r[ROLE_ACT_SCALE].uniform(0.1, 10.0, (c["rows"], 1)).astype(np.float32)
         return dict(x=x.astype(np.float16))
+    if idx == 6:
+        return fp8_moe(seed, c["T"], c["E"], c["k"], c["N"], c["K"])
     raise KeyError(idx)

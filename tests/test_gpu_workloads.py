@@ -128,3 +128,14 @@ def test_workload5_int4_quantizer_sampled_rows():
     ref_q, ref_s = oracle.quantize_int4_rows(x[rows])
     assert np.array_equal(host(wl.qs)[rows], ref_s)
     assert np.array_equal(host(wl.q)[rows], ref_q)
+
+
+def test_workload6_fp8_moe_decode_sampled_rows():
+    # the FP8 block-scaled kernel under routing, weight-streaming schedule
+    wl = _run(6)
+    off, srt, p2s, _ = _check_route(wl)
+    d = wl.d
+    rows = _sample_rows(off, n_per=2, max_experts=6)
+    ref = oracle.grouped_gemm_qfp8_block(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], off, srt,
+                                         d["k"], rows=rows)["y"]
+    assert_rows_close(host(wl.y)[rows], ref, what="fp8 decode full size")
