@@ -20,7 +20,8 @@ reordering.  Sources, by page:
     fp16 activations; its rule is a reading, see quant.py.)
   * megamoe_rm.cu (route_prep, fc1_rm, fc2_rm, combine kernels: stable
     per-expert ordering, -1 ids, per-expert global scale, SiLU-gated FC1,
-    k-ordered fp32 combine).
+    k-ordered fp32 combine; the up-first w13 and 128x4-swizzled scale layout
+    it reads, layouts.py).
 
 Parity pins: every function here is checked, in tests/test_oracle_*.py,
 against something other than itself (torch's codecs, brute force in pure
@@ -35,5 +36,6 @@ from .gemm import (grouped_gemm_qint4, grouped_gemm_qfp8_block, grouped_gemm_qnv
 from .combine import scatter_combine
 from .layer import int4_layer, nvfp4_layer, fp8_dense
 from .quant import quantize_int4_rows
+from .layouts import scale_swizzle_offset, unswizzle_scales, swizzle_scales, repack_nvfp4
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -1,0 +1,94 @@
+"""Pins of oracle/layouts.py (the FlashInfer/megamoe_rm.cu NVFP4 layout and
+its repack into the library's linear layout)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import layouts
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "nvfp4_scale_swizzle_offsets.txt")
+
+
+def test_hand_worked_offsets():
+    rows = [l.split() for l in open(GOLDEN) if l.strip() and not l.startswith("#")]
+    for r, c, off in rows:
+        assert layouts.scale_swizzle_offset(int(r), int(c), 8) == int(off), (r, c)
+
+
+@pytest.mark.parametrize("R,C", [(128, 4), (256, 12), (384, 28)])
+def test_offsets_are_a_permutation(R, C):
+    rr, cc = np.meshgrid(np.arange(R), np.arange(C), indexing="ij")
+    off = layouts.scale_swizzle_offset(rr, cc, C).ravel()
+    assert np.array_equal(np.sort(off), np.arange(R * C))
+
+
+def test_each_tile_holds_128_rows_by_4_columns():
+    R, C = 256, 12
+    rr, cc = np.meshgrid(np.arange(R), np.arange(C), indexing="ij")
+    tile = layouts.scale_swizzle_offset(rr, cc, C) // 512
+    for t in range(R * C // 512):
+        r, c = rr[tile == t], cc[tile == t]
+        assert r.size == 512
+        assert np.array_equal(np.unique(r), np.arange(128) + 128 * (t // (C // 4)))
+        assert np.array_equal(np.unique(c), np.arange(4) + 4 * (t % (C // 4)))
+
+
+def test_swizzle_round_trip():
+    rng = np.random.default_rng(3)
+    s = rng.integers(0, 256, (2, 256, 20), dtype=np.uint8)
+    sw = layouts.swizzle_scales(s)
+    assert sw.shape == (2, 256 * 20)
+    assert np.array_equal(layouts.unswizzle_scales(sw, 256, 20), s)
+
+
+def test_rejects_shapes_outside_the_tiling():
+    with pytest.raises(ValueError):
+        layouts.unswizzle_scales(np.zeros((1, 100 * 8), np.uint8), 100, 8)
+    with pytest.raises(ValueError):
+        layouts.swizzle_scales(np.zeros((1, 128, 6), np.uint8))
+
+
+def test_repacked_silu_layer_matches_the_page_layout_brute_force():
+    # w13 with up rows first and swizzled scales -> repack -> the oracle's
+    # gate-first SiLU-gated GEMM; against a per-element computation that reads
+    # the page's layout directly (up = rows [0, I), gate = rows [I, 2I), each
+    # scale found through the offset of its (row, block)).
+    rng = np.random.default_rng(4)
+    I, K, T = 64, 64, 3
+    R, C = 2 * I, K // 16
+    w = rng.integers(0, 256, (1, R, K // 2), dtype=np.uint8)
+    s_lin = rng.integers(0x30, 0x48, (1, R, C), dtype=np.uint8)
+    s_swz = layouts.swizzle_scales(s_lin)
+    x = oracle.round_to_bf16(rng.standard_normal((T, K)))
+    xb = (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    gs = np.array([0.75], np.float32)
+    w2, s2 = layouts.repack_nvfp4(w, s_swz, swap_halves=True)
+    offs = np.array([0, T], np.int32)
+    h = oracle.grouped_gemm_qnvfp4(xb, "sorted", w2, s2, gs, offs, None, 1, act="silu_mul")["y"]
+
+    def e2m1(code):
+        sgn, e, m = code >> 3, (code >> 1) & 3, code & 1
+        mag = m / 2 if e == 0 else 2.0 ** (e - 1) * (1 + m / 2)
+        return -mag if sgn else mag
+
+    def ue4m3(b):
+        e, m = (b >> 3) & 15, b & 7
+        return 2.0 ** -6 * m / 8 if e == 0 else 2.0 ** (e - 7) * (1 + m / 8)
+
+    flat = s_swz[0]
+    for t in range(T):
+        for j in range(I):
+            acc = {}
+            for name, row in (("up", j), ("gate", I + j)):
+                total = 0.0
+                for k in range(K):
+                    byte = int(w[0, row, k // 2])
+                    code = byte & 15 if k % 2 == 0 else byte >> 4
+                    sc = ue4m3(int(flat[layouts.scale_swizzle_offset(row, k // 16, C)]))
+                    total += float(x[t, k]) * e2m1(code) * sc
+                acc[name] = 0.75 * total
+            g, u = acc["gate"], acc["up"]
+            want = g / (1 + np.exp(-g)) * u
+            assert abs(h[t, j] - want) <= 1e-12 * max(1.0, abs(want))
