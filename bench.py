@@ -1,6 +1,6 @@
 """Throughput of the quantized MoE grouped-GEMM path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload {0,1,2,3,4,5,6}]
+    python bench.py [--steps K] [--warmup W] [--workload {0,1,2,3,4,5,6,7}]
 
 One step is one pass of the whole hot path over one batch of seeded
 synthetic input already resident in HBM:
@@ -16,6 +16,8 @@ synthetic input already resident in HBM:
      of 4 in a full W4A4 chain)
   6  FP8 block-scaled MoE projection, decode: 8 tokens, E=256, top-8,
      N=4096 K=7168: route + FP8 GEMM (weight-streaming schedule)
+  7  one-shot NVFP4 weight repack of 2's gate+up weights (E=256, 4096 rows,
+     K=7168) from the up-first, 128x4-swizzled-scale layout of megamoe_rm.cu
 Prints ONE JSON line: whole-path throughput, the dominant kernel's roofline
 fraction (its launches timed with HIP events on the launch stream inside the
 timed region) and the CPU oracle's throughput on the host as a reported
@@ -86,6 +88,9 @@ class Workload:
         self.mq, self.idx = mq, idx
         self.cfg = synth.WORKLOADS[idx]
         self.d = d = synth.workload(idx)
+        if self.cfg["kind"] == "repack":
+            self._init_repack(torch)
+            return
         if self.cfg["kind"] == "quant":
             self.E, self.k, self.T = 1, 1, self.cfg["rows"]
         else:
@@ -169,6 +174,17 @@ class Workload:
         self.dtype = "f16_to_int4"
         self.dom = ("quant_int4_rows_reg", ["quant.hip", "common.h"], "hbm", PEAK["hbm_GBps"])
 
+    def _init_repack(self, torch):
+        d = self.d
+        self.E, self.k, self.T = d["E"], 1, 0
+        self.w_in, self.sf_in = _dev(d["w"]), _dev(d["sf"])
+        self.w_out = torch.empty_like(self.w_in)
+        self.sf_out = torch.empty(d["E"], d["N"], d["K"] // 16, dtype=torch.uint8, device="cuda")
+        self.weight_bytes = repack_bytes(d["E"], d["N"], d["K"])
+        self.flops = 0.0
+        self.dtype = "u8"
+        self.dom = ("repack_nvfp4", ["repack.hip", "kernels.h", "common.h"], "hbm", PEAK["hbm_GBps"])
+
     def step(self, ev=None):
         """One pass of the path; `ev` = (start, end) events around the
         dominant kernel."""
@@ -177,6 +193,12 @@ class Workload:
         if kind == "quant":
             if ev: ev[0].record()
             mq.quantize_int4_rows(self.x, q=self.q, scale=self.qs)
+            if ev: ev[1].record()
+            return
+        if kind == "repack":
+            if ev: ev[0].record()
+            mq.nvfp4_repack(self.w_in, self.sf_in, swap_halves=bool(self.cfg["swap"]), w_out=self.w_out,
+                            sf_out=self.sf_out)
             if ev: ev[1].record()
             return
         offs, srt, p2s, _ = mq.moe_route_prep(self.ids, self.E, out=self.route_out, workspace=self.ws)
@@ -209,14 +231,14 @@ class Workload:
 
     def dominant_launches(self):
         """(launches of the dominant kernel per step, index of the timed one)."""
-        return (1, 0) if self.cfg["kind"] in ("fp8", "quant") or self.idx == 0 else (2, 0)
+        return (1, 0) if self.cfg["kind"] in ("fp8", "quant", "repack") or self.idx == 0 else (2, 0)
 
     def dominant_bytes(self):
         """Fewest HBM bytes one launch of the dominant kernel can move: every
         operand read once, every output written once."""
         d, P = self.d, self.T * self.k
         kind = self.cfg["kind"]
-        if kind == "quant":
+        if kind in ("quant", "repack"):
             return self.weight_bytes
         if kind == "fp8":
             N, K = d["N"], d["K"]
@@ -233,7 +255,7 @@ class Workload:
         (value, unit) in bytes (HBM-bound) or flops (MFMA-bound)."""
         d = self.d
         kind = self.cfg["kind"]
-        if kind == "quant":
+        if kind in ("quant", "repack"):
             return self.weight_bytes, "byte"
         if kind == "fp8" and self.idx == 6:
             return self.weight_bytes, "byte"
@@ -247,6 +269,12 @@ class Workload:
         return 2.0 * int(((ids >= 0) & (ids < self.E)).sum()) * 2 * d["I"] * d["H"], "flop"
 
 
+def repack_bytes(E, N, K):
+    """Bytes a repack must move: every weight and scale byte read once and
+    written once."""
+    return float(2 * E * N * (K // 2 + K // 16))
+
+
 # ---------------------------------------------------------------- CPU oracle
 def cpu_baseline(idx: int, d, budget_s: float = 10.0):
     """The CPU oracle, as it stands, on a bounded sample of the workload."""
@@ -256,8 +284,18 @@ def cpu_baseline(idx: int, d, budget_s: float = 10.0):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
     except Exception:
         cores = os.cpu_count()
-    kind = {0: "int4", 1: "fp8", 2: "nvfp4", 3: "nvfp4", 4: "int4", 5: "quant", 6: "fp8"}[idx]
+    kind = {0: "int4", 1: "fp8", 2: "nvfp4", 3: "nvfp4", 4: "int4", 5: "quant", 6: "fp8",
+            7: "repack"}[idx]
     times = []
+    if kind == "repack":
+        ne = 64
+        nbytes = repack_bytes(ne, d["N"], d["K"])
+        while sum(times) < budget_s and len(times) < 5:
+            t = time.perf_counter()
+            oracle.repack_nvfp4(d["w"][:ne], d["sf"][:ne], True)
+            times.append(time.perf_counter() - t)
+        return dict(value=nbytes / float(np.median(times)) / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                    sample=f"{ne} of {d['E']} experts, median of {len(times)} runs")
     if kind == "quant":
         x = d["x"]
         rows = np.arange(0, x.shape[0], 64)
@@ -344,7 +382,7 @@ def _csv_rows(path):
 
 def _short_name(name):
     """Kernel base name: no return type, namespaces, template or call arguments."""
-    base = name.split("(")[0] if not name.startswith("void ") else name[5:]
+    base = name[5:] if name.startswith("void ") else name
     base = base.replace("(anonymous namespace)::", "").split("(")[0].split("<")[0]
     return base.split("::")[-1]
 
@@ -361,17 +399,23 @@ def summarize_profiles(idx: int, pdir: str, steps: int = 50, warmup: int = 10):
         wl.d = {}
         wl.T, wl.k, wl.E = cfg["rows"], 1, 1
         wl.weight_bytes = float(cfg["rows"] * (2 * cfg["K"] + cfg["K"] // 2 + 4))
+    elif cfg["kind"] == "repack":
+        wl.d = {}
+        wl.T, wl.k, wl.E = 0, 1, cfg["E"]
+        wl.weight_bytes = repack_bytes(cfg["E"], cfg["N"], cfg["K"])
     else:
         wl.d = synth.workload(idx)
         wl.T, wl.k, wl.E = wl.d["T"], wl.d["k"], wl.d["E"]
     d = wl.d
     tag = ("fp8_decode" if idx == 6 else None) or \
-        {"fp8": "fp8_prefill", "int4": "int4_prefill", "quant": "quant_int4_rows_reg"}.get(cfg["kind"]) or \
+        {"fp8": "fp8_prefill", "int4": "int4_prefill", "quant": "quant_int4_rows_reg",
+         "repack": "repack_nvfp4"}.get(cfg["kind"]) or \
         ("nvfp4_decode" if idx == 2 else "nvfp4_prefill")
     srcs = {"fp8_prefill": ["gemm_fp8.hip", "common.h", "tile.h", "pipeline.h"],
             "fp8_decode": ["gemm_fp8.hip", "common.h", "tile.h", "pipeline.h"],
             "int4_prefill": ["gemm_int4.hip", "common.h", "tile.h"],
-            "quant_int4_rows_reg": ["quant.hip", "common.h"]}.get(
+            "quant_int4_rows_reg": ["quant.hip", "common.h"],
+            "repack_nvfp4": ["repack.hip", "kernels.h", "common.h"]}.get(
         tag, ["gemm_nvfp4.hip", "nvfp4.h", "common.h", "tile.h", "pipeline.h"])
     if cfg["kind"] == "fp8":
         ids = d["topk_ids"].reshape(-1)
@@ -535,7 +579,7 @@ def main():
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     cfg = wl.cfg
-    if args.workload in (2, 5, 6):
+    if args.workload in (2, 5, 6, 7):
         value, unit = wl.weight_bytes / (ms * 1e-3) / 1e9, "GB/s"
     else:
         value, unit = wl.flops / (ms * 1e-3) / 1e12, "TFLOP/s"

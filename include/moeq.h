@@ -8,6 +8,9 @@
  *   grouped_gemm_qfp8_block FP8 e4m3 GEMM, 1x128 A / 128x128 B block scales
  *   grouped_gemm_qnvfp4     NVFP4 (E2M1 + UE4M3 per-16 + global) x bf16 GEMM
  *   moe_scatter_combine     top-k weighted sum back to token rows
+ * with two helpers around it:
+ *   moe_quantize_int4       per-row INT4 activation quantization
+ *   moe_nvfp4_repack        one-shot NVFP4 weight layout conversion
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer (memory the caller allocated
@@ -100,7 +103,7 @@ int32_t moeq_abi_version(void);
  *                                     than -1 (those pairs are skipped too)
  *   workspace       device scratch of moe_route_prep_workspace_bytes() bytes
  *                   (may be NULL when that is 0); contents on entry ignored
- * Requires T >= 0, 1 <= topk <= 64, 1 <= E <= 4096, T*topk < 2^31.
+ * Requires T >= 0, 1 <= topk <= 64, 1 <= E <= 1024, T*topk < 2^31.
  * T == 0 writes expert_offsets = 0 and n_invalid = 0.
  * ---------------------------------------------------------------------- */
 size_t moe_route_prep_workspace_bytes(int64_t T, int32_t topk, int32_t E); /* host */
@@ -174,7 +177,10 @@ moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int6
  *   x         bf16  [rows_a][K]       activations
  *   w         uint8 [E][N][K/2]       E2M1 codes
  *   w_sf      uint8 [E][N][K/16]      UE4M3 block scales (sign bit clear;
- *                                     0x7F is not a valid scale)
+ *                                     0x7F is not a valid scale).  [TLK]'s
+ *                                     uint32 [E][N][K/64] packing (block
+ *                                     4g+j in bits 8j..8j+7 of word g) is
+ *                                     the same bytes and may be passed as is
  *   w_gscale  f32   [E]               per-expert global scale
  *   out       [P][N] (NONE) or [P][N/2] (SILU_MUL), BF16 | F16 | F32
  *   y[s][n] = w_gscale[e] * sum_k x[r][k] * e2m1(w[e][n][k])
@@ -230,6 +236,33 @@ moeq_status moe_quantize_int4(const void* x, moeq_dtype x_dtype, int64_t rows, i
 moeq_status moe_scatter_combine(const void* y, moeq_dtype y_dtype, const int32_t* pair_to_sorted,
                                 const float* topk_weights, int64_t T, int32_t topk, int64_t N,
                                 moeq_dtype out_dtype, void* out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_nvfp4_repack - convert NVFP4 expert weights from the layout [MMRM]
+ * reads in place (its header comment and scale_off) to the layout of
+ * grouped_gemm_qnvfp4.  One-shot, at weight-load time.
+ *
+ *   w_in    uint8 [E][N][K/2]   E2M1 codes, rows as stored for [MMRM]
+ *   sf_in   uint8 [E][N*K/16]   UE4M3 scales of each expert's [N][K/16]
+ *                               scale matrix in 128x4 tiles: the byte of
+ *                               row r, block column c sits at
+ *                                 ((r/128)*(K/64) + c/4) * 512
+ *                                 + (r%32)*16 + ((r/32)%4)*4 + c%4
+ *   swap_halves  0: rows keep their order (a w2 / down projection);
+ *                1: the matrix is a w13 with the up rows [0, N/2) first
+ *                   and the gate rows [N/2, N) second; the output puts the
+ *                   gate rows first, the order of MOEQ_ACT_SILU_MUL
+ *   w_out   uint8 [E][N][K/2]   out: row n = input row n (swap 0) or
+ *                               (n + N/2) mod N (swap 1)
+ *   sf_out  uint8 [E][N][K/16]  out: row-major scales, rows as w_out
+ * A pure byte permutation: the outputs are bit-exact copies of input bytes.
+ * Requires 1 <= E <= 1024, N % 128 == 0 and K % 64 == 0 (else MOEQ_EALIGN),
+ * N*K < 2^36, all four pointers non-NULL and 16-byte aligned, and the two
+ * outputs disjoint from each other and from the inputs (no in-place repack:
+ * MOEQ_EINVAL).  The per-expert global scale needs no repack.
+ * ---------------------------------------------------------------------- */
+moeq_status moe_nvfp4_repack(const uint8_t* w_in, const uint8_t* sf_in, int64_t E, int64_t N, int64_t K,
+                             int32_t swap_halves, uint8_t* w_out, uint8_t* sf_out, void* stream);
 
 #ifdef __cplusplus
 }

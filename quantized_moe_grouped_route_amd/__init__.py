@@ -30,7 +30,8 @@ _DTYPE_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32, tor
 
 EXPORTS = ("moeq_last_error", "moeq_abi_version", "moe_route_prep_workspace_bytes",
            "moe_route_prep", "grouped_gemm_qint4", "grouped_gemm_qfp8_block",
-           "grouped_gemm_qnvfp4", "moe_scatter_combine", "moe_quantize_int4")
+           "grouped_gemm_qnvfp4", "moe_scatter_combine", "moe_quantize_int4",
+           "moe_nvfp4_repack")
 
 
 class MoeqError(RuntimeError):
@@ -64,6 +65,7 @@ def lib():
                                       i32, i32, vp, i32, vp]),
         "moe_scatter_combine": (i32, [vp, i32, vp, vp, i64, i32, i64, i32, vp, vp]),
         "moe_quantize_int4": (i32, [vp, i32, i64, i64, vp, vp, vp]),
+        "moe_nvfp4_repack": (i32, [vp, vp, i64, i64, i64, i32, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -206,10 +208,14 @@ def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, t
                         a_row="token", act="none", out_dtype=torch.bfloat16, out=None, P=None,
                         sched="auto"):
     """NVFP4 W4A16 grouped GEMM: x bf16 [rows_a][K], w uint8 [E][N][K/2]
-    (E2M1), w_sf uint8 [E][N][K/16] (UE4M3), w_gscale f32 [E].  Returns out
-    [P][N] (act 'none') or [P][N/2] ('silu_mul')."""
+    (E2M1), w_sf uint8 [E][N][K/16] (UE4M3) or int32 [E][N][K/64] (four
+    UE4M3 per word, block 4g+j in bits 8j..8j+7: the same bytes), w_gscale
+    f32 [E].  Returns out [P][N] (act 'none') or [P][N/2] ('silu_mul')."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w, "w", torch.uint8, 3)
+    if isinstance(w_sf, torch.Tensor) and w_sf.dtype == torch.int32 and w_sf.dim() == 3:
+        _need(w_sf, "w_sf", torch.int32, 3)
+        w_sf = w_sf.view(torch.uint8)                   # [E][N][K/64] words -> [E][N][K/16] bytes
     _need(w_sf, "w_sf", torch.uint8, 3)
     _need(w_gscale, "w_gscale", torch.float32, 1)
     E, P, arow = _grouped_common(x, expert_offsets, sorted_pair_ids, a_row, P)
@@ -262,7 +268,32 @@ def quantize_int4_rows(x, *, q=None, scale=None):
     _need(q, "q", (torch.uint8,), 2)
     _need(scale, "scale", (torch.float32,), 1)
     if tuple(q.shape) != (rows, K // 2) or tuple(scale.shape) != (rows,):
-        raise MoeqError("quantize_int4_rows: q must be [rows][K/2] and scale [rows]")
+        raise ValueError("quantize_int4_rows: q must be [rows][K/2] and scale [rows]")
     st = lib().moe_quantize_int4(_ptr(x), _DTYPE_CODE[x.dtype], rows, K, _ptr(q), _ptr(scale), _stream())
     _check("moe_quantize_int4", st)
     return q, scale
+
+
+def nvfp4_repack(w, sf_swizzled, *, swap_halves: bool, w_out=None, sf_out=None):
+    """Convert NVFP4 expert weights from the in-place layout of megamoe_rm.cu
+    (w uint8 [E][N][K/2]; sf_swizzled uint8 [E][N*K/16] in 128x4 tiles;
+    swap_halves for a w13 stored up rows first) to grouped_gemm_qnvfp4's
+    layout.  Returns (w_out [E][N][K/2], sf_out [E][N][K/16])."""
+    _need(w, "w", torch.uint8, 3)
+    _need(sf_swizzled, "sf_swizzled", torch.uint8, 2)
+    E, N, Kh = w.shape
+    K = 2 * Kh
+    if tuple(sf_swizzled.shape) != (E, N * K // 16):
+        raise ValueError("sf_swizzled must be [E][N*K/16]")
+    if w_out is None:
+        w_out = torch.empty_like(w)
+    if sf_out is None:
+        sf_out = torch.empty(E, N, K // 16, dtype=torch.uint8, device=w.device)
+    _need(w_out, "w_out", torch.uint8, 3)
+    _need(sf_out, "sf_out", torch.uint8, 3)
+    if tuple(w_out.shape) != (E, N, Kh) or tuple(sf_out.shape) != (E, N, K // 16):
+        raise ValueError("w_out must be [E][N][K/2] and sf_out [E][N][K/16]")
+    st = lib().moe_nvfp4_repack(_ptr(w), _ptr(sf_swizzled), E, N, K, int(bool(swap_halves)),
+                                _ptr(w_out), _ptr(sf_out), _stream())
+    _check("moe_nvfp4_repack", st)
+    return w_out, sf_out

@@ -47,4 +47,9 @@ hipError_t launch_gemm_fp8(const GroupedArgs& g, const uint8_t* a, const float* 
 hipError_t launch_gemm_nvfp4(const GroupedArgs& g, const uint16_t* x, const uint8_t* w,
                              const uint8_t* w_sf, const float* w_gscale, hipStream_t stream);
 
+// NVFP4 weight repack: megamoe_rm.cu layout (swizzled scales, optionally up
+// rows first) -> grouped_gemm_qnvfp4's, E experts of N rows and K columns.
+hipError_t launch_repack_nvfp4(const uint8_t* w_in, const uint8_t* sf_in, int64_t E, int64_t N, int64_t K,
+                               int swap_halves, uint8_t* w_out, uint8_t* sf_out, hipStream_t stream);
+
 }  // namespace moeq

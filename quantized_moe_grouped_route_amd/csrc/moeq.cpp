@@ -232,4 +232,31 @@ moeq_status moe_quantize_int4(const void* x, moeq_dtype x_dtype, int64_t rows, i
                     fn);
 }
 
+moeq_status moe_nvfp4_repack(const uint8_t* w_in, const uint8_t* sf_in, int64_t E, int64_t N, int64_t K,
+                             int32_t swap_halves, uint8_t* w_out, uint8_t* sf_out, void* stream) {
+  const char* fn = "moe_nvfp4_repack";
+  if (E < 1 || E > kMaxE) return fail(MOEQ_EINVAL, "%s: E=%lld outside [1, %d]", fn, (long long)E, kMaxE);
+  if (N <= 0 || K <= 0 || N > (1 << 20) || K > (1 << 17))
+    return fail(MOEQ_EINVAL, "%s: N=%lld K=%lld out of range", fn, (long long)N, (long long)K);
+  if (N * K >= (int64_t(1) << 36)) return fail(MOEQ_EINVAL, "%s: N*K=%lld too large", fn, (long long)(N * K));
+  if (N % 128 != 0 || K % 64 != 0)
+    return fail(MOEQ_EALIGN, "%s: N=%lld must be a multiple of 128 and K=%lld of 64 (128x4 scale tiles)", fn,
+                (long long)N, (long long)K);
+  if (swap_halves != 0 && swap_halves != 1) return fail(MOEQ_EINVAL, "%s: swap_halves=%d", fn, swap_halves);
+  if (!w_in || !sf_in || !w_out || !sf_out) return fail(MOEQ_EINVAL, "%s: null pointer", fn);
+  if (!aligned(w_in, 16) || !aligned(sf_in, 16) || !aligned(w_out, 16) || !aligned(sf_out, 16))
+    return fail(MOEQ_EALIGN, "%s: pointers must be 16-byte aligned", fn);
+  const uintptr_t wb = (uintptr_t)(E * N * (K / 2)), sb = (uintptr_t)(E * N * (K / 16));
+  auto overlap = [](const void* a, uintptr_t na, const void* b, uintptr_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+  };
+  if (overlap(w_out, wb, w_in, wb) || overlap(w_out, wb, sf_in, sb) || overlap(w_out, wb, sf_out, sb) ||
+      overlap(sf_out, sb, w_in, wb) || overlap(sf_out, sb, sf_in, sb))
+    return fail(MOEQ_EINVAL, "%s: an output overlaps an input or the other output (no in-place repack)", fn);
+  return hip_status(moeq::launch_repack_nvfp4(w_in, sf_in, E, N, K, swap_halves, w_out, sf_out,
+                                              (hipStream_t)stream),
+                    fn);
+}
+
 }  // extern "C"

@@ -224,8 +224,20 @@ def nvfp4_moe(seed: int, T: int, E: int, k: int, H: int, I: int, *, routing="dis
     return d
 
 
-# ------------------------------------------------------ the five workloads
-# Sizes of the five measured workloads (seed = 1000 + index).
+def nvfp4_stored_weights(seed: int, E: int, N: int, K: int):
+    """NVFP4 expert weights as another runtime stores them (megamoe_rm.cu's
+    in-place layout): w [E][N][K/2] uniform E2M1 code bytes and the UE4M3
+    scales of each expert as one run of N*K/16 bytes, sf [E][N*K/16].  The
+    scale bytes are drawn iid, so drawing them directly in the stored byte
+    order gives the same distribution as drawing a [N][K/16] matrix and
+    rearranging it; no layout arithmetic happens here."""
+    r = streams(seed)
+    return dict(w=uniform_bytes(r[ROLE_W1], (E, N, K // 2)),
+                sf=scale_bytes(r[ROLE_S1], (E, N * K // 16)), E=E, N=N, K=K)
+
+
+# ------------------------------------------------------ the measured workloads
+# Sizes of the measured workloads (seed = 1000 + index).
 WORKLOADS = {
     0: dict(name="w4a4_int4_tiny", kind="int4", T=64, E=4, k=2, N=256, K=256),
     1: dict(name="fp8_block_dense_1024x4096x7168", kind="fp8", M=1024, N=4096, K=7168),
@@ -239,6 +251,10 @@ WORKLOADS = {
     # the FP8 block-scaled kernel under routing: one 8-token decode step of a
     # DeepSeek-V3-shaped expert projection (gate+up, N = 2I = 4096, K = H)
     6: dict(name="fp8_block_moe_decode_T8", kind="fp8", T=8, E=256, k=8, N=4096, K=7168),
+    # one-shot repack of workload 2's gate+up weights (E=256 experts of
+    # 2I = 4096 rows, K = H = 7168) from the up-first, 128x4-swizzled-scale
+    # layout of megamoe_rm.cu
+    7: dict(name="nvfp4_repack_w13_E256_N4096_K7168", kind="repack", E=256, N=4096, K=7168, swap=1),
 }
 
 
@@ -264,4 +280,6 @@ def workload(idx: int):
         return dict(x=x.astype(np.float16))
     if idx == 6:
         return fp8_moe(seed, c["T"], c["E"], c["k"], c["N"], c["K"])
+    if idx == 7:
+        return nvfp4_stored_weights(seed, c["E"], c["N"], c["K"])
     raise KeyError(idx)

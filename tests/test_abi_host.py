@@ -166,3 +166,24 @@ def test_binding_raises_without_gpu_tensors():
     import torch
     with pytest.raises(ValueError):
         mq.moe_route_prep(torch.zeros(4, 2, dtype=torch.int32), 4)
+
+
+def _repack(L, **kw):
+    a = dict(w=A16, sf=0x20000, E=2, N=256, K=128, swap=1, wo=0x40000, so=0x80000)
+    a.update(kw)
+    return L.moe_nvfp4_repack(a["w"], a["sf"], a["E"], a["N"], a["K"], a["swap"], a["wo"], a["so"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=192), mq.EALIGN), (dict(K=96), mq.EALIGN), (dict(E=0), mq.EINVAL),
+    (dict(E=1025), mq.EINVAL), (dict(swap=2), mq.EINVAL), (dict(w=None), mq.EINVAL),
+    (dict(so=None), mq.EINVAL), (dict(sf=0x20008), mq.EALIGN), (dict(wo=ODD), mq.EALIGN),
+    (dict(wo=A16), mq.EINVAL),                          # in place
+    (dict(wo=0x10000 + 0x3000), mq.EINVAL),             # overlaps the tail of w_in
+    (dict(so=0x40000 + 0x7000), mq.EINVAL),             # overlaps w_out
+    (dict(so=0x20000), mq.EINVAL),                      # scales in place
+    (dict(N=1 << 20, K=1 << 17), mq.EINVAL),            # N*K too large
+])
+def test_repack_rejects(L, kw, status):
+    assert _repack(L, **kw) == status
+    assert b"moe_nvfp4_repack" in L.moeq_last_error()

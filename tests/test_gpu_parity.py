@@ -379,3 +379,69 @@ def test_w4a4_chain_with_quantized_activations():
     out = mq.moe_scatter_combine(y, p2s, dev(d["topk_weights"]), out_dtype=torch.float32)
     ref_out = oracle.scatter_combine(host(y).astype(np.float64), host(p2s), d["topk_weights"])
     assert_rows_close(host(out), ref_out, what="chain combine")
+
+
+# ------------------------------------------------------- NVFP4 layout repack
+@pytest.mark.parametrize("E,N,K", [(1, 128, 64), (3, 256, 128), (2, 384, 1216), (2, 512, 2176),
+                                   (1, 256, 4096)])
+@pytest.mark.parametrize("swap", [False, True])
+def test_nvfp4_repack_bit_exact(E, N, K, swap):
+    # K/64 = 1, 2, 19, 34, 64 scale quads per row: a partial 16-tile group,
+    # ragged tails and whole groups; N/128 = 1..4 row blocks.
+    d = synth.nvfp4_stored_weights(60 + N + K, E, N, K)
+    w_out, sf_out = mq.nvfp4_repack(dev(d["w"]), dev(d["sf"]), swap_halves=swap)
+    rw, rs = oracle.repack_nvfp4(d["w"], d["sf"], swap)
+    assert np.array_equal(host(w_out), rw)
+    assert np.array_equal(host(sf_out), rs)
+
+
+def test_nvfp4_repack_leaves_bytes_outside_untouched():
+    E, N, K = 2, 256, 256
+    d = synth.nvfp4_stored_weights(70, E, N, K)
+    w_big = torch.full((E + 1, N, K // 2), 0xA5, dtype=torch.uint8, device="cuda")
+    s_big = torch.full((E + 1, N, K // 16), 0x5A, dtype=torch.uint8, device="cuda")
+    mq.nvfp4_repack(dev(d["w"]), dev(d["sf"]), swap_halves=True, w_out=w_big[:E], sf_out=s_big[:E])
+    rw, rs = oracle.repack_nvfp4(d["w"], d["sf"], True)
+    assert np.array_equal(host(w_big[:E]), rw) and np.array_equal(host(s_big[:E]), rs)
+    assert bool((w_big[E] == 0xA5).all()) and bool((s_big[E] == 0x5A).all())
+
+
+def test_nvfp4_repacked_layer_matches_gate_first_layer():
+    # Weights generated gate-first (the library's layout) are put into the
+    # up-first, swizzled layout on the host, repacked on the GPU, and must
+    # give back the original bytes and the same FC1 (SiLU-gated) and FC2
+    # outputs as the original layout.
+    T, E, k, H, I = 96, 4, 2, 384, 256
+    d = synth.nvfp4_moe(61, T, E, k, H, I, routing="repeat")
+    up_first = np.concatenate([d["w1"][:, I:], d["w1"][:, :I]], axis=1)
+    s_up_first = oracle.swizzle_scales(np.concatenate([d["s1"][:, I:], d["s1"][:, :I]], axis=1))
+    s2_swz = oracle.swizzle_scales(d["s2"])
+    w1, s1 = mq.nvfp4_repack(dev(up_first), dev(s_up_first), swap_halves=True)
+    w2, s2 = mq.nvfp4_repack(dev(d["w2"]), dev(s2_swz), swap_halves=False)
+    assert np.array_equal(host(w1), d["w1"]) and np.array_equal(host(s1), d["s1"])
+    assert np.array_equal(host(w2), d["w2"]) and np.array_equal(host(s2), d["s2"])
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    h = mq.grouped_gemm_qnvfp4(dev(d["x"]), w1, s1, dev(d["g1"]), offs, srt, k, act="silu_mul")
+    ref_h = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], host(offs), host(srt),
+                                       k, act="silu_mul")["y"]
+    assert_rows_close(host(h)[: ref_h.shape[0]], ref_h, what="FC1 on repacked weights")
+    y = mq.grouped_gemm_qnvfp4(h, w2, s2, dev(d["g2"]), offs, srt, k, a_row="sorted",
+                               out_dtype=torch.float32)
+    ref_y = oracle.grouped_gemm_qnvfp4(bf16_bits(h), "sorted", d["w2"], d["s2"], d["g2"], host(offs),
+                                       host(srt), k)["y"]
+    assert_rows_close(host(y)[: ref_y.shape[0]], ref_y, what="FC2 on repacked weights")
+
+
+def test_nvfp4_u32_packed_scales_are_the_same_bytes():
+    # [TLK]'s packed form: word g of a row holds blocks 4g..4g+3, block 4g+j
+    # in bits 8j..8j+7; built here with explicit shifts, not a memory view
+    T, E, k, H, I = 40, 3, 2, 256, 128
+    d = synth.nvfp4_moe(62, T, E, k, H, I)
+    b = d["s1"].astype(np.uint32).reshape(E, 2 * I, H // 64, 4)
+    packed = (b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)).astype(np.uint32)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    y = mq.grouped_gemm_qnvfp4(dev(d["x"]), dev(d["w1"]), dev(packed.view(np.int32)), dev(d["g1"]), offs, srt,
+                               k, act="silu_mul", out_dtype=torch.float32)
+    ref = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], host(offs), host(srt), k,
+                                     act="silu_mul")["y"]
+    assert_rows_close(host(y)[: ref.shape[0]], ref, what="nvfp4 u32-packed scales")

@@ -139,3 +139,14 @@ def test_workload6_fp8_moe_decode_sampled_rows():
     ref = oracle.grouped_gemm_qfp8_block(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], off, srt,
                                          d["k"], rows=rows)["y"]
     assert_rows_close(host(wl.y)[rows], ref, what="fp8 decode full size")
+
+
+def test_workload7_nvfp4_repack_sampled_experts():
+    wl = _run(7)
+    d = wl.d
+    experts = np.unique(np.concatenate([[0, 1, d["E"] - 1],
+                                        np.random.default_rng(7).integers(0, d["E"], 3)]))
+    for e in experts:
+        rw, rs = oracle.repack_nvfp4(d["w"][e:e + 1], d["sf"][e:e + 1], bool(wl.cfg["swap"]))
+        assert np.array_equal(host(wl.w_out[int(e)]), rw[0]), e
+        assert np.array_equal(host(wl.sf_out[int(e)]), rs[0]), e
