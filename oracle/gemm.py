@@ -44,14 +44,21 @@ def gemm_rows(offsets, sorted_pair_ids, topk: int, a_row: str, rows=None):
     return s, e, r
 
 
-def silu_mul(y: np.ndarray) -> np.ndarray:
+def silu_mul(y: np.ndarray, limit=None) -> np.ndarray:
     """SiLU-gated product over the two halves of y [n][2I]: columns [0, I) are
     the gate g, columns [I, 2I) the up projection u; h = g / (1 + exp(-g)) * u.
     (The SiLU(gate)*up between the two GEMMs of an NVFP4 / Mixtral-style MoE
-    layer; megamoe_rm.cu's fc1_rm computes the same product, with a clamp that
-    is not part of this definition.)"""
+    layer.)
+
+    limit: the clamped variant of megamoe_rm.cu's fc1_rm epilogue (the GLM
+    SwiGLU), applied to the already scaled GEMM outputs before the product:
+    the gate is bounded above only, g <- min(g, limit); the up projection is
+    bounded on both sides, u <- min(max(u, -limit), limit).  None: no clamp."""
     I = y.shape[1] // 2
     g, u = y[:, :I], y[:, I:]
+    if limit is not None:
+        g = np.minimum(g, limit)
+        u = np.clip(u, -limit, limit)
     return g / (1.0 + np.exp(-g)) * u
 
 
@@ -110,7 +117,7 @@ def grouped_gemm_qfp8_block(a, a_scale, a_row, w, w_scale, offsets, sorted_pair_
 
 
 def grouped_gemm_qnvfp4(x, a_row, w, w_sf, w_gscale, offsets, sorted_pair_ids, topk,
-                        act="none", rows=None):
+                        act="none", rows=None, limit=None):
     """NVFP4 W4A16 grouped GEMM (tilelang_kernels.py grouped_gemm_fp4, with the
     per-expert global scale of megamoe_rm.cu).
 
@@ -119,7 +126,8 @@ def grouped_gemm_qnvfp4(x, a_row, w, w_sf, w_gscale, offsets, sorted_pair_ids, t
       Wd[e, n, k] = e2m1(W[e, n, k]) * ue4m3(w_sf[e, n, k // 16])
       y[s, n]     = w_gscale[e] * sum_k x[r, k] * Wd[e, n, k]
     With w_gscale = 1 this is tilelang_kernels.py's dequantize-then-linear.
-    act 'silu_mul' returns silu_mul(y).  Returns dict(y=float64)."""
+    act 'silu_mul' returns silu_mul(y, limit) (megamoe_rm.cu applies the
+    global scale, then the clamp, then the product).  Returns dict(y=float64)."""
     s, e, r = gemm_rows(offsets, sorted_pair_ids, topk, a_row, rows)
     N = w.shape[1]
     X = bf16_value(np.asarray(x)[r])
@@ -130,5 +138,7 @@ def grouped_gemm_qnvfp4(x, a_row, w, w_sf, w_gscale, offsets, sorted_pair_ids, t
             ue4m3_value(np.asarray(w_sf)[ex]), 16, axis=1)
         y[m] = float(np.asarray(w_gscale)[ex]) * (X[m] @ Wd.T)
     if act == "silu_mul":
-        y = silu_mul(y)
+        y = silu_mul(y, limit)
+    elif limit is not None:
+        raise ValueError("limit applies to act 'silu_mul' only")
     return dict(y=y)

@@ -74,6 +74,41 @@ def test_silu_mul_matches_torch():
     assert oracle.silu_mul(np.array([[0.0, 3.0]]))[0, 0] == 0.0
 
 
+def test_silu_mul_limit_special_cases():
+    # the clamp of megamoe_rm.cu's fc1_rm epilogue (gate bounded above only,
+    # up bounded on both sides) pinned by limits where it reduces to known
+    # results and by the shape of the clamp
+    rng = np.random.default_rng(9)
+    y = rng.standard_normal((6, 16)) * 8
+    assert np.array_equal(oracle.silu_mul(y, np.inf), oracle.silu_mul(y))     # no clamp
+    assert np.all(oracle.silu_mul(y, 0.0) == 0)                                # u clamped to 0
+    big = np.abs(y).max() + 1
+    assert np.array_equal(oracle.silu_mul(y, big), oracle.silu_mul(y))         # nothing reaches it
+    L = 7.0
+    silu7 = float(torch.nn.functional.silu(torch.tensor(L, dtype=torch.float64)))
+    # gate above the limit: flat, equal to the value at the limit
+    h = oracle.silu_mul(np.array([[10.0, 1e6, L, 3.0, 3.0, 3.0]]), L)[0]
+    assert h[0] == h[1] == h[2] == silu7 * 3.0
+    # up beyond +-limit: flat at +-limit (a gate of 0.5 keeps silu small)
+    h = oracle.silu_mul(np.array([[L, L, L, 20.0, -20.0, 6.5]]), L)[0]
+    assert h[0] == silu7 * L and h[1] == -silu7 * L and h[2] == silu7 * 6.5
+    # gate far below -limit is NOT clamped: silu(-30) is ~ -2.8e-12, not silu(-7)
+    h = oracle.silu_mul(np.array([[-30.0, 1.0]]), L)[0]
+    ref = float(torch.nn.functional.silu(torch.tensor(-30.0, dtype=torch.float64)))
+    assert h[0] == ref and abs(h[0]) < 1e-10
+
+
+def test_nvfp4_limit_only_with_silu_mul():
+    d = synth.nvfp4_moe(14, T=4, E=2, k=1, H=32, I=16)
+    off, srt, inv, _ = oracle.route_prep(d["topk_ids"], 2)
+    with pytest.raises(ValueError):
+        oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], off, srt, 1, limit=1.0)
+    y = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], off, srt, 1)["y"]
+    h = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], off, srt, 1,
+                                   act="silu_mul", limit=0.05)["y"]
+    assert np.array_equal(h, oracle.silu_mul(y, 0.05))
+
+
 def test_int4_silu_mul_gate_first():
     d = synth.int4_moe(13, T=6, E=2, k=1, N=8, K=32)
     off, srt, inv, _ = oracle.route_prep(d["topk_ids"], 2)
