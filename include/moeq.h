@@ -68,8 +68,11 @@ typedef enum { MOEQ_F16 = 1, MOEQ_BF16 = 2, MOEQ_F32 = 3, MOEQ_I32 = 4 } moeq_dt
 
 /* MOEQ_ACT_SILU_MUL: the GEMM's N = 2I columns are [gate | up]
  * (columns [0, I) gate, [I, 2I) up); the call writes I columns
- * h = silu(gate) * up, silu(g) = g / (1 + exp(-g)). */
-typedef enum { MOEQ_ACT_NONE = 0, MOEQ_ACT_SILU_MUL = 1 } moeq_act;
+ * h = silu(gate) * up, silu(g) = g / (1 + exp(-g)).
+ * MOEQ_ACT_SILU_MUL_LIMIT (grouped_gemm_qnvfp4 only): the clamped form of
+ * [MMRM] fc1_rm's epilogue, applied to the scaled outputs before the
+ * product: gate = min(gate, limit), up = min(max(up, -limit), limit). */
+typedef enum { MOEQ_ACT_NONE = 0, MOEQ_ACT_SILU_MUL = 1, MOEQ_ACT_SILU_MUL_LIMIT = 2 } moeq_act;
 
 typedef enum { MOEQ_AROW_TOKEN = 0, MOEQ_AROW_SORTED = 1 } moeq_arow;
 
@@ -182,7 +185,10 @@ moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int6
  *                                     4g+j in bits 8j..8j+7 of word g) is
  *                                     the same bytes and may be passed as is
  *   w_gscale  f32   [E]               per-expert global scale
- *   out       [P][N] (NONE) or [P][N/2] (SILU_MUL), BF16 | F16 | F32
+ *   act       NONE, SILU_MUL, or SILU_MUL_LIMIT with act_limit (host f32,
+ *             > 0, +inf allowed; ignored for the other acts; a NaN, zero
+ *             or negative limit gives MOEQ_EINVAL)
+ *   out       [P][N] (NONE) or [P][N/2] (SILU_MUL*), BF16 | F16 | F32
  *   y[s][n] = w_gscale[e] * sum_k x[r][k] * e2m1(w[e][n][k])
  *                                  * ue4m3(w_sf[e][n][k/16])
  * Requires K % 128 == 0 and N % 128 == 0 (else MOEQ_EALIGN), 16-byte
@@ -194,7 +200,7 @@ moeq_status grouped_gemm_qnvfp4(const void* x, int64_t rows_a, moeq_arow a_row,
                                 const uint8_t* w, const uint8_t* w_sf, const float* w_gscale,
                                 const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
                                 int64_t P, int32_t topk, int32_t E, int64_t N, int64_t K,
-                                moeq_act act, moeq_dtype out_dtype, void* out,
+                                moeq_act act, float act_limit, moeq_dtype out_dtype, void* out,
                                 moeq_sched sched, void* stream);
 
 /* ------------------------------------------------------------------------

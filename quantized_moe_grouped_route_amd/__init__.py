@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libmoeq.so")
 OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP = 0, 1, 2, 3, 4
 F16, BF16, F32, I32 = 1, 2, 3, 4
 ACT = {"none": 0, "silu_mul": 1}
+ACT_SILU_MUL_LIMIT = 2
 AROW = {"token": 0, "sorted": 1}
 SCHED = {"auto": 0, "decode": 1, "prefill": 2}
 
@@ -62,7 +63,7 @@ def lib():
         "grouped_gemm_qfp8_block": (i32, [vp, vp, i64, i32, vp, vp, vp, vp, i64, i32, i32, i64,
                                           i64, i32, vp, i32, vp]),
         "grouped_gemm_qnvfp4": (i32, [vp, i64, i32, vp, vp, vp, vp, vp, i64, i32, i32, i64, i64,
-                                      i32, i32, vp, i32, vp]),
+                                      i32, C.c_float, i32, vp, i32, vp]),
         "moe_scatter_combine": (i32, [vp, i32, vp, vp, i64, i32, i64, i32, vp, vp]),
         "moe_quantize_int4": (i32, [vp, i32, i64, i64, vp, vp, vp]),
         "moe_nvfp4_repack": (i32, [vp, vp, i64, i64, i64, i32, vp, vp, vp]),
@@ -205,12 +206,13 @@ def grouped_gemm_qfp8_block(a, a_scale, w, w_scale, expert_offsets, sorted_pair_
 
 
 def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, topk: int, *,
-                        a_row="token", act="none", out_dtype=torch.bfloat16, out=None, P=None,
-                        sched="auto"):
+                        a_row="token", act="none", limit=None, out_dtype=torch.bfloat16, out=None,
+                        P=None, sched="auto"):
     """NVFP4 W4A16 grouped GEMM: x bf16 [rows_a][K], w uint8 [E][N][K/2]
     (E2M1), w_sf uint8 [E][N][K/16] (UE4M3) or int32 [E][N][K/64] (four
     UE4M3 per word, block 4g+j in bits 8j..8j+7: the same bytes), w_gscale
-    f32 [E].  Returns out [P][N] (act 'none') or [P][N/2] ('silu_mul')."""
+    f32 [E].  Returns out [P][N] (act 'none') or [P][N/2] ('silu_mul';
+    with `limit`, the clamped SwiGLU of megamoe_rm.cu's fc1_rm)."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w, "w", torch.uint8, 3)
     if isinstance(w_sf, torch.Tensor) and w_sf.dtype == torch.int32 and w_sf.dim() == 3:
@@ -223,11 +225,14 @@ def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, t
     K = 2 * Kh
     if En != E or x.shape[1] != K or tuple(w_sf.shape) != (E, N, K // 16) or w_gscale.numel() != E:
         raise ValueError("inconsistent NVFP4 operand shapes")
+    if limit is not None and act != "silu_mul":
+        raise ValueError("limit applies to act 'silu_mul' only")
+    act_code = ACT[act] if limit is None else ACT_SILU_MUL_LIMIT
     out = _out(out, P, N // 2 if act == "silu_mul" else N, out_dtype, x.device)
     st = lib().grouped_gemm_qnvfp4(_ptr(x), x.shape[0], arow, _ptr(w), _ptr(w_sf), _ptr(w_gscale),
                                    _ptr(expert_offsets), _ptr(sorted_pair_ids), P, topk, E, N, K,
-                                   ACT[act], _DTYPE_CODE[out_dtype], _ptr(out), SCHED[sched],
-                                   _stream())
+                                   act_code, 0.0 if limit is None else float(limit),
+                                   _DTYPE_CODE[out_dtype], _ptr(out), SCHED[sched], _stream())
     _check("grouped_gemm_qnvfp4", st)
     return out
 

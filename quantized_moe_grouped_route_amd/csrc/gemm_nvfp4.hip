@@ -25,6 +25,18 @@ namespace {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// SiLU-gated product of the scaled gate and up outputs.  A finite limit
+// applies the clamp of megamoe_rm.cu's fc1_rm epilogue first: the gate is
+// bounded above only, the up projection on both sides.  The limit is
+// uniform, so the branch costs no divergence.
+__device__ __forceinline__ float swiglu(float g, float u, float limit) {
+  if (limit < __builtin_inff()) {
+    g = fminf(g, limit);
+    u = fminf(fmaxf(u, -limit), limit);
+  }
+  return silu(g) * u;
+}
+
 // ------------------------------------------------------------------ prefill
 // CU work unit: a workgroup of 4 waves owns a 128 (activation rows) x 256
 // (weight rows; for SILU_MUL 128 gate rows + the 128 matching up rows)
@@ -59,7 +71,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale,
     const int* __restrict__ offsets, const int* __restrict__ sorted_ids, int topk, int E, int P, int N,
-    int K, void* __restrict__ out) {
+    int K, void* __restrict__ out, float limit) {
   using namespace pf;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
   __shared__ int tile_start[kMaxExperts + 1];
@@ -197,7 +209,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
         for (int r = 0; r < 4; ++r) {
           const int i = 4 * q + r;
           if (SILU) {
-            v[0][r] = silu(gs * acc[0][y][i]) * (gs * acc[1][y][i]);
+            v[0][r] = swiglu(gs * acc[0][y][i], gs * acc[1][y][i], limit);
             v[1][r] = 0.f;
           } else {
             v[0][r] = gs * acc[0][y][i];
@@ -346,7 +358,8 @@ template <int OUT, bool SILU, bool WIDE>
 __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale, const int* __restrict__ offsets,
-    const int* __restrict__ sorted_ids, int topk, int E, int P, int N, int K, void* __restrict__ out) {
+    const int* __restrict__ sorted_ids, int topk, int E, int P, int N, int K, void* __restrict__ out,
+    float limit) {
   constexpr int CPS = dc::cps<WIDE>();
   constexpr int D = dc::depth<WIDE>();
   constexpr int kSlot = dc::slot_bytes<WIDE>();
@@ -533,7 +546,7 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
         if (SILU) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            o[row * I + t.nt * 16 + 4 * g + i] = OutT<OUT>::from(silu(gs * acc0[i]) * (gs * acc1[i]));
+            o[row * I + t.nt * 16 + 4 * g + i] = OutT<OUT>::from(swiglu(gs * acc0[i], gs * acc1[i], limit));
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -560,18 +573,18 @@ hipError_t go(const GroupedArgs& g, bool decode, const uint16_t* x, const uint8_
     if (g.K % 512 == 0)
       hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, true>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
                          g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N,
-                         g.K, g.out);
+                         g.K, g.out, g.act_limit);
     else
       hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, false>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
                          g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N,
-                         g.K, g.out);
+                         g.K, g.out, g.act_limit);
   } else {
     const int64_t mt_ub = (g.P + pf::kM - 1) / pf::kM + std::min<int64_t>(g.E, g.P);
     const int64_t items_ub = mt_ub * (g.N / pf::kN);
     const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus * 2);
     hipLaunchKernelGGL((nvfp4_prefill<OUT, SILU>), dim3(grid), dim3(pf::kThreads), 0, stream, x,
                        g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P,
-                       g.N, g.K, g.out);
+                       g.N, g.K, g.out, g.act_limit);
   }
   return hipGetLastError();
 }

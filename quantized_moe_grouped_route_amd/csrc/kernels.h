@@ -34,6 +34,7 @@ struct GroupedArgs {
   int N;                    // GEMM columns (2I for SILU_MUL)
   int K;
   int silu_mul;             // 1: write I = N/2 columns silu(gate) * up
+  float act_limit;          // SwiGLU clamp (NVFP4 only); +inf: none
   int out_kind;             // OutKind
   void* out;
   int sched;                // 0 auto, 1 decode, 2 prefill

@@ -6,6 +6,7 @@
 // reported as status codes because the boundary is C.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -84,6 +85,7 @@ moeq::GroupedArgs make_args(const int32_t* offsets, const int32_t* sorted, int64
   g.N = (int)N;
   g.K = (int)K;
   g.silu_mul = silu ? 1 : 0;
+  g.act_limit = INFINITY;
   g.out_kind = (int)od;
   g.out = out;
   g.sched = (int)sched;
@@ -97,7 +99,7 @@ extern "C" {
 
 const char* moeq_last_error(void) { return g_err.c_str(); }
 
-int32_t moeq_abi_version(void) { return 1; }
+int32_t moeq_abi_version(void) { return 2; }
 
 size_t moe_route_prep_workspace_bytes(int64_t T, int32_t topk, int32_t E) {
   if (T < 0 || topk < 1 || E < 1) return 0;
@@ -176,21 +178,25 @@ moeq_status grouped_gemm_qnvfp4(const void* x, int64_t rows_a, moeq_arow a_row, 
                                 const uint8_t* w_sf, const float* w_gscale,
                                 const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
                                 int64_t P, int32_t topk, int32_t E, int64_t N, int64_t K,
-                                moeq_act act, moeq_dtype out_dtype, void* out,
+                                moeq_act act, float act_limit, moeq_dtype out_dtype, void* out,
                                 moeq_sched sched, void* stream) {
   const char* fn = "grouped_gemm_qnvfp4";
   moeq_status st = check_grouped(fn, x, rows_a, a_row, w, expert_offsets, P, topk, E, N, K, out);
   if (st != MOEQ_OK) return st;
   if (!w_sf || !w_gscale) return fail(MOEQ_EINVAL, "%s: null scale pointer", fn);
   if (!aligned(w_sf, 16) || !aligned(w_gscale, 4)) return fail(MOEQ_EALIGN, "%s: scales misaligned", fn);
-  if (act != MOEQ_ACT_NONE && act != MOEQ_ACT_SILU_MUL) return fail(MOEQ_EUNSUPPORTED, "%s: act %d", fn, act);
+  if (act != MOEQ_ACT_NONE && act != MOEQ_ACT_SILU_MUL && act != MOEQ_ACT_SILU_MUL_LIMIT)
+    return fail(MOEQ_EUNSUPPORTED, "%s: act %d", fn, act);
+  if (act == MOEQ_ACT_SILU_MUL_LIMIT && !(act_limit > 0.0f))
+    return fail(MOEQ_EINVAL, "%s: act_limit %g must be > 0", fn, (double)act_limit);
   if (out_dtype != MOEQ_F16 && out_dtype != MOEQ_BF16 && out_dtype != MOEQ_F32)
     return fail(MOEQ_EUNSUPPORTED, "%s: out dtype %d", fn, out_dtype);
   if (a_row == MOEQ_AROW_TOKEN && !sorted_pair_ids && rows_a < P)
     return fail(MOEQ_EINVAL, "%s: identity rows need rows_a >= P", fn);
   if (sched < MOEQ_SCHED_AUTO || sched > MOEQ_SCHED_PREFILL) return fail(MOEQ_EINVAL, "%s: sched %d", fn, sched);
   moeq::GroupedArgs g = make_args(expert_offsets, sorted_pair_ids, rows_a, a_row, P, topk, E, N, K,
-                                  act == MOEQ_ACT_SILU_MUL, out_dtype, out, sched);
+                                  act != MOEQ_ACT_NONE, out_dtype, out, sched);
+  if (act == MOEQ_ACT_SILU_MUL_LIMIT) g.act_limit = act_limit;
   return hip_status(moeq::launch_gemm_nvfp4(g, static_cast<const uint16_t*>(x), w, w_sf, w_gscale,
                                             (hipStream_t)stream),
                     fn);

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(L):
     raw = C.CDLL(mq.LIB_PATH)
     for f in declared_functions():
         assert hasattr(raw, f), f
-    assert L.moeq_abi_version() == 1
+    assert L.moeq_abi_version() == 2
 
 
 def test_workspace_bytes(L):
@@ -83,7 +83,7 @@ def _int4(L, **kw):
     (dict(E=2000), mq.EINVAL), (dict(topk=0), mq.EINVAL), (dict(P=-1), mq.EINVAL),
     (dict(a=None), mq.EINVAL), (dict(w=ODD), mq.EALIGN), (dict(out=ODD), mq.EALIGN),
     (dict(sa=None), mq.EINVAL), (dict(act=7), mq.EUNSUPPORTED), (dict(od=9), mq.EUNSUPPORTED),
-    (dict(od=mq.I32, act=1), mq.EUNSUPPORTED), (dict(arow=5), mq.EINVAL),
+    (dict(od=mq.I32, act=1), mq.EUNSUPPORTED), (dict(arow=5), mq.EINVAL), (dict(act=2), mq.EUNSUPPORTED),
     (dict(srt=None, rows=8, P=16), mq.EINVAL), (dict(sched=9), mq.EINVAL),
     (dict(rows=0), mq.EINVAL), (dict(K=1 << 18), mq.EINVAL),
 ])
@@ -110,17 +110,19 @@ def test_fp8_rejects(L, kw, status):
 
 def _nvfp4(L, **kw):
     a = dict(x=A16, rows=16, arow=0, w=A16, sf=A16, gs=A16, off=A16, srt=A16, P=16, topk=2, E=4,
-             N=256, K=256, act=0, od=mq.BF16, out=A16, sched=0)
+             N=256, K=256, act=0, lim=0.0, od=mq.BF16, out=A16, sched=0)
     a.update(kw)
     return L.grouped_gemm_qnvfp4(a["x"], a["rows"], a["arow"], a["w"], a["sf"], a["gs"], a["off"],
                                  a["srt"], a["P"], a["topk"], a["E"], a["N"], a["K"], a["act"],
-                                 a["od"], a["out"], a["sched"], None)
+                                 a["lim"], a["od"], a["out"], a["sched"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(K=96), mq.EALIGN), (dict(N=32), mq.EALIGN), (dict(sf=ODD), mq.EALIGN),
     (dict(gs=None), mq.EINVAL), (dict(od=mq.I32), mq.EUNSUPPORTED), (dict(act=3), mq.EUNSUPPORTED),
-    (dict(x=None), mq.EINVAL),
+    (dict(x=None), mq.EINVAL), (dict(act=2, lim=0.0, K=96), mq.EALIGN),
+    (dict(act=2, lim=0.0), mq.EINVAL), (dict(act=2, lim=-1.0), mq.EINVAL),
+    (dict(act=2, lim=float("nan")), mq.EINVAL),
 ])
 def test_nvfp4_rejects(L, kw, status):
     assert _nvfp4(L, **kw) == status

@@ -445,3 +445,26 @@ def test_nvfp4_u32_packed_scales_are_the_same_bytes():
     ref = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], host(offs), host(srt), k,
                                      act="silu_mul")["y"]
     assert_rows_close(host(y)[: ref.shape[0]], ref, what="nvfp4 u32-packed scales")
+
+
+@pytest.mark.parametrize("sched", ["prefill", "decode"])
+def test_nvfp4_silu_mul_limit(sched):
+    # megamoe_rm.cu's clamped SwiGLU: a limit of 0.15 clamps about a quarter
+    # of the gates and half of the up values of this input
+    T, E, k, H, I = 150, 5, 2, 256, 128
+    lim = float(np.float32(0.15))
+    d = synth.nvfp4_moe(41, T, E, k, H, I, routing="repeat")
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    args = (dev(d["x"]), dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k)
+    h = mq.grouped_gemm_qnvfp4(*args, act="silu_mul", limit=lim, out_dtype=torch.float32, sched=sched)
+    ref = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], host(offs), host(srt), k,
+                                     act="silu_mul", limit=lim)["y"]
+    assert_rows_close(host(h)[: ref.shape[0]], ref, what=f"nvfp4 limit {sched}")
+    plain = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], host(offs), host(srt), k,
+                                       act="silu_mul")["y"]
+    assert np.abs(plain - ref).max() > 0.05 * np.abs(plain).max()     # the clamp is active
+    # an infinite limit is the plain product, bit for bit
+    h_inf = mq.grouped_gemm_qnvfp4(*args, act="silu_mul", limit=float("inf"), out_dtype=torch.float32,
+                                   sched=sched)
+    h_plain = mq.grouped_gemm_qnvfp4(*args, act="silu_mul", out_dtype=torch.float32, sched=sched)
+    assert torch.equal(h_inf, h_plain)
