@@ -107,3 +107,33 @@ def test_route_worked_example():
     assert inv.tolist() == [2, 0, 1, 3, -1, 4]
     assert bad == 0
     assert oracle.route_prep(np.array([[7, -2]], np.int32), 3)[3] == 2
+
+
+def test_pair_rows_and_sum_pairs_worked_example():
+    # T=2, k=2, E=2; token 1 slot 0 has no expert.  Sorted order: expert 0
+    # holds pair 1, expert 1 holds pairs 0 and 3 (ascending pair id).
+    ids = np.array([[1, 0], [-1, 1]], np.int32)
+    off, srt, p2s, _ = oracle.route_prep(ids, 2)
+    assert list(srt[:3]) == [1, 0, 3]
+    y = np.array([[1.0, 2.0], [3.0, 4.0], [5.0, 6.0]])
+    w = np.array([[0.5, 0.25], [0.9, 2.0]], np.float32)
+    ypart, valid = oracle.pair_rows(y, srt, w)
+    assert list(valid) == [True, True, False, True]
+    assert np.array_equal(ypart, [[1.5, 2.0], [0.25, 0.5], [0.0, 0.0], [10.0, 12.0]])
+    out = oracle.sum_pairs(ypart, p2s, 2, 2)
+    assert np.array_equal(out, [[1.75, 2.5], [10.0, 12.0]])
+
+
+def test_pair_path_equals_scatter_combine():
+    # weighting in the FC2 epilogue then summing pair rows is the same sum,
+    # in the same slot order, as the weighted scatter-combine
+    rng = np.random.default_rng(3)
+    T, k, E, N = 37, 4, 6, 24
+    ids = synth.uniform_ids_with_repeats(rng, T, k, E)
+    ids[rng.random((T, k)) < 0.1] = -1
+    off, srt, p2s, _ = oracle.route_prep(ids, E)
+    y = rng.standard_normal((int(off[-1]), N))
+    w = synth.softmax_weights(rng, T, k)
+    ypart, valid = oracle.pair_rows(y, srt, w)
+    assert np.array_equal(valid, p2s >= 0)
+    assert np.array_equal(oracle.sum_pairs(ypart, p2s, T, k), oracle.scatter_combine(y, p2s, w))
