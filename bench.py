@@ -81,11 +81,11 @@ def _traffic(kernel_tag, sources):
 class Workload:
     """Device buffers and the launch sequence of one step."""
 
-    def __init__(self, idx: int):
+    def __init__(self, idx: int, fc2: str = "sorted"):
         import torch
         import synth
         import quantized_moe_grouped_route_amd as mq
-        self.mq, self.idx = mq, idx
+        self.mq, self.idx, self.fc2 = mq, idx, fc2
         self.cfg = synth.WORKLOADS[idx]
         self.d = d = synth.workload(idx)
         if self.cfg["kind"] == "repack":
@@ -148,6 +148,7 @@ class Workload:
             self.w2, self.s2, self.g2 = _dev(d["w2"]), _dev(d["s2"]), _dev(d["g2"])
             self.h = torch.empty(P, I, dtype=torch.bfloat16, device="cuda")
             self.y = torch.empty(P, H, dtype=torch.bfloat16, device="cuda")
+            self.tw_flat = self.tw.reshape(-1)
             self.out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
             ids = d["topk_ids"].reshape(-1)
             valid = ids[(ids >= 0) & (ids < E)]
@@ -225,9 +226,15 @@ class Workload:
             mq.grouped_gemm_qnvfp4(self.x, self.w1, self.s1, self.g1, offs, srt, self.k, act="silu_mul",
                                    out=self.h)
             if ev: ev[1].record()
-            mq.grouped_gemm_qnvfp4(self.h, self.w2, self.s2, self.g2, offs, srt, self.k,
-                                   a_row="sorted", out=self.y)
-            mq.moe_scatter_combine(self.y, p2s, self.tw, out=self.out)
+            if self.fc2 == "pair":
+                # top-k weight in FC2's epilogue, rows in pair order, then the pair sum
+                mq.grouped_gemm_qnvfp4(self.h, self.w2, self.s2, self.g2, offs, srt, self.k,
+                                       a_row="sorted", pair_weights=self.tw_flat, out=self.y)
+                mq.moe_sum_pairs(self.y, p2s, self.T, self.k, out=self.out)
+            else:
+                mq.grouped_gemm_qnvfp4(self.h, self.w2, self.s2, self.g2, offs, srt, self.k,
+                                       a_row="sorted", out=self.y)
+                mq.moe_scatter_combine(self.y, p2s, self.tw, out=self.out)
 
     def dominant_launches(self):
         """(launches of the dominant kernel per step, index of the timed one)."""
@@ -510,6 +517,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=1, choices=sorted(__import__("synth").WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fc2", choices=("sorted", "pair"), default="sorted",
+                    help="NVFP4 workloads: FC2 writes sorted rows and the combine applies the top-k "
+                         "weights (sorted), or FC2's epilogue applies them and writes pair-ordered "
+                         "rows that a pair sum adds (pair)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device 5 times (a kernel of known traffic "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -542,7 +553,7 @@ def main():
         print(json.dumps({"copy_bytes_read_per_launch": src.numel() * 4,
                           "copy_bytes_written_per_launch": dst.numel() * 4}), flush=True)
         return
-    wl = Workload(args.workload)
+    wl = Workload(args.workload, args.fc2)
     torch.cuda.synchronize()
     host_s = []
     for _ in range(args.warmup):
@@ -594,6 +605,8 @@ def main():
             "kernel": tag, "kernel_ms": round(dom_ms, 5)}
     config = {"workload": cfg["name"]}
     config.update({k: v for k, v in cfg.items() if k not in ("name", "kind")})
+    if cfg["kind"] == "nvfp4":
+        config["fc2_epilogue"] = args.fc2
     if args.workload in (2, 6):
         config["active_experts"] = wl.active
         config["weight_bytes"] = wl.weight_bytes

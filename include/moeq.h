@@ -8,6 +8,8 @@
  *   grouped_gemm_qfp8_block FP8 e4m3 GEMM, 1x128 A / 128x128 B block scales
  *   grouped_gemm_qnvfp4     NVFP4 (E2M1 + UE4M3 per-16 + global) x bf16 GEMM
  *   moe_scatter_combine     top-k weighted sum back to token rows
+ *   (or: grouped_gemm_qnvfp4 with pair_weights + moe_sum_pairs, the top-k
+ *   weight applied in FC2's epilogue)
  * with two helpers around it:
  *   moe_quantize_int4       per-row INT4 activation quantization
  *   moe_nvfp4_repack        one-shot NVFP4 weight layout conversion
@@ -188,6 +190,14 @@ moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int6
  *   act       NONE, SILU_MUL, or SILU_MUL_LIMIT with act_limit (host f32,
  *             > 0, +inf allowed; ignored for the other acts; a NaN, zero
  *             or negative limit gives MOEQ_EINVAL)
+ *   pair_weights  NULL, or f32 [P] indexed by pair id (topk_weights
+ *             flattened): [MMRM] fc2_rm's epilogue.  Sorted row s is then
+ *             multiplied by pair_weights[p], p = sorted_pair_ids[s], and
+ *             written to out row p (pair order) instead of row s; rows of
+ *             pairs without an expert are not written.  Needs act NONE
+ *             (else MOEQ_EUNSUPPORTED) and sorted_pair_ids (else
+ *             MOEQ_EINVAL); every pair id must be < P, as moe_route_prep's
+ *             are.  moe_sum_pairs then sums each token's rows.
  *   out       [P][N] (NONE) or [P][N/2] (SILU_MUL*), BF16 | F16 | F32
  *   y[s][n] = w_gscale[e] * sum_k x[r][k] * e2m1(w[e][n][k])
  *                                  * ue4m3(w_sf[e][n][k/16])
@@ -200,8 +210,8 @@ moeq_status grouped_gemm_qnvfp4(const void* x, int64_t rows_a, moeq_arow a_row,
                                 const uint8_t* w, const uint8_t* w_sf, const float* w_gscale,
                                 const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
                                 int64_t P, int32_t topk, int32_t E, int64_t N, int64_t K,
-                                moeq_act act, float act_limit, moeq_dtype out_dtype, void* out,
-                                moeq_sched sched, void* stream);
+                                moeq_act act, float act_limit, const float* pair_weights,
+                                moeq_dtype out_dtype, void* out, moeq_sched sched, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_quantize_int4 - per-row symmetric INT4 quantization of activations.
@@ -242,6 +252,24 @@ moeq_status moe_quantize_int4(const void* x, moeq_dtype x_dtype, int64_t rows, i
 moeq_status moe_scatter_combine(const void* y, moeq_dtype y_dtype, const int32_t* pair_to_sorted,
                                 const float* topk_weights, int64_t T, int32_t topk, int64_t N,
                                 moeq_dtype out_dtype, void* out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_sum_pairs - per-token sum of pre-weighted rows in pair order.
+ * [MMRM] combine: the rows fc2_rm's epilogue wrote (grouped_gemm_qnvfp4
+ * with pair_weights) summed over a token's pairs that have an expert, in
+ * slot order, in fp32, rounded once.
+ *
+ *   y_pairs        [T*topk][N] y_dtype (F16 | BF16 | F32), row t*topk + j
+ *   pair_to_sorted int32 [T*topk] from moe_route_prep (< 0: no expert, the
+ *                  row is skipped and need not hold a value)
+ *   out            [T][N] out_dtype (F16 | BF16 | F32)
+ *   out[t][:] = sum_{j < topk, pair_to_sorted[t*topk+j] >= 0}
+ *                 y_pairs[t*topk+j][:]
+ * A token with no routed pair gets a zero row.  Requires N % 8 == 0,
+ * 16-byte aligned y_pairs and out, 1 <= topk <= 64.
+ * ---------------------------------------------------------------------- */
+moeq_status moe_sum_pairs(const void* y_pairs, moeq_dtype y_dtype, const int32_t* pair_to_sorted, int64_t T,
+                          int32_t topk, int64_t N, moeq_dtype out_dtype, void* out, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_nvfp4_repack - convert NVFP4 expert weights from the layout [MMRM]

@@ -32,7 +32,7 @@ _DTYPE_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32, tor
 EXPORTS = ("moeq_last_error", "moeq_abi_version", "moe_route_prep_workspace_bytes",
            "moe_route_prep", "grouped_gemm_qint4", "grouped_gemm_qfp8_block",
            "grouped_gemm_qnvfp4", "moe_scatter_combine", "moe_quantize_int4",
-           "moe_nvfp4_repack")
+           "moe_nvfp4_repack", "moe_sum_pairs")
 
 
 class MoeqError(RuntimeError):
@@ -63,10 +63,11 @@ def lib():
         "grouped_gemm_qfp8_block": (i32, [vp, vp, i64, i32, vp, vp, vp, vp, i64, i32, i32, i64,
                                           i64, i32, vp, i32, vp]),
         "grouped_gemm_qnvfp4": (i32, [vp, i64, i32, vp, vp, vp, vp, vp, i64, i32, i32, i64, i64,
-                                      i32, C.c_float, i32, vp, i32, vp]),
+                                      i32, C.c_float, vp, i32, vp, i32, vp]),
         "moe_scatter_combine": (i32, [vp, i32, vp, vp, i64, i32, i64, i32, vp, vp]),
         "moe_quantize_int4": (i32, [vp, i32, i64, i64, vp, vp, vp]),
         "moe_nvfp4_repack": (i32, [vp, vp, i64, i64, i64, i32, vp, vp, vp]),
+        "moe_sum_pairs": (i32, [vp, i32, vp, i64, i32, i64, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -206,13 +207,15 @@ def grouped_gemm_qfp8_block(a, a_scale, w, w_scale, expert_offsets, sorted_pair_
 
 
 def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, topk: int, *,
-                        a_row="token", act="none", limit=None, out_dtype=torch.bfloat16, out=None,
-                        P=None, sched="auto"):
+                        a_row="token", act="none", limit=None, pair_weights=None,
+                        out_dtype=torch.bfloat16, out=None, P=None, sched="auto"):
     """NVFP4 W4A16 grouped GEMM: x bf16 [rows_a][K], w uint8 [E][N][K/2]
     (E2M1), w_sf uint8 [E][N][K/16] (UE4M3) or int32 [E][N][K/64] (four
     UE4M3 per word, block 4g+j in bits 8j..8j+7: the same bytes), w_gscale
     f32 [E].  Returns out [P][N] (act 'none') or [P][N/2] ('silu_mul';
-    with `limit`, the clamped SwiGLU of megamoe_rm.cu's fc1_rm)."""
+    with `limit`, the clamped SwiGLU of megamoe_rm.cu's fc1_rm).
+    pair_weights (f32, T*topk values, e.g. topk_weights): megamoe_rm.cu's
+    fc2_rm epilogue, out row p = w[p] * y of pair p, in pair order."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w, "w", torch.uint8, 3)
     if isinstance(w_sf, torch.Tensor) and w_sf.dtype == torch.int32 and w_sf.dim() == 3:
@@ -228,10 +231,14 @@ def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, t
     if limit is not None and act != "silu_mul":
         raise ValueError("limit applies to act 'silu_mul' only")
     act_code = ACT[act] if limit is None else ACT_SILU_MUL_LIMIT
+    if pair_weights is not None:
+        _need(pair_weights, "pair_weights", torch.float32)
+        if sorted_pair_ids is None or pair_weights.numel() != sorted_pair_ids.numel():
+            raise ValueError("pair_weights needs sorted_pair_ids and one weight per pair")
     out = _out(out, P, N // 2 if act == "silu_mul" else N, out_dtype, x.device)
     st = lib().grouped_gemm_qnvfp4(_ptr(x), x.shape[0], arow, _ptr(w), _ptr(w_sf), _ptr(w_gscale),
                                    _ptr(expert_offsets), _ptr(sorted_pair_ids), P, topk, E, N, K,
-                                   act_code, 0.0 if limit is None else float(limit),
+                                   act_code, 0.0 if limit is None else float(limit), _ptr(pair_weights),
                                    _DTYPE_CODE[out_dtype], _ptr(out), SCHED[sched], _stream())
     _check("grouped_gemm_qnvfp4", st)
     return out
@@ -257,6 +264,25 @@ def moe_scatter_combine(y, pair_to_sorted, topk_weights, *, out_dtype=None, out=
                                    _ptr(topk_weights), T, k, N, _DTYPE_CODE[out_dtype], _ptr(out),
                                    _stream())
     _check("moe_scatter_combine", st)
+    return out
+
+
+def moe_sum_pairs(y_pairs, pair_to_sorted, T: int, topk: int, *, out_dtype=None, out=None):
+    """out[t] = sum_j y_pairs[t*topk + j] over the slots of token t that have
+    an expert (pair_to_sorted >= 0), fp32 in slot order, one rounding: the
+    combine that follows grouped_gemm_qnvfp4(..., pair_weights=...)."""
+    _need(y_pairs, "y_pairs", (torch.float16, torch.bfloat16, torch.float32), 2)
+    _need(pair_to_sorted, "pair_to_sorted", torch.int32, 1)
+    N = y_pairs.shape[1]
+    if pair_to_sorted.numel() != T * topk or y_pairs.shape[0] < T * topk:
+        raise ValueError("pair_to_sorted needs T*topk entries and y_pairs T*topk rows")
+    out_dtype = out_dtype or y_pairs.dtype
+    if out is None:
+        out = torch.empty(T, N, dtype=out_dtype, device=y_pairs.device)
+    _need(out, "out", out_dtype, 2)
+    st = lib().moe_sum_pairs(_ptr(y_pairs), _DTYPE_CODE[y_pairs.dtype], _ptr(pair_to_sorted), T, topk, N,
+                             _DTYPE_CODE[out_dtype], _ptr(out), _stream())
+    _check("moe_sum_pairs", st)
     return out
 
 

@@ -1,6 +1,8 @@
 // Top-k weighted scatter back to token rows (megamoe_rm.cu's combine: a
 // token's pairs that have an expert, summed in slot order in fp32 and
 // rounded once; tilelang_kernels.py: zero output plus weighted rows).
+// PAIRS: the rows are already weighted and in pair order (the output of
+// fc2_rm's epilogue), so token t's rows are t*topk .. t*topk+topk-1.
 //
 // One thread owns 8 consecutive columns of one token row: it reads the
 // pair table entries of its token, then 8 elements (16 or 32 bytes) of each
@@ -51,7 +53,7 @@ __device__ __forceinline__ void store8(void* out, int64_t off, const float v[8])
   }
 }
 
-template <int YK, int OK>
+template <int YK, int OK, bool PAIRS>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restrict__ y,
                                                            const int* __restrict__ p2s,
                                                            const float* __restrict__ tw, int T,
@@ -63,36 +65,52 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
   if (c >= N) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < topk; ++j) {
-    const int s = p2s[(int64_t)t * topk + j];
+    const int64_t p = (int64_t)t * topk + j;
+    const int s = p2s[p];
     if (s < 0 || s >= P) continue;
-    const float w = tw[(int64_t)t * topk + j];
     float v[8];
-    load8<YK>(y, (int64_t)s * N + c, v);
+    load8<YK>(y, (PAIRS ? p : (int64_t)s) * N + c, v);
+    if (PAIRS) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(w, v[q], acc[q]);
+      for (int q = 0; q < 8; ++q) acc[q] += v[q];
+    } else {
+      const float w = tw[p];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(w, v[q], acc[q]);
+    }
   }
   store8<OK>(out, (int64_t)t * N + c, acc);
 }
 
-template <int YK>
+template <int YK, bool PAIRS>
 hipError_t launch_y(const void* y, const int* p2s, const float* tw, int T, int topk, int N,
                     int64_t P, int out_kind, void* out, hipStream_t stream) {
   const dim3 grid(((N / 8 + kThreads - 1) / kThreads) * T);
   switch (out_kind) {
     case OUT_F16:
-      hipLaunchKernelGGL((combine_kernel<YK, OUT_F16>), grid, dim3(kThreads), 0, stream, y, p2s, tw,
+      hipLaunchKernelGGL((combine_kernel<YK, OUT_F16, PAIRS>), grid, dim3(kThreads), 0, stream, y, p2s, tw,
                          T, topk, N, P, out);
       break;
     case OUT_BF16:
-      hipLaunchKernelGGL((combine_kernel<YK, OUT_BF16>), grid, dim3(kThreads), 0, stream, y, p2s,
+      hipLaunchKernelGGL((combine_kernel<YK, OUT_BF16, PAIRS>), grid, dim3(kThreads), 0, stream, y, p2s,
                          tw, T, topk, N, P, out);
       break;
     default:
-      hipLaunchKernelGGL((combine_kernel<YK, OUT_F32>), grid, dim3(kThreads), 0, stream, y, p2s, tw,
+      hipLaunchKernelGGL((combine_kernel<YK, OUT_F32, PAIRS>), grid, dim3(kThreads), 0, stream, y, p2s, tw,
                          T, topk, N, P, out);
       break;
   }
   return hipGetLastError();
+}
+
+template <bool PAIRS>
+hipError_t launch_kind(const void* y, int y_kind, const int* p2s, const float* tw, int T, int topk, int N,
+                       int64_t P, int out_kind, void* out, hipStream_t stream) {
+  switch (y_kind) {
+    case OUT_F16: return launch_y<OUT_F16, PAIRS>(y, p2s, tw, T, topk, N, P, out_kind, out, stream);
+    case OUT_BF16: return launch_y<OUT_BF16, PAIRS>(y, p2s, tw, T, topk, N, P, out_kind, out, stream);
+    default: return launch_y<OUT_F32, PAIRS>(y, p2s, tw, T, topk, N, P, out_kind, out, stream);
+  }
 }
 
 }  // namespace
@@ -101,11 +119,8 @@ hipError_t launch_combine(const void* y, int y_kind, const int* p2s, const float
                           int topk, int N, int64_t P, int out_kind, void* out,
                           hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  switch (y_kind) {
-    case OUT_F16: return launch_y<OUT_F16>(y, p2s, tw, T, topk, N, P, out_kind, out, stream);
-    case OUT_BF16: return launch_y<OUT_BF16>(y, p2s, tw, T, topk, N, P, out_kind, out, stream);
-    default: return launch_y<OUT_F32>(y, p2s, tw, T, topk, N, P, out_kind, out, stream);
-  }
+  if (tw == nullptr) return launch_kind<true>(y, y_kind, p2s, tw, T, topk, N, P, out_kind, out, stream);
+  return launch_kind<false>(y, y_kind, p2s, tw, T, topk, N, P, out_kind, out, stream);
 }
 
 }  // namespace moeq

@@ -66,12 +66,16 @@ constexpr int kStageBytes = kABytes + kBBytes + kSBytes;
 constexpr int kThreads = 256;
 }  // namespace pf
 
-template <int OUT, bool SILU>
+// PAIR (act NONE only): megamoe_rm.cu's fc2_rm epilogue.  Sorted row s is
+// scaled by the top-k weight of its pair p = sorted_ids[s] and written to
+// output row p instead of s.
+template <int OUT, bool SILU, bool PAIR>
 __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale,
     const int* __restrict__ offsets, const int* __restrict__ sorted_ids, int topk, int E, int P, int N,
-    int K, void* __restrict__ out, float limit) {
+    int K, void* __restrict__ out, float limit, const float* __restrict__ pair_w) {
+  static_assert(!(SILU && PAIR), "pair-ordered output is for act NONE");
   using namespace pf;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
   __shared__ int tile_start[kMaxExperts + 1];
@@ -202,6 +206,8 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
 #pragma unroll
     for (int y = 0; y < 4; ++y) {
       uint8_t* orow = otile + (32 * y + l32) * kOutPitch;
+      float gy = gs;
+      if (PAIR) gy *= pair_w[sorted_ids[t.row0 + min(32 * y + l32, t.rows - 1)]];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float v[2][4];
@@ -212,8 +218,8 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
             v[0][r] = swiglu(gs * acc[0][y][i], gs * acc[1][y][i], limit);
             v[1][r] = 0.f;
           } else {
-            v[0][r] = gs * acc[0][y][i];
-            v[1][r] = gs * acc[1][y][i];
+            v[0][r] = gy * acc[0][y][i];
+            v[1][r] = gy * acc[1][y][i];
           }
         }
         // weight columns 8q + 4*slice + r of the lane's 32-row operand(s)
@@ -222,10 +228,11 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
         for (int a2 = 0; a2 < (SILU ? 1 : 2); ++a2) {
           if constexpr (!kStaged) {
             const int rr = 32 * y + l32;
-            if (rr < t.rows)
-              *reinterpret_cast<float4*>(static_cast<float*>(out) + (int64_t)(t.row0 + rr) * ldo +
-                                         (int64_t)t.nt * kCols + col0 + 32 * a2) =
-                  make_float4(v[a2][0], v[a2][1], v[a2][2], v[a2][3]);
+            if (rr < t.rows) {
+              const int64_t orow_i = PAIR ? (int64_t)sorted_ids[t.row0 + rr] : (int64_t)(t.row0 + rr);
+              *reinterpret_cast<float4*>(static_cast<float*>(out) + orow_i * ldo + (int64_t)t.nt * kCols + col0 +
+                                         32 * a2) = make_float4(v[a2][0], v[a2][1], v[a2][2], v[a2][3]);
+            }
             continue;
           }
           uint8_t* dst = orow + (col0 + 32 * a2) * (int)sizeof(T);
@@ -242,13 +249,15 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
     raw_barrier();
     if constexpr (kStaged) {
       constexpr int kChunksPerRow = kCols * (int)sizeof(T) / 16;
-      uint8_t* obase = static_cast<uint8_t*>(out) + ((int64_t)t.row0 * ldo + (int64_t)t.nt * kCols) * (int)sizeof(T);
+      uint8_t* obase = static_cast<uint8_t*>(out) + (int64_t)t.nt * kCols * (int)sizeof(T);
 #pragma unroll 4
       for (int i = 0; i < kM * kChunksPerRow / kThreads; ++i) {
         const int ci = tid + kThreads * i;
         const int r = ci / kChunksPerRow, c = ci % kChunksPerRow;
-        if (r < t.rows)
-          st16(obase + (int64_t)r * ldo * (int)sizeof(T) + c * 16, ld16(otile + r * kOutPitch + c * 16));
+        if (r < t.rows) {
+          const int64_t orow_i = PAIR ? (int64_t)sorted_ids[t.row0 + r] : (int64_t)(t.row0 + r);
+          st16(obase + orow_i * ldo * (int)sizeof(T) + c * 16, ld16(otile + r * kOutPitch + c * 16));
+        }
       }
     }
   }
@@ -354,12 +363,13 @@ __device__ __forceinline__ void wait_vm(int n) {
   asm volatile("" ::: "memory");
 }
 
-template <int OUT, bool SILU, bool WIDE>
+template <int OUT, bool SILU, bool WIDE, bool PAIR>
 __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale, const int* __restrict__ offsets,
     const int* __restrict__ sorted_ids, int topk, int E, int P, int N, int K, void* __restrict__ out,
-    float limit) {
+    float limit, const float* __restrict__ pair_w) {
+  static_assert(!(SILU && PAIR), "pair-ordered output is for act NONE");
   constexpr int CPS = dc::cps<WIDE>();
   constexpr int D = dc::depth<WIDE>();
   constexpr int kSlot = dc::slot_bytes<WIDE>();
@@ -548,10 +558,16 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
           for (int i = 0; i < 4; ++i)
             o[row * I + t.nt * 16 + 4 * g + i] = OutT<OUT>::from(swiglu(gs * acc0[i], gs * acc1[i], limit));
         } else {
+          float gy = gs;
+          int64_t orow_i = row;
+          if (PAIR) {
+            orow_i = sorted_ids[row];
+            gy *= pair_w[orow_i];
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            o[row * N + t.nt * 32 + 4 * g + i] = OutT<OUT>::from(gs * acc0[i]);
-            o[row * N + t.nt * 32 + 16 + 4 * g + i] = OutT<OUT>::from(gs * acc1[i]);
+            o[orow_i * N + t.nt * 32 + 4 * g + i] = OutT<OUT>::from(gy * acc0[i]);
+            o[orow_i * N + t.nt * 32 + 16 + 4 * g + i] = OutT<OUT>::from(gy * acc1[i]);
           }
         }
       }
@@ -563,7 +579,7 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
   }
 }
 
-template <int OUT, bool SILU>
+template <int OUT, bool SILU, bool PAIR>
 hipError_t go(const GroupedArgs& g, bool decode, const uint16_t* x, const uint8_t* w,
               const uint8_t* sf, const float* gsc, hipStream_t stream) {
   if (decode) {
@@ -571,20 +587,20 @@ hipError_t go(const GroupedArgs& g, bool decode, const uint16_t* x, const uint8_
     // items over the waves itself
     const int grid = g.num_cus * 2;
     if (g.K % 512 == 0)
-      hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, true>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
+      hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, true, PAIR>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
                          g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N,
-                         g.K, g.out, g.act_limit);
+                         g.K, g.out, g.act_limit, g.pair_weights);
     else
-      hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, false>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
+      hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, false, PAIR>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
                          g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N,
-                         g.K, g.out, g.act_limit);
+                         g.K, g.out, g.act_limit, g.pair_weights);
   } else {
     const int64_t mt_ub = (g.P + pf::kM - 1) / pf::kM + std::min<int64_t>(g.E, g.P);
     const int64_t items_ub = mt_ub * (g.N / pf::kN);
     const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus * 2);
-    hipLaunchKernelGGL((nvfp4_prefill<OUT, SILU>), dim3(grid), dim3(pf::kThreads), 0, stream, x,
+    hipLaunchKernelGGL((nvfp4_prefill<OUT, SILU, PAIR>), dim3(grid), dim3(pf::kThreads), 0, stream, x,
                        g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P,
-                       g.N, g.K, g.out, g.act_limit);
+                       g.N, g.K, g.out, g.act_limit, g.pair_weights);
   }
   return hipGetLastError();
 }
@@ -600,15 +616,22 @@ hipError_t launch_gemm_nvfp4(const GroupedArgs& g, const uint16_t* x, const uint
   const bool decode = g.sched == 1 || g.N % pf::kN != 0 || (g.sched == 0 && g.P < (int64_t)16 * g.E);
   if (g.silu_mul) {
     switch (g.out_kind) {
-      case OUT_F16: return go<OUT_F16, true>(g, decode, x, w, w_sf, w_gscale, stream);
-      case OUT_BF16: return go<OUT_BF16, true>(g, decode, x, w, w_sf, w_gscale, stream);
-      default: return go<OUT_F32, true>(g, decode, x, w, w_sf, w_gscale, stream);
+      case OUT_F16: return go<OUT_F16, true, false>(g, decode, x, w, w_sf, w_gscale, stream);
+      case OUT_BF16: return go<OUT_BF16, true, false>(g, decode, x, w, w_sf, w_gscale, stream);
+      default: return go<OUT_F32, true, false>(g, decode, x, w, w_sf, w_gscale, stream);
+    }
+  }
+  if (g.pair_weights) {
+    switch (g.out_kind) {
+      case OUT_F16: return go<OUT_F16, false, true>(g, decode, x, w, w_sf, w_gscale, stream);
+      case OUT_BF16: return go<OUT_BF16, false, true>(g, decode, x, w, w_sf, w_gscale, stream);
+      default: return go<OUT_F32, false, true>(g, decode, x, w, w_sf, w_gscale, stream);
     }
   }
   switch (g.out_kind) {
-    case OUT_F16: return go<OUT_F16, false>(g, decode, x, w, w_sf, w_gscale, stream);
-    case OUT_BF16: return go<OUT_BF16, false>(g, decode, x, w, w_sf, w_gscale, stream);
-    default: return go<OUT_F32, false>(g, decode, x, w, w_sf, w_gscale, stream);
+    case OUT_F16: return go<OUT_F16, false, false>(g, decode, x, w, w_sf, w_gscale, stream);
+    case OUT_BF16: return go<OUT_BF16, false, false>(g, decode, x, w, w_sf, w_gscale, stream);
+    default: return go<OUT_F32, false, false>(g, decode, x, w, w_sf, w_gscale, stream);
   }
 }
 

@@ -14,7 +14,8 @@ size_t route_lds_bytes(int E);
 hipError_t launch_route(const int* ids, int P, int E, int* offsets, int* sorted_ids,
                         int* pair_to_sorted, int* n_invalid, void* ws, hipStream_t stream);
 
-// Combine.  y_kind / out_kind are OutKind values.
+// Combine.  y_kind / out_kind are OutKind values.  tw == null: y holds
+// pre-weighted rows in pair order (row t*topk + j), summed unweighted.
 hipError_t launch_combine(const void* y, int y_kind, const int* p2s, const float* tw, int T,
                           int topk, int N, int64_t P, int out_kind, void* out, hipStream_t stream);
 
@@ -35,6 +36,7 @@ struct GroupedArgs {
   int K;
   int silu_mul;             // 1: write I = N/2 columns silu(gate) * up
   float act_limit;          // SwiGLU clamp (NVFP4 only); +inf: none
+  const float* pair_weights;  // [P] or null: write w[p] * y to row p = sorted_ids[s] (NVFP4 only)
   int out_kind;             // OutKind
   void* out;
   int sched;                // 0 auto, 1 decode, 2 prefill

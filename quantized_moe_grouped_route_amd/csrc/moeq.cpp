@@ -86,6 +86,7 @@ moeq::GroupedArgs make_args(const int32_t* offsets, const int32_t* sorted, int64
   g.K = (int)K;
   g.silu_mul = silu ? 1 : 0;
   g.act_limit = INFINITY;
+  g.pair_weights = nullptr;
   g.out_kind = (int)od;
   g.out = out;
   g.sched = (int)sched;
@@ -178,8 +179,8 @@ moeq_status grouped_gemm_qnvfp4(const void* x, int64_t rows_a, moeq_arow a_row, 
                                 const uint8_t* w_sf, const float* w_gscale,
                                 const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
                                 int64_t P, int32_t topk, int32_t E, int64_t N, int64_t K,
-                                moeq_act act, float act_limit, moeq_dtype out_dtype, void* out,
-                                moeq_sched sched, void* stream) {
+                                moeq_act act, float act_limit, const float* pair_weights,
+                                moeq_dtype out_dtype, void* out, moeq_sched sched, void* stream) {
   const char* fn = "grouped_gemm_qnvfp4";
   moeq_status st = check_grouped(fn, x, rows_a, a_row, w, expert_offsets, P, topk, E, N, K, out);
   if (st != MOEQ_OK) return st;
@@ -189,6 +190,11 @@ moeq_status grouped_gemm_qnvfp4(const void* x, int64_t rows_a, moeq_arow a_row, 
     return fail(MOEQ_EUNSUPPORTED, "%s: act %d", fn, act);
   if (act == MOEQ_ACT_SILU_MUL_LIMIT && !(act_limit > 0.0f))
     return fail(MOEQ_EINVAL, "%s: act_limit %g must be > 0", fn, (double)act_limit);
+  if (pair_weights) {
+    if (act != MOEQ_ACT_NONE) return fail(MOEQ_EUNSUPPORTED, "%s: pair_weights need act NONE", fn);
+    if (!sorted_pair_ids) return fail(MOEQ_EINVAL, "%s: pair_weights need sorted_pair_ids", fn);
+    if (!aligned(pair_weights, 4)) return fail(MOEQ_EALIGN, "%s: pair_weights misaligned", fn);
+  }
   if (out_dtype != MOEQ_F16 && out_dtype != MOEQ_BF16 && out_dtype != MOEQ_F32)
     return fail(MOEQ_EUNSUPPORTED, "%s: out dtype %d", fn, out_dtype);
   if (a_row == MOEQ_AROW_TOKEN && !sorted_pair_ids && rows_a < P)
@@ -197,6 +203,7 @@ moeq_status grouped_gemm_qnvfp4(const void* x, int64_t rows_a, moeq_arow a_row, 
   moeq::GroupedArgs g = make_args(expert_offsets, sorted_pair_ids, rows_a, a_row, P, topk, E, N, K,
                                   act != MOEQ_ACT_NONE, out_dtype, out, sched);
   if (act == MOEQ_ACT_SILU_MUL_LIMIT) g.act_limit = act_limit;
+  g.pair_weights = pair_weights;
   return hip_status(moeq::launch_gemm_nvfp4(g, static_cast<const uint16_t*>(x), w, w_sf, w_gscale,
                                             (hipStream_t)stream),
                     fn);
@@ -221,6 +228,26 @@ moeq_status moe_scatter_combine(const void* y, moeq_dtype y_dtype, const int32_t
   return hip_status(moeq::launch_combine(y, (int)y_dtype, pair_to_sorted, topk_weights, (int)T, topk,
                                          (int)N, T * (int64_t)topk, (int)out_dtype, out,
                                          (hipStream_t)stream),
+                    fn);
+}
+
+moeq_status moe_sum_pairs(const void* y_pairs, moeq_dtype y_dtype, const int32_t* pair_to_sorted, int64_t T,
+                          int32_t topk, int64_t N, moeq_dtype out_dtype, void* out, void* stream) {
+  const char* fn = "moe_sum_pairs";
+  if (T < 0) return fail(MOEQ_EINVAL, "%s: T=%lld < 0", fn, (long long)T);
+  if (topk < 1 || topk > kMaxTopk) return fail(MOEQ_EINVAL, "%s: topk=%d outside [1, %d]", fn, topk, kMaxTopk);
+  if (N <= 0 || N > (1 << 24)) return fail(MOEQ_EINVAL, "%s: N=%lld out of range", fn, (long long)N);
+  if (N % 8 != 0) return fail(MOEQ_EALIGN, "%s: N=%lld must be a multiple of 8", fn, (long long)N);
+  if (T * (int64_t)topk >= (int64_t(1) << 31)) return fail(MOEQ_EINVAL, "%s: T*topk too large", fn);
+  if (y_dtype != MOEQ_F16 && y_dtype != MOEQ_BF16 && y_dtype != MOEQ_F32)
+    return fail(MOEQ_EUNSUPPORTED, "%s: y dtype %d", fn, y_dtype);
+  if (out_dtype != MOEQ_F16 && out_dtype != MOEQ_BF16 && out_dtype != MOEQ_F32)
+    return fail(MOEQ_EUNSUPPORTED, "%s: out dtype %d", fn, out_dtype);
+  if (T > 0 && (!y_pairs || !pair_to_sorted || !out)) return fail(MOEQ_EINVAL, "%s: null pointer", fn);
+  if (!aligned(y_pairs, 16) || !aligned(out, 16) || !aligned(pair_to_sorted, 4))
+    return fail(MOEQ_EALIGN, "%s: pointers misaligned", fn);
+  return hip_status(moeq::launch_combine(y_pairs, (int)y_dtype, pair_to_sorted, nullptr, (int)T, topk, (int)N,
+                                         T * (int64_t)topk, (int)out_dtype, out, (hipStream_t)stream),
                     fn);
 }
 

@@ -110,11 +110,11 @@ def test_fp8_rejects(L, kw, status):
 
 def _nvfp4(L, **kw):
     a = dict(x=A16, rows=16, arow=0, w=A16, sf=A16, gs=A16, off=A16, srt=A16, P=16, topk=2, E=4,
-             N=256, K=256, act=0, lim=0.0, od=mq.BF16, out=A16, sched=0)
+             N=256, K=256, act=0, lim=0.0, pw=None, od=mq.BF16, out=A16, sched=0)
     a.update(kw)
     return L.grouped_gemm_qnvfp4(a["x"], a["rows"], a["arow"], a["w"], a["sf"], a["gs"], a["off"],
                                  a["srt"], a["P"], a["topk"], a["E"], a["N"], a["K"], a["act"],
-                                 a["lim"], a["od"], a["out"], a["sched"], None)
+                                 a["lim"], a["pw"], a["od"], a["out"], a["sched"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -123,6 +123,8 @@ def _nvfp4(L, **kw):
     (dict(x=None), mq.EINVAL), (dict(act=2, lim=0.0, K=96), mq.EALIGN),
     (dict(act=2, lim=0.0), mq.EINVAL), (dict(act=2, lim=-1.0), mq.EINVAL),
     (dict(act=2, lim=float("nan")), mq.EINVAL),
+    (dict(pw=A16, act=1), mq.EUNSUPPORTED), (dict(pw=A16, srt=None), mq.EINVAL),
+    (dict(pw=ODD), mq.EALIGN),
 ])
 def test_nvfp4_rejects(L, kw, status):
     assert _nvfp4(L, **kw) == status
@@ -189,3 +191,18 @@ def _repack(L, **kw):
 def test_repack_rejects(L, kw, status):
     assert _repack(L, **kw) == status
     assert b"moe_nvfp4_repack" in L.moeq_last_error()
+
+
+def _sum_pairs(L, **kw):
+    a = dict(y=A16, yd=mq.BF16, p2s=A16, T=8, topk=2, N=256, od=mq.BF16, out=A16)
+    a.update(kw)
+    return L.moe_sum_pairs(a["y"], a["yd"], a["p2s"], a["T"], a["topk"], a["N"], a["od"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=12), mq.EALIGN), (dict(T=-2), mq.EINVAL), (dict(topk=0), mq.EINVAL),
+    (dict(yd=mq.I32), mq.EUNSUPPORTED), (dict(od=7), mq.EUNSUPPORTED), (dict(y=None), mq.EINVAL),
+    (dict(p2s=None), mq.EINVAL), (dict(out=ODD), mq.EALIGN),
+])
+def test_sum_pairs_rejects(L, kw, status):
+    assert _sum_pairs(L, **kw) == status

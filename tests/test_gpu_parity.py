@@ -468,3 +468,72 @@ def test_nvfp4_silu_mul_limit(sched):
                                    sched=sched)
     h_plain = mq.grouped_gemm_qnvfp4(*args, act="silu_mul", out_dtype=torch.float32, sched=sched)
     assert torch.equal(h_inf, h_plain)
+
+
+def _pair_case(seed, T, E, k, H, I, drop=0.1):
+    d = synth.nvfp4_moe(seed, T, E, k, H, I, routing="repeat")
+    rng = np.random.default_rng(seed)
+    d["topk_ids"][rng.random((T, k)) < drop] = -1          # pairs without an expert
+    return d
+
+
+@pytest.mark.parametrize("sched", ["prefill", "decode"])
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
+def test_nvfp4_fc2_pair_weighted_epilogue(sched, odt):
+    # megamoe_rm.cu's fc2_rm epilogue: w[p] * y in pair row p; rows of pairs
+    # without an expert keep their previous contents
+    T, E, k, H, I = 120, 5, 3, 256, 256
+    d = _pair_case(63, T, E, k, H, I)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    P = T * k
+    hs = synth.normal_bf16(np.random.default_rng(2), (P, I))
+    tw = dev(d["topk_weights"].reshape(-1))
+    out = torch.full((P, H), float("nan"), dtype=odt, device="cuda")
+    mq.grouped_gemm_qnvfp4(dev(hs), dev(d["w2"]), dev(d["s2"]), dev(d["g2"]), offs, srt, k, a_row="sorted",
+                           pair_weights=tw, out=out, out_dtype=odt, sched=sched)
+    y = oracle.grouped_gemm_qnvfp4(hs, "sorted", d["w2"], d["s2"], d["g2"], host(offs), host(srt), k)["y"]
+    ypart, valid = oracle.pair_rows(y, host(srt), d["topk_weights"])
+    got = host(out)
+    assert valid.sum() < P and np.all(np.isnan(got[~valid]))
+    assert_rows_close(got[valid], ypart[valid], what=f"fc2 pair epilogue {sched}")
+
+
+@pytest.mark.parametrize("ydt,odt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.float32),
+                                     (torch.float16, torch.bfloat16)])
+def test_sum_pairs(ydt, odt):
+    T, k, E, N = 77, 4, 6, 264
+    rng = np.random.default_rng(4)
+    ids = synth.uniform_ids_with_repeats(rng, T, k, E)
+    ids[rng.random((T, k)) < 0.15] = -1
+    ids[5] = -1                                                 # a token with no expert
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(ids), E)
+    yp = torch.from_numpy(rng.standard_normal((T * k, N)).astype(np.float32)).to(ydt).cuda()
+    yp[torch.from_numpy(host(p2s) < 0).cuda()] = float("nan")    # unrouted rows hold garbage
+    out = mq.moe_sum_pairs(yp, p2s, T, k, out_dtype=odt)
+    ref = oracle.sum_pairs(np.nan_to_num(host(yp)), host(p2s), T, k)
+    assert_rows_close(host(out), ref, what="sum_pairs")
+    assert bool((out[5] == 0).all())
+
+
+@pytest.mark.parametrize("sched", ["prefill", "decode"])
+def test_nvfp4_layer_with_fc2_pair_epilogue(sched):
+    # FC1 -> FC2 with the top-k weight in its epilogue -> pair sum, against
+    # the oracle; the same layer through the sorted FC2 and the weighted
+    # scatter-combine meets the same bar
+    T, E, k, H, I = 90, 4, 2, 512, 256
+    d = _pair_case(64, T, E, k, H, I)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    h = mq.grouped_gemm_qnvfp4(dev(d["x"]), dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k,
+                               act="silu_mul", sched=sched)
+    tw = dev(d["topk_weights"])
+    yp = mq.grouped_gemm_qnvfp4(h, dev(d["w2"]), dev(d["s2"]), dev(d["g2"]), offs, srt, k, a_row="sorted",
+                                pair_weights=tw.reshape(-1), sched=sched)
+    out = mq.moe_sum_pairs(yp, p2s, T, k)
+    y = oracle.grouped_gemm_qnvfp4(bf16_bits(h), "sorted", d["w2"], d["s2"], d["g2"], host(offs), host(srt),
+                                   k)["y"]
+    ref = oracle.scatter_combine(y, host(p2s), d["topk_weights"])
+    assert_rows_close(host(out), ref, what=f"layer, pair epilogue {sched}")
+    ys = mq.grouped_gemm_qnvfp4(h, dev(d["w2"]), dev(d["s2"]), dev(d["g2"]), offs, srt, k, a_row="sorted",
+                                sched=sched)
+    out2 = mq.moe_scatter_combine(ys, p2s, tw)
+    assert_rows_close(host(out2), ref, what=f"layer, sorted FC2 {sched}")

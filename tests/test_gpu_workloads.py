@@ -19,9 +19,9 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def _run(idx):
+def _run(idx, fc2="sorted"):
     import bench
-    wl = bench.Workload(idx)
+    wl = bench.Workload(idx, fc2)
     wl.step()
     torch.cuda.synchronize()
     return wl
@@ -99,6 +99,24 @@ def test_workload3_nvfp4_prefill_zipf():
     sizes = np.diff(host(wl.route_out[0]))
     assert sizes.min() == 0 and sizes.max() > 1000      # skewed, with empty experts
     _nvfp4_checks(wl, n_per=2)
+
+
+@pytest.mark.parametrize("idx", [2, 3])
+def test_nvfp4_workloads_with_fc2_pair_epilogue(idx):
+    # the step with the top-k weight in FC2's epilogue: pair rows of sampled
+    # sorted rows, then the whole pair sum against the oracle on the GPU's rows
+    wl = _run(idx, fc2="pair")
+    off, srt, p2s, _ = _check_route(wl)
+    d = wl.d
+    rows = _sample_rows(off, n_per=1 if idx == 2 else 2)
+    hb = bf16_bits(wl.h)
+    y_ref = oracle.grouped_gemm_qnvfp4(hb, "sorted", d["w2"], d["s2"], d["g2"], off, srt, d["k"], rows=rows)["y"]
+    pairs = srt[rows]
+    w = d["topk_weights"].reshape(-1)[pairs]
+    assert_rows_close(host(wl.y)[pairs], w[:, None] * y_ref, what="FC2 pair rows")
+    yp = host(wl.y)
+    yp[p2s < 0] = 0
+    assert_rows_close(host(wl.out), oracle.sum_pairs(yp, p2s, wl.T, wl.k), what="pair sum")
 
 
 def test_workload4_w4a4_mixtral():
