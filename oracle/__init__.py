@@ -29,7 +29,8 @@ Python, a differently structured algorithm, invariants).  No function is
 parity unpinned.
 """
 from .formats import (unpack_nibbles, int4_value, e2m1_value, e4m3fn_value, ue4m3_value,
-                      bf16_value, round_to_f16, round_to_bf16, round_to)
+                      bf16_value, round_to_f16, round_to_bf16, round_to, f16_value, f16_bits,
+                      bf16_to_f16_bits)
 from .route import route_prep
 from .gemm import (grouped_gemm_qint4, grouped_gemm_qfp8_block, grouped_gemm_qnvfp4, silu_mul,
                    gemm_rows)

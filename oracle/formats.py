@@ -72,6 +72,26 @@ def bf16_value(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def f16_value(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns (uint16) -> float64."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def f16_bits(x: np.ndarray) -> np.ndarray:
+    """float64 -> IEEE binary16 bits, rounded once to nearest even (overflow
+    to +-inf, gradual underflow), as numpy's double->half conversion does."""
+    return np.asarray(x, np.float64).astype(np.float16).view(np.uint16)
+
+
+def bf16_to_f16_bits(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bits -> binary16 bits of the nearest binary16 value (ties to
+    even).  Exact for every bf16 value of magnitude in [2^-14, 65504]: bf16
+    carries 8 significant bits and binary16 11.  Used when bf16 activations
+    are handed to the fp16 form of the NVFP4 GEMM (megamoe_rm.cu converts its
+    bf16 input to fp16 in route_prep the same way)."""
+    return f16_bits(bf16_value(bits))
+
+
 def round_to_f16(x: np.ndarray) -> np.ndarray:
     """Round float64 to the nearest IEEE binary16 (ties to even); returned as
     float64.  numpy's double->half conversion rounds once, to nearest even."""

@@ -22,7 +22,7 @@ from __future__ import annotations
 import numpy as np
 
 from .formats import (unpack_nibbles, int4_value, e4m3fn_value, e2m1_value, ue4m3_value,
-                      bf16_value)
+                      bf16_value, f16_value)
 
 
 def gemm_rows(offsets, sorted_pair_ids, topk: int, a_row: str, rows=None):
@@ -117,11 +117,12 @@ def grouped_gemm_qfp8_block(a, a_scale, a_row, w, w_scale, offsets, sorted_pair_
 
 
 def grouped_gemm_qnvfp4(x, a_row, w, w_sf, w_gscale, offsets, sorted_pair_ids, topk,
-                        act="none", rows=None, limit=None):
+                        act="none", rows=None, limit=None, x_dtype="bf16"):
     """NVFP4 W4A16 grouped GEMM (tilelang_kernels.py grouped_gemm_fp4, with the
     per-expert global scale of megamoe_rm.cu).
 
-    x [rows_a][K] bf16 bits; w [E][N][K/2] E2M1 codes packed two per byte;
+    x [rows_a][K] bf16 bits (x_dtype 'bf16') or IEEE binary16 bits ('f16',
+    megamoe_rm.cu's fp16 activations); w [E][N][K/2] E2M1 codes packed two per byte;
     w_sf [E][N][K/16] UE4M3 per-16 block scales; w_gscale [E] f32.
       Wd[e, n, k] = e2m1(W[e, n, k]) * ue4m3(w_sf[e, n, k // 16])
       y[s, n]     = w_gscale[e] * sum_k x[r, k] * Wd[e, n, k]
@@ -130,7 +131,9 @@ def grouped_gemm_qnvfp4(x, a_row, w, w_sf, w_gscale, offsets, sorted_pair_ids, t
     global scale, then the clamp, then the product).  Returns dict(y=float64)."""
     s, e, r = gemm_rows(offsets, sorted_pair_ids, topk, a_row, rows)
     N = w.shape[1]
-    X = bf16_value(np.asarray(x)[r])
+    if x_dtype not in ("bf16", "f16"):
+        raise ValueError(x_dtype)
+    X = (bf16_value if x_dtype == "bf16" else f16_value)(np.asarray(x)[r])
     y = np.zeros((s.size, N), np.float64)
     for ex in np.unique(e):
         m = e == ex

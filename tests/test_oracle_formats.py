@@ -104,3 +104,30 @@ def test_round_to_f16_matches_torch_from_f32():
     ref = torch.from_numpy(x).to(torch.float16).to(torch.float64).numpy()
     got = oracle.round_to_f16(x.astype(np.float64))
     assert np.array_equal(got, ref)
+
+
+def test_f16_value_known_patterns():
+    bits = np.array([0x0000, 0x3C00, 0xC000, 0x7BFF, 0x0001, 0x0400, 0x3555, 0x7C00], np.uint16)
+    v = oracle.f16_value(bits)
+    assert list(v[:7]) == [0.0, 1.0, -2.0, 65504.0, 2.0 ** -24, 2.0 ** -14, 0.25 * (1 + 341 / 1024)]
+    assert np.isposinf(v[7])
+    assert np.array_equal(oracle.f16_bits(v[:7]), bits[:7])
+
+
+def test_bf16_to_f16_exact_in_range_and_matches_torch_everywhere():
+    import torch
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.bf16_to_f16_bits(bits)
+    # every bf16 value of magnitude in [2^-14, 65504] converts exactly
+    v = oracle.bf16_value(bits)
+    m = np.isfinite(v) & (np.abs(v) >= 2.0 ** -14) & (np.abs(v) <= 65504)
+    assert np.array_equal(oracle.f16_value(got[m]), v[m])
+    # overflow and the largest finite boundary
+    assert oracle.bf16_to_f16_bits(np.array([0x4780], np.uint16))[0] == 0x7C00     # 65536 -> inf
+    assert oracle.bf16_to_f16_bits(np.array([0x477F], np.uint16))[0] == 0x7BF8     # 65280, exact
+    # all 65536 patterns against torch's own bf16 -> f16 conversion (NaNs: both NaN)
+    t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float16)
+    ref = t.view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(v)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all(np.isnan(oracle.f16_value(got[nan])))

@@ -253,3 +253,23 @@ def test_scaling_a_scale_scales_rows_exactly():
     y2 = oracle.grouped_gemm_qint4(d["a"], sa, "token", d["w"], d["w_scale"], off, srt, 2)["y"]
     rows4 = (srt[: off[-1]] // 2) == 4
     assert np.array_equal(y2[rows4], 2 * y1[rows4]) and np.array_equal(y2[~rows4], y1[~rows4])
+
+
+def test_nvfp4_f16_activations_equal_bf16_when_exact():
+    # bf16 activations in the binary16 normal range convert exactly, so the
+    # fp16 form of the GEMM gives the same fp64 result; a value below 2^-14
+    # rounds and changes it by at most its rounding error
+    d = synth.nvfp4_moe(15, T=6, E=2, k=1, H=64, I=32)
+    off, srt, inv, _ = oracle.route_prep(d["topk_ids"], 2)
+    x = d["x"].copy()
+    v = oracle.bf16_value(x)
+    x[np.abs(v) < 2.0 ** -14] = 0x3F80                     # 1.0: keep every value exact
+    xh = oracle.bf16_to_f16_bits(x)
+    yb = oracle.grouped_gemm_qnvfp4(x, "token", d["w1"], d["s1"], d["g1"], off, srt, 1)["y"]
+    yh = oracle.grouped_gemm_qnvfp4(xh, "token", d["w1"], d["s1"], d["g1"], off, srt, 1, x_dtype="f16")["y"]
+    assert np.array_equal(yb, yh)
+    x[0, 0] = 0x3300                                       # bf16 2^-25: an fp16 tie, rounds to 0
+    xh = oracle.bf16_to_f16_bits(x)
+    assert xh[0, 0] == 0
+    with pytest.raises(ValueError):
+        oracle.grouped_gemm_qnvfp4(xh, "token", d["w1"], d["s1"], d["g1"], off, srt, 1, x_dtype="f32")
