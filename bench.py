@@ -8,7 +8,8 @@ synthetic input already resident in HBM:
   1  FP8 e4m3 1x128 / 128x128 block-scaled dense GEMM M=1024 N=4096
      K=7168 (default): route (E=1) + FP8 GEMM
   2  NVFP4 W4A16 decode, 8 tokens, E=256, top-8, H=7168 I=2048:
-     route + FC1 (SiLU-gated) + FC2 + combine
+     route + FC1 (SiLU-gated) + FC2 + combine; with --act f16 (default) the
+     bf16 input is first cast to binary16 and h is binary16
   3  NVFP4 W4A16 prefill, 4096 tokens, Zipf(1.1) routing: as 2
   4  W4A4 INT4 Mixtral-like, 8192 tokens, E=8, top-2, H=4096 I=14336:
      route + FC1 (SiLU-gated) + FC2 (int4 rows in sorted order) + combine
@@ -81,11 +82,11 @@ def _traffic(kernel_tag, sources):
 class Workload:
     """Device buffers and the launch sequence of one step."""
 
-    def __init__(self, idx: int, fc2: str = "sorted"):
+    def __init__(self, idx: int, fc2: str = "sorted", act: str = "f16"):
         import torch
         import synth
         import quantized_moe_grouped_route_amd as mq
-        self.mq, self.idx, self.fc2 = mq, idx, fc2
+        self.mq, self.idx, self.fc2, self.act = mq, idx, fc2, act
         self.cfg = synth.WORKLOADS[idx]
         self.d = d = synth.workload(idx)
         if self.cfg["kind"] == "repack":
@@ -146,7 +147,9 @@ class Workload:
             self.x = _dev(d["x"])
             self.w1, self.s1, self.g1 = _dev(d["w1"]), _dev(d["s1"]), _dev(d["g1"])
             self.w2, self.s2, self.g2 = _dev(d["w2"]), _dev(d["s2"]), _dev(d["g2"])
-            self.h = torch.empty(P, I, dtype=torch.bfloat16, device="cuda")
+            hdt = torch.float16 if act == "f16" else torch.bfloat16
+            self.xh = torch.empty(T, H, dtype=torch.float16, device="cuda") if act == "f16" else None
+            self.h = torch.empty(P, I, dtype=hdt, device="cuda")
             self.y = torch.empty(P, H, dtype=torch.bfloat16, device="cuda")
             self.tw_flat = self.tw.reshape(-1)
             self.out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
@@ -157,7 +160,7 @@ class Workload:
             self.weight_bytes = float(self.active * per_expert)
             self.fc1_bytes = float(self.active * (2 * I * H // 2 + 2 * I * H // 16 + 4))
             self.flops = 2.0 * valid.size * (2 * I * H + H * I)
-            self.dtype = "bf16_x_nvfp4"
+            self.dtype = "f16_x_nvfp4" if act == "f16" else "bf16_x_nvfp4"
             if idx == 2:
                 self.dom = ("nvfp4_decode", ["gemm_nvfp4.hip", "nvfp4.h", "common.h", "tile.h", "pipeline.h"], "hbm",
                             PEAK["hbm_GBps"])
@@ -222,9 +225,13 @@ class Workload:
                                   a_row="sorted", out=self.y)
             mq.moe_scatter_combine(self.y, p2s, self.tw, out=self.out)
         else:
+            x = self.x
+            if self.act == "f16":
+                # megamoe_rm.cu's fp16 activations: the bf16 input is cast once
+                x = mq.cast_bf16_to_f16(self.x, out=self.xh)
             if ev: ev[0].record()
-            mq.grouped_gemm_qnvfp4(self.x, self.w1, self.s1, self.g1, offs, srt, self.k, act="silu_mul",
-                                   out=self.h)
+            mq.grouped_gemm_qnvfp4(x, self.w1, self.s1, self.g1, offs, srt, self.k, act="silu_mul",
+                                   out=self.h, out_dtype=self.h.dtype)
             if ev: ev[1].record()
             if self.fc2 == "pair":
                 # top-k weight in FC2's epilogue, rows in pair order, then the pair sum
@@ -517,6 +524,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=1, choices=sorted(__import__("synth").WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--act", choices=("bf16", "f16"), default="f16",
+                    help="NVFP4 workloads: GEMMs on the bf16 activations, or on binary16 activations "
+                         "(the bf16 input cast once, h kept in binary16; half the dequant work)")
     ap.add_argument("--fc2", choices=("sorted", "pair"), default="sorted",
                     help="NVFP4 workloads: FC2 writes sorted rows and the combine applies the top-k "
                          "weights (sorted), or FC2's epilogue applies them and writes pair-ordered "
@@ -553,7 +563,7 @@ def main():
         print(json.dumps({"copy_bytes_read_per_launch": src.numel() * 4,
                           "copy_bytes_written_per_launch": dst.numel() * 4}), flush=True)
         return
-    wl = Workload(args.workload, args.fc2)
+    wl = Workload(args.workload, args.fc2, args.act)
     torch.cuda.synchronize()
     host_s = []
     for _ in range(args.warmup):
@@ -607,6 +617,7 @@ def main():
     config.update({k: v for k, v in cfg.items() if k not in ("name", "kind")})
     if cfg["kind"] == "nvfp4":
         config["fc2_epilogue"] = args.fc2
+        config["activations"] = args.act
     if args.workload in (2, 6):
         config["active_experts"] = wl.active
         config["weight_bytes"] = wl.weight_bytes

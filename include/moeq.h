@@ -177,9 +177,13 @@ moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int6
  * (E2M1 weights with UE4M3 scales per 16 along K, bf16 activations) with
  * the per-expert global scale of [MMRM] (alpha = weight_scale_2 /
  * input_scale).  Weights are dequantized exactly (every E2M1 x UE4M3
- * product is a bf16 value) in registers, never as a separate pass.
+ * product is both a bf16 and a binary16 value) in registers, never as a
+ * separate pass.
  *
- *   x         bf16  [rows_a][K]       activations
+ *   x         [rows_a][K] activations of x_dtype: BF16, or F16 ([MMRM]'s
+ *             fp16 activations; the weights are then dequantized and
+ *             multiplied in fp16, at half the dequantization work; see
+ *             moe_cast_bf16_to_f16)
  *   w         uint8 [E][N][K/2]       E2M1 codes
  *   w_sf      uint8 [E][N][K/16]      UE4M3 block scales (sign bit clear;
  *                                     0x7F is not a valid scale).  [TLK]'s
@@ -206,12 +210,25 @@ moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int6
  * weight-streaming schedule when P < 16 * E or N % 256 != 0; PREFILL with
  * N % 256 != 0 falls back to it as well.
  * ---------------------------------------------------------------------- */
-moeq_status grouped_gemm_qnvfp4(const void* x, int64_t rows_a, moeq_arow a_row,
+moeq_status grouped_gemm_qnvfp4(const void* x, moeq_dtype x_dtype, int64_t rows_a, moeq_arow a_row,
                                 const uint8_t* w, const uint8_t* w_sf, const float* w_gscale,
                                 const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
                                 int64_t P, int32_t topk, int32_t E, int64_t N, int64_t K,
                                 moeq_act act, float act_limit, const float* pair_weights,
                                 moeq_dtype out_dtype, void* out, moeq_sched sched, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_cast_bf16_to_f16 - bf16 -> IEEE binary16 conversion of activations,
+ * for the F16 form of grouped_gemm_qnvfp4 ([MMRM] route_prep converts its
+ * bf16 input to fp16 the same way).  Each value is rounded once to the
+ * nearest binary16 (ties to even, overflow to +-inf), so every bf16 value
+ * of magnitude in [2^-14, 65504] converts exactly.
+ *
+ *   x  uint16 [n] bf16 bits;  y  uint16 [n] binary16 bits (out)
+ * Requires n % 8 == 0 (else MOEQ_EALIGN), 16-byte aligned x and y, and y
+ * either equal to x (in place) or disjoint from it (else MOEQ_EINVAL).
+ * ---------------------------------------------------------------------- */
+moeq_status moe_cast_bf16_to_f16(const uint16_t* x, int64_t n, uint16_t* y, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_quantize_int4 - per-row symmetric INT4 quantization of activations.

@@ -32,7 +32,7 @@ _DTYPE_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32, tor
 EXPORTS = ("moeq_last_error", "moeq_abi_version", "moe_route_prep_workspace_bytes",
            "moe_route_prep", "grouped_gemm_qint4", "grouped_gemm_qfp8_block",
            "grouped_gemm_qnvfp4", "moe_scatter_combine", "moe_quantize_int4",
-           "moe_nvfp4_repack", "moe_sum_pairs")
+           "moe_nvfp4_repack", "moe_sum_pairs", "moe_cast_bf16_to_f16")
 
 
 class MoeqError(RuntimeError):
@@ -62,12 +62,13 @@ def lib():
                                      i32, i32, vp, i32, vp]),
         "grouped_gemm_qfp8_block": (i32, [vp, vp, i64, i32, vp, vp, vp, vp, i64, i32, i32, i64,
                                           i64, i32, vp, i32, vp]),
-        "grouped_gemm_qnvfp4": (i32, [vp, i64, i32, vp, vp, vp, vp, vp, i64, i32, i32, i64, i64,
+        "grouped_gemm_qnvfp4": (i32, [vp, i32, i64, i32, vp, vp, vp, vp, vp, i64, i32, i32, i64, i64,
                                       i32, C.c_float, vp, i32, vp, i32, vp]),
         "moe_scatter_combine": (i32, [vp, i32, vp, vp, i64, i32, i64, i32, vp, vp]),
         "moe_quantize_int4": (i32, [vp, i32, i64, i64, vp, vp, vp]),
         "moe_nvfp4_repack": (i32, [vp, vp, i64, i64, i64, i32, vp, vp, vp]),
         "moe_sum_pairs": (i32, [vp, i32, vp, i64, i32, i64, i32, vp, vp]),
+        "moe_cast_bf16_to_f16": (i32, [vp, i64, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -209,14 +210,15 @@ def grouped_gemm_qfp8_block(a, a_scale, w, w_scale, expert_offsets, sorted_pair_
 def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, topk: int, *,
                         a_row="token", act="none", limit=None, pair_weights=None,
                         out_dtype=torch.bfloat16, out=None, P=None, sched="auto"):
-    """NVFP4 W4A16 grouped GEMM: x bf16 [rows_a][K], w uint8 [E][N][K/2]
+    """NVFP4 W4A16 grouped GEMM: x bf16 or f16 [rows_a][K] (f16: dequant and
+    MFMA in binary16, megamoe_rm.cu's fp16 activations), w uint8 [E][N][K/2]
     (E2M1), w_sf uint8 [E][N][K/16] (UE4M3) or int32 [E][N][K/64] (four
     UE4M3 per word, block 4g+j in bits 8j..8j+7: the same bytes), w_gscale
     f32 [E].  Returns out [P][N] (act 'none') or [P][N/2] ('silu_mul';
     with `limit`, the clamped SwiGLU of megamoe_rm.cu's fc1_rm).
     pair_weights (f32, T*topk values, e.g. topk_weights): megamoe_rm.cu's
     fc2_rm epilogue, out row p = w[p] * y of pair p, in pair order."""
-    _need(x, "x", torch.bfloat16, 2)
+    _need(x, "x", (torch.bfloat16, torch.float16), 2)
     _need(w, "w", torch.uint8, 3)
     if isinstance(w_sf, torch.Tensor) and w_sf.dtype == torch.int32 and w_sf.dim() == 3:
         _need(w_sf, "w_sf", torch.int32, 3)
@@ -236,7 +238,8 @@ def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, t
         if sorted_pair_ids is None or pair_weights.numel() != sorted_pair_ids.numel():
             raise ValueError("pair_weights needs sorted_pair_ids and one weight per pair")
     out = _out(out, P, N // 2 if act == "silu_mul" else N, out_dtype, x.device)
-    st = lib().grouped_gemm_qnvfp4(_ptr(x), x.shape[0], arow, _ptr(w), _ptr(w_sf), _ptr(w_gscale),
+    st = lib().grouped_gemm_qnvfp4(_ptr(x), _DTYPE_CODE[x.dtype], x.shape[0], arow, _ptr(w), _ptr(w_sf),
+                                   _ptr(w_gscale),
                                    _ptr(expert_offsets), _ptr(sorted_pair_ids), P, topk, E, N, K,
                                    act_code, 0.0 if limit is None else float(limit), _ptr(pair_weights),
                                    _DTYPE_CODE[out_dtype], _ptr(out), SCHED[sched], _stream())
@@ -283,6 +286,21 @@ def moe_sum_pairs(y_pairs, pair_to_sorted, T: int, topk: int, *, out_dtype=None,
     st = lib().moe_sum_pairs(_ptr(y_pairs), _DTYPE_CODE[y_pairs.dtype], _ptr(pair_to_sorted), T, topk, N,
                              _DTYPE_CODE[out_dtype], _ptr(out), _stream())
     _check("moe_sum_pairs", st)
+    return out
+
+
+def cast_bf16_to_f16(x, *, out=None):
+    """bf16 tensor -> binary16 tensor of the same shape, each value rounded
+    once to nearest even (exact for magnitudes in [2^-14, 65504]); `out` may
+    be x viewed as float16 (in place) or a separate contiguous tensor."""
+    _need(x, "x", torch.bfloat16)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float16, device=x.device)
+    _need(out, "out", torch.float16)
+    if out.numel() != x.numel():
+        raise ValueError("out must have as many elements as x")
+    st = lib().moe_cast_bf16_to_f16(_ptr(x), x.numel(), _ptr(out), _stream())
+    _check("moe_cast_bf16_to_f16", st)
     return out
 
 

@@ -16,6 +16,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef unsigned u32;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -52,6 +54,14 @@ __device__ __forceinline__ v16f mfma_bf16_32x32x16(v8bf a, v8bf b, v16f c) {
 // D[4*(l/16) + i][l%16].
 __device__ __forceinline__ v4f mfma_bf16_16x16x32(v8bf a, v8bf b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// binary16 forms of the two bf16 MFMAs above (same operand layouts).
+__device__ __forceinline__ v16f mfma_f16_32x32x16(v8h a, v8h b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma_f16_16x16x32(v8h a, v8h b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // Row of the 32x32 output held in accumulator value i by lane l.

@@ -69,7 +69,8 @@ constexpr int kThreads = 256;
 // PAIR (act NONE only): megamoe_rm.cu's fc2_rm epilogue.  Sorted row s is
 // scaled by the top-k weight of its pair p = sorted_ids[s] and written to
 // output row p instead of s.
-template <int OUT, bool SILU, bool PAIR>
+// H16: the activations are binary16 (dequant and MFMA in fp16), else bf16.
+template <int OUT, bool SILU, bool PAIR, bool H16>
 __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale,
@@ -171,17 +172,33 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
         const u32x4 q0 = ld16(st + boff0), q1 = ld16(st + boff1);
         const uint32_t sc0 = *reinterpret_cast<const uint16_t*>(st + soff0);
         const uint32_t sc1 = *reinterpret_cast<const uint16_t*>(st + soff1);
-        const float s00 = e4m3_to_f32(sc0 & 0xffu), s01 = e4m3_to_f32(sc0 >> 8);
-        const float s10 = e4m3_to_f32(sc1 & 0xffu), s11 = e4m3_to_f32(sc1 >> 8);
+        if constexpr (H16) {
+          const v2h h0 = ue4m3x2_f16(sc0), h1 = ue4m3x2_f16(sc1);
+          const v2h s00 = {h0.x, h0.x}, s01 = {h0.y, h0.y}, s10 = {h1.x, h1.x}, s11 = {h1.y, h1.y};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const v8bf wf0 = __builtin_bit_cast(v8bf, dequant8_bf16(q0[s], s < 2 ? s00 : s01));
-          const v8bf wf1 = __builtin_bit_cast(v8bf, dequant8_bf16(q1[s], s < 2 ? s10 : s11));
+          for (int s = 0; s < 4; ++s) {
+            const v8h wf0 = __builtin_bit_cast(v8h, dequant8_f16(q0[s], s < 2 ? s00 : s01));
+            const v8h wf1 = __builtin_bit_cast(v8h, dequant8_f16(q1[s], s < 2 ? s10 : s11));
 #pragma unroll
-          for (int y = 0; y < NY; ++y) {
-            const v8bf xf = *reinterpret_cast<const v8bf*>(st + (32 * y + l32) * 128 + aoff[s]);
-            acc[0][y] = mfma_bf16_32x32x16(wf0, xf, acc[0][y]);
-            acc[1][y] = mfma_bf16_32x32x16(wf1, xf, acc[1][y]);
+            for (int y = 0; y < NY; ++y) {
+              const v8h xf = *reinterpret_cast<const v8h*>(st + (32 * y + l32) * 128 + aoff[s]);
+              acc[0][y] = mfma_f16_32x32x16(wf0, xf, acc[0][y]);
+              acc[1][y] = mfma_f16_32x32x16(wf1, xf, acc[1][y]);
+            }
+          }
+        } else {
+          const float s00 = e4m3_to_f32(sc0 & 0xffu), s01 = e4m3_to_f32(sc0 >> 8);
+          const float s10 = e4m3_to_f32(sc1 & 0xffu), s11 = e4m3_to_f32(sc1 >> 8);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const v8bf wf0 = __builtin_bit_cast(v8bf, dequant8_bf16(q0[s], s < 2 ? s00 : s01));
+            const v8bf wf1 = __builtin_bit_cast(v8bf, dequant8_bf16(q1[s], s < 2 ? s10 : s11));
+#pragma unroll
+            for (int y = 0; y < NY; ++y) {
+              const v8bf xf = *reinterpret_cast<const v8bf*>(st + (32 * y + l32) * 128 + aoff[s]);
+              acc[0][y] = mfma_bf16_32x32x16(wf0, xf, acc[0][y]);
+              acc[1][y] = mfma_bf16_32x32x16(wf1, xf, acc[1][y]);
+            }
           }
         }
       }
@@ -363,7 +380,7 @@ __device__ __forceinline__ void wait_vm(int n) {
   asm volatile("" ::: "memory");
 }
 
-template <int OUT, bool SILU, bool WIDE, bool PAIR>
+template <int OUT, bool SILU, bool WIDE, bool PAIR, bool H16>
 __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale, const int* __restrict__ offsets,
@@ -534,14 +551,26 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
     if (q + D < nq) issue(slot);
 #pragma unroll
     for (int cp = 0; cp < CPS; ++cp) {
-      const float a0 = e4m3_to_f32(q0[cp] & 0xffu), a1 = e4m3_to_f32(q0[cp] >> 8);
-      const float b0 = e4m3_to_f32(q1[cp] & 0xffu), b1 = e4m3_to_f32(q1[cp] >> 8);
+      if constexpr (H16) {
+        const v2h ha = ue4m3x2_f16(q0[cp]), hb = ue4m3x2_f16(q1[cp]);
+        const v2h a0 = {ha.x, ha.x}, a1 = {ha.y, ha.y}, b0 = {hb.x, hb.x}, b1 = {hb.y, hb.y};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc0 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16_hi(w0[cp][j], j < 2 ? a0 : a1)),
-                                  __builtin_bit_cast(v8bf, xv[cp][j]), acc0);
-        acc1 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16_hi(w1[cp][j], j < 2 ? b0 : b1)),
-                                  __builtin_bit_cast(v8bf, xv[cp][j]), acc1);
+        for (int j = 0; j < 4; ++j) {
+          acc0 = mfma_f16_16x16x32(__builtin_bit_cast(v8h, dequant8_f16(w0[cp][j], j < 2 ? a0 : a1)),
+                                   __builtin_bit_cast(v8h, xv[cp][j]), acc0);
+          acc1 = mfma_f16_16x16x32(__builtin_bit_cast(v8h, dequant8_f16(w1[cp][j], j < 2 ? b0 : b1)),
+                                   __builtin_bit_cast(v8h, xv[cp][j]), acc1);
+        }
+      } else {
+        const float a0 = e4m3_to_f32(q0[cp] & 0xffu), a1 = e4m3_to_f32(q0[cp] >> 8);
+        const float b0 = e4m3_to_f32(q1[cp] & 0xffu), b1 = e4m3_to_f32(q1[cp] >> 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc0 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16_hi(w0[cp][j], j < 2 ? a0 : a1)),
+                                    __builtin_bit_cast(v8bf, xv[cp][j]), acc0);
+          acc1 = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, dequant8_bf16_hi(w1[cp][j], j < 2 ? b0 : b1)),
+                                    __builtin_bit_cast(v8bf, xv[cp][j]), acc1);
+        }
       }
     }
     if (++st == steps) {
@@ -579,7 +608,7 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
   }
 }
 
-template <int OUT, bool SILU, bool PAIR>
+template <int OUT, bool SILU, bool PAIR, bool H16>
 hipError_t go(const GroupedArgs& g, bool decode, const uint16_t* x, const uint8_t* w,
               const uint8_t* sf, const float* gsc, hipStream_t stream) {
   if (decode) {
@@ -587,52 +616,58 @@ hipError_t go(const GroupedArgs& g, bool decode, const uint16_t* x, const uint8_
     // items over the waves itself
     const int grid = g.num_cus * 2;
     if (g.K % 512 == 0)
-      hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, true, PAIR>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
+      hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, true, PAIR, H16>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
                          g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N,
                          g.K, g.out, g.act_limit, g.pair_weights);
     else
-      hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, false, PAIR>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
+      hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, false, PAIR, H16>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
                          g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N,
                          g.K, g.out, g.act_limit, g.pair_weights);
   } else {
     const int64_t mt_ub = (g.P + pf::kM - 1) / pf::kM + std::min<int64_t>(g.E, g.P);
     const int64_t items_ub = mt_ub * (g.N / pf::kN);
     const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus * 2);
-    hipLaunchKernelGGL((nvfp4_prefill<OUT, SILU, PAIR>), dim3(grid), dim3(pf::kThreads), 0, stream, x,
+    hipLaunchKernelGGL((nvfp4_prefill<OUT, SILU, PAIR, H16>), dim3(grid), dim3(pf::kThreads), 0, stream, x,
                        g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P,
                        g.N, g.K, g.out, g.act_limit, g.pair_weights);
   }
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_gemm_nvfp4(const GroupedArgs& g, const uint16_t* x, const uint8_t* w,
-                             const uint8_t* w_sf, const float* w_gscale, hipStream_t stream) {
-  if (g.P == 0) return hipSuccess;
+template <bool H16>
+hipError_t dispatch(const GroupedArgs& g, const uint16_t* x, const uint8_t* w, const uint8_t* w_sf,
+                    const float* w_gscale, hipStream_t stream) {
   // The streaming schedule when asked for, under AUTO while experts average
   // fewer than 16 rows, and whenever N is not a multiple of the prefill
   // tile (256), which the prefill schedule cannot cover.
   const bool decode = g.sched == 1 || g.N % pf::kN != 0 || (g.sched == 0 && g.P < (int64_t)16 * g.E);
   if (g.silu_mul) {
     switch (g.out_kind) {
-      case OUT_F16: return go<OUT_F16, true, false>(g, decode, x, w, w_sf, w_gscale, stream);
-      case OUT_BF16: return go<OUT_BF16, true, false>(g, decode, x, w, w_sf, w_gscale, stream);
-      default: return go<OUT_F32, true, false>(g, decode, x, w, w_sf, w_gscale, stream);
+      case OUT_F16: return go<OUT_F16, true, false, H16>(g, decode, x, w, w_sf, w_gscale, stream);
+      case OUT_BF16: return go<OUT_BF16, true, false, H16>(g, decode, x, w, w_sf, w_gscale, stream);
+      default: return go<OUT_F32, true, false, H16>(g, decode, x, w, w_sf, w_gscale, stream);
     }
   }
   if (g.pair_weights) {
     switch (g.out_kind) {
-      case OUT_F16: return go<OUT_F16, false, true>(g, decode, x, w, w_sf, w_gscale, stream);
-      case OUT_BF16: return go<OUT_BF16, false, true>(g, decode, x, w, w_sf, w_gscale, stream);
-      default: return go<OUT_F32, false, true>(g, decode, x, w, w_sf, w_gscale, stream);
+      case OUT_F16: return go<OUT_F16, false, true, H16>(g, decode, x, w, w_sf, w_gscale, stream);
+      case OUT_BF16: return go<OUT_BF16, false, true, H16>(g, decode, x, w, w_sf, w_gscale, stream);
+      default: return go<OUT_F32, false, true, H16>(g, decode, x, w, w_sf, w_gscale, stream);
     }
   }
   switch (g.out_kind) {
-    case OUT_F16: return go<OUT_F16, false, false>(g, decode, x, w, w_sf, w_gscale, stream);
-    case OUT_BF16: return go<OUT_BF16, false, false>(g, decode, x, w, w_sf, w_gscale, stream);
-    default: return go<OUT_F32, false, false>(g, decode, x, w, w_sf, w_gscale, stream);
+    case OUT_F16: return go<OUT_F16, false, false, H16>(g, decode, x, w, w_sf, w_gscale, stream);
+    case OUT_BF16: return go<OUT_BF16, false, false, H16>(g, decode, x, w, w_sf, w_gscale, stream);
+    default: return go<OUT_F32, false, false, H16>(g, decode, x, w, w_sf, w_gscale, stream);
   }
+}
+}  // namespace
+
+hipError_t launch_gemm_nvfp4(const GroupedArgs& g, const uint16_t* x, const uint8_t* w,
+                             const uint8_t* w_sf, const float* w_gscale, hipStream_t stream) {
+  if (g.P == 0) return hipSuccess;
+  return g.x_f16 ? dispatch<true>(g, x, w, w_sf, w_gscale, stream)
+                 : dispatch<false>(g, x, w, w_sf, w_gscale, stream);
 }
 
 }  // namespace moeq

@@ -37,6 +37,7 @@ struct GroupedArgs {
   int silu_mul;             // 1: write I = N/2 columns silu(gate) * up
   float act_limit;          // SwiGLU clamp (NVFP4 only); +inf: none
   const float* pair_weights;  // [P] or null: write w[p] * y to row p = sorted_ids[s] (NVFP4 only)
+  int x_f16;                // NVFP4: activations are binary16 (else bf16)
   int out_kind;             // OutKind
   void* out;
   int sched;                // 0 auto, 1 decode, 2 prefill
@@ -49,6 +50,9 @@ hipError_t launch_gemm_fp8(const GroupedArgs& g, const uint8_t* a, const float* 
                            const uint8_t* w, const float* w_scale, hipStream_t stream);
 hipError_t launch_gemm_nvfp4(const GroupedArgs& g, const uint16_t* x, const uint8_t* w,
                              const uint8_t* w_sf, const float* w_gscale, hipStream_t stream);
+
+// bf16 -> binary16 (round to nearest even), n values, n % 8 == 0.
+hipError_t launch_cast_bf16_f16(const uint16_t* x, int64_t n, uint16_t* y, int num_cus, hipStream_t stream);
 
 // NVFP4 weight repack: megamoe_rm.cu layout (swizzled scales, optionally up
 // rows first) -> grouped_gemm_qnvfp4's, E experts of N rows and K columns.

@@ -87,6 +87,7 @@ moeq::GroupedArgs make_args(const int32_t* offsets, const int32_t* sorted, int64
   g.silu_mul = silu ? 1 : 0;
   g.act_limit = INFINITY;
   g.pair_weights = nullptr;
+  g.x_f16 = 0;
   g.out_kind = (int)od;
   g.out = out;
   g.sched = (int)sched;
@@ -175,7 +176,7 @@ moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int6
   return hip_status(moeq::launch_gemm_fp8(g, a, a_scale, w, w_scale, (hipStream_t)stream), fn);
 }
 
-moeq_status grouped_gemm_qnvfp4(const void* x, int64_t rows_a, moeq_arow a_row, const uint8_t* w,
+moeq_status grouped_gemm_qnvfp4(const void* x, moeq_dtype x_dtype, int64_t rows_a, moeq_arow a_row, const uint8_t* w,
                                 const uint8_t* w_sf, const float* w_gscale,
                                 const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
                                 int64_t P, int32_t topk, int32_t E, int64_t N, int64_t K,
@@ -186,6 +187,7 @@ moeq_status grouped_gemm_qnvfp4(const void* x, int64_t rows_a, moeq_arow a_row, 
   if (st != MOEQ_OK) return st;
   if (!w_sf || !w_gscale) return fail(MOEQ_EINVAL, "%s: null scale pointer", fn);
   if (!aligned(w_sf, 16) || !aligned(w_gscale, 4)) return fail(MOEQ_EALIGN, "%s: scales misaligned", fn);
+  if (x_dtype != MOEQ_BF16 && x_dtype != MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "%s: x dtype %d", fn, x_dtype);
   if (act != MOEQ_ACT_NONE && act != MOEQ_ACT_SILU_MUL && act != MOEQ_ACT_SILU_MUL_LIMIT)
     return fail(MOEQ_EUNSUPPORTED, "%s: act %d", fn, act);
   if (act == MOEQ_ACT_SILU_MUL_LIMIT && !(act_limit > 0.0f))
@@ -204,6 +206,7 @@ moeq_status grouped_gemm_qnvfp4(const void* x, int64_t rows_a, moeq_arow a_row, 
                                   act != MOEQ_ACT_NONE, out_dtype, out, sched);
   if (act == MOEQ_ACT_SILU_MUL_LIMIT) g.act_limit = act_limit;
   g.pair_weights = pair_weights;
+  g.x_f16 = x_dtype == MOEQ_F16 ? 1 : 0;
   return hip_status(moeq::launch_gemm_nvfp4(g, static_cast<const uint16_t*>(x), w, w_sf, w_gscale,
                                             (hipStream_t)stream),
                     fn);
@@ -249,6 +252,18 @@ moeq_status moe_sum_pairs(const void* y_pairs, moeq_dtype y_dtype, const int32_t
   return hip_status(moeq::launch_combine(y_pairs, (int)y_dtype, pair_to_sorted, nullptr, (int)T, topk, (int)N,
                                          T * (int64_t)topk, (int)out_dtype, out, (hipStream_t)stream),
                     fn);
+}
+
+moeq_status moe_cast_bf16_to_f16(const uint16_t* x, int64_t n, uint16_t* y, void* stream) {
+  const char* fn = "moe_cast_bf16_to_f16";
+  if (n < 0 || n >= (int64_t(1) << 40)) return fail(MOEQ_EINVAL, "%s: n=%lld out of range", fn, (long long)n);
+  if (n % 8 != 0) return fail(MOEQ_EALIGN, "%s: n=%lld must be a multiple of 8", fn, (long long)n);
+  if (n > 0 && (!x || !y)) return fail(MOEQ_EINVAL, "%s: null pointer", fn);
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(MOEQ_EALIGN, "%s: pointers must be 16-byte aligned", fn);
+  const uintptr_t a = (uintptr_t)x, b = (uintptr_t)y, nb = (uintptr_t)(2 * n);
+  if (n > 0 && a != b && a < b + nb && b < a + nb)
+    return fail(MOEQ_EINVAL, "%s: x and y overlap (only exact in-place is allowed)", fn);
+  return hip_status(moeq::launch_cast_bf16_f16(x, n, y, device_cus(), (hipStream_t)stream), fn);
 }
 
 moeq_status moe_quantize_int4(const void* x, moeq_dtype x_dtype, int64_t rows, int64_t K, uint8_t* q,

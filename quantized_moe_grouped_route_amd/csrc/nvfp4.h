@@ -49,6 +49,26 @@ __device__ __forceinline__ u32x4 dequant8_bf16_hi(u32 word, float scale) {
                hi_halves(p2.x * scale, p2.y * scale), hi_halves(p3.x * scale, p3.y * scale)};
 }
 
+// binary16 form, for binary16 activations.  Every E2M1 x UE4M3 product is
+// also a binary16 value (at most 6 significant bits, magnitudes in
+// [2^-10, 2688]), so the packed fp16 multiply is exact too; it halves the
+// VALU work of the fp32 form: per 8 codes, 4 conversions and 4 packed
+// multiplies.
+// Two UE4M3 scale bytes (bytes 0 and 1 of `two`) -> their binary16 values.
+__device__ __forceinline__ v2h ue4m3x2_f16(u32 two) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(two, 1.0f, false);
+}
+template <int SEL>
+__device__ __forceinline__ u32 e2m1x2_times(u32 word, v2h s2) {
+  const v2h p = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, SEL) * s2;
+  return __builtin_bit_cast(u32, p);
+}
+// 8 E2M1 codes (one word, elements 0..7) times the scale held twice in s2.
+__device__ __forceinline__ u32x4 dequant8_f16(u32 word, v2h s2) {
+  return u32x4{e2m1x2_times<0>(word, s2), e2m1x2_times<1>(word, s2), e2m1x2_times<2>(word, s2),
+               e2m1x2_times<3>(word, s2)};
+}
+
 // Packed pair of output elements of kind KIND (bf16 or f16) from two floats.
 template <int KIND>
 __device__ __forceinline__ u32 pack2(float lo, float hi) {

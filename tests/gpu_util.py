@@ -13,6 +13,11 @@ def dev(x: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(x).cuda()
 
 
+def dev_f16(bits: np.ndarray) -> torch.Tensor:
+    """binary16 bit patterns (uint16) -> float16 device tensor."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.float16)).cuda()
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.float().cpu().numpy().astype(np.float64)

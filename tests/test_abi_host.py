@@ -109,10 +109,10 @@ def test_fp8_rejects(L, kw, status):
 
 
 def _nvfp4(L, **kw):
-    a = dict(x=A16, rows=16, arow=0, w=A16, sf=A16, gs=A16, off=A16, srt=A16, P=16, topk=2, E=4,
-             N=256, K=256, act=0, lim=0.0, pw=None, od=mq.BF16, out=A16, sched=0)
+    a = dict(x=A16, xd=mq.BF16, rows=16, arow=0, w=A16, sf=A16, gs=A16, off=A16, srt=A16, P=16, topk=2,
+             E=4, N=256, K=256, act=0, lim=0.0, pw=None, od=mq.BF16, out=A16, sched=0)
     a.update(kw)
-    return L.grouped_gemm_qnvfp4(a["x"], a["rows"], a["arow"], a["w"], a["sf"], a["gs"], a["off"],
+    return L.grouped_gemm_qnvfp4(a["x"], a["xd"], a["rows"], a["arow"], a["w"], a["sf"], a["gs"], a["off"],
                                  a["srt"], a["P"], a["topk"], a["E"], a["N"], a["K"], a["act"],
                                  a["lim"], a["pw"], a["od"], a["out"], a["sched"], None)
 
@@ -124,7 +124,7 @@ def _nvfp4(L, **kw):
     (dict(act=2, lim=0.0), mq.EINVAL), (dict(act=2, lim=-1.0), mq.EINVAL),
     (dict(act=2, lim=float("nan")), mq.EINVAL),
     (dict(pw=A16, act=1), mq.EUNSUPPORTED), (dict(pw=A16, srt=None), mq.EINVAL),
-    (dict(pw=ODD), mq.EALIGN),
+    (dict(pw=ODD), mq.EALIGN), (dict(xd=mq.F32), mq.EUNSUPPORTED), (dict(xd=mq.I32), mq.EUNSUPPORTED),
 ])
 def test_nvfp4_rejects(L, kw, status):
     assert _nvfp4(L, **kw) == status
@@ -206,3 +206,13 @@ def _sum_pairs(L, **kw):
 ])
 def test_sum_pairs_rejects(L, kw, status):
     assert _sum_pairs(L, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=12), mq.EALIGN), (dict(n=-8), mq.EINVAL), (dict(x=None), mq.EINVAL), (dict(y=ODD), mq.EALIGN),
+    (dict(y=A16 + 16), mq.EINVAL),                       # partial overlap
+])
+def test_cast_rejects(L, kw, status):
+    a = dict(x=A16, n=64, y=0x20000)
+    a.update(kw)
+    assert L.moe_cast_bf16_to_f16(a["x"], a["n"], a["y"], None) == status

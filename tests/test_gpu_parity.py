@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from tests.gpu_util import dev, host, bf16_bits, assert_rows_close
+from tests.gpu_util import dev, dev_f16, host, bf16_bits, assert_rows_close
 
 pytestmark = pytest.mark.gpu
 
@@ -219,47 +219,63 @@ def test_fp8_decode_sorted_rows_and_empty_experts():
 
 
 # ------------------------------------------------------------------ NVFP4
+def _xin(x_bf16_bits, xdt):
+    """Activations for the GEMM in the form xdt ('bf16' or 'f16'): (device
+    tensor, the bits the oracle reads).  The f16 form is the oracle's
+    rounding of the bf16 values (exact for these inputs' magnitudes except
+    the rare |x| < 2^-14)."""
+    if xdt == "bf16":
+        return dev(x_bf16_bits), x_bf16_bits
+    bits = oracle.bf16_to_f16_bits(x_bf16_bits)
+    return dev_f16(bits), bits
+
+
+@pytest.mark.parametrize("xdt", ["bf16", "f16"])
 @pytest.mark.parametrize("sched", ["prefill", "decode"])
 @pytest.mark.parametrize("act", ["none", "silu_mul"])
-def test_nvfp4(sched, act):
+def test_nvfp4(sched, act, xdt):
     T, E, k, H, I = 150, 5, 2, 256, 128
     d = synth.nvfp4_moe(41, T, E, k, H, I, routing="repeat")
+    xg, xb = _xin(d["x"], xdt)
     offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
-    y = mq.grouped_gemm_qnvfp4(dev(d["x"]), dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k,
+    y = mq.grouped_gemm_qnvfp4(xg, dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k,
                                act=act, out_dtype=torch.float32, sched=sched)
-    ref = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], host(offs),
-                                     host(srt), k, act=act)["y"]
-    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 {sched} {act}")
+    ref = oracle.grouped_gemm_qnvfp4(xb, "token", d["w1"], d["s1"], d["g1"], host(offs),
+                                     host(srt), k, act=act, x_dtype=xdt)["y"]
+    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 {sched} {act} {xdt}")
 
 
+@pytest.mark.parametrize("xdt", ["bf16", "f16"])
 @pytest.mark.parametrize("sched", ["prefill", "decode"])
-def test_nvfp4_sorted_rows_full_code_range(sched):
+def test_nvfp4_sorted_rows_full_code_range(sched, xdt):
     # every scale byte 0x00..0x7E occurs; SORTED activation rows
     T, E, k, H, I = 64, 3, 2, 512, 128
     d = synth.nvfp4_moe(42, T, E, k, H, I, scale_lo=0x00, scale_hi=0x7E)
     offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
     P = T * k
-    xs = synth.normal_bf16(np.random.default_rng(1), (P, I))
-    y = mq.grouped_gemm_qnvfp4(dev(xs), dev(d["w2"]), dev(d["s2"]), dev(d["g2"]), offs, srt, k,
+    xg, xb = _xin(synth.normal_bf16(np.random.default_rng(1), (P, I)), xdt)
+    y = mq.grouped_gemm_qnvfp4(xg, dev(d["w2"]), dev(d["s2"]), dev(d["g2"]), offs, srt, k,
                                a_row="sorted", out_dtype=torch.float32, sched=sched)
-    ref = oracle.grouped_gemm_qnvfp4(xs, "sorted", d["w2"], d["s2"], d["g2"], host(offs),
-                                     host(srt), k)["y"]
-    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 sorted {sched}")
+    ref = oracle.grouped_gemm_qnvfp4(xb, "sorted", d["w2"], d["s2"], d["g2"], host(offs),
+                                     host(srt), k, x_dtype=xdt)["y"]
+    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 sorted {sched} {xdt}")
 
 
+@pytest.mark.parametrize("xdt", ["bf16", "f16"])
 @pytest.mark.parametrize("H", [1024, 1536, 2176, 3200])
-def test_nvfp4_decode_chunk_counts(H):
+def test_nvfp4_decode_chunk_counts(H, xdt):
     # K / 128 = 8, 12, 17, 25 weight chunks per lane: exactly the in-flight
     # depth, a partial refill, one steady pass plus a tail, several passes
     # plus a ragged tail.
     T, E, k, I = 20, 3, 2, 128
     d = synth.nvfp4_moe(45, T, E, k, H, I, routing="repeat")
+    xg, xb = _xin(d["x"], xdt)
     offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
-    y = mq.grouped_gemm_qnvfp4(dev(d["x"]), dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k,
+    y = mq.grouped_gemm_qnvfp4(xg, dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k,
                                act="silu_mul", out_dtype=torch.float32, sched="decode")
-    ref = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], host(offs),
-                                     host(srt), k, act="silu_mul")["y"]
-    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 decode H={H}")
+    ref = oracle.grouped_gemm_qnvfp4(xb, "token", d["w1"], d["s1"], d["g1"], host(offs),
+                                     host(srt), k, act="silu_mul", x_dtype=xdt)["y"]
+    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 decode H={H} {xdt}")
 
 
 @pytest.mark.parametrize("I", [64, 192])
@@ -277,18 +293,20 @@ def test_nvfp4_n_not_multiple_of_prefill_tile(I, sched):
     assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 N={2 * I} {sched}")
 
 
+@pytest.mark.parametrize("xdt", ["bf16", "f16"])
 @pytest.mark.parametrize("act", ["silu_mul", "none"])
-def test_nvfp4_decode_several_items_per_wave(act):
+def test_nvfp4_decode_several_items_per_wave(act, xdt):
     # More 4-row tiles x column blocks than the streaming schedule has waves,
     # so each wave runs several items back to back, with K / 512 = 3 (an odd
     # number of 4-chunk groups per item) and ragged last tiles.
     T, E, k, H, I = 203, 4, 2, 1536, 512
     d = synth.nvfp4_moe(47, T, E, k, H, I, routing="repeat")
+    xg, xb = _xin(d["x"], xdt)
     offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
-    y = mq.grouped_gemm_qnvfp4(dev(d["x"]), dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k,
+    y = mq.grouped_gemm_qnvfp4(xg, dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k,
                                act=act, out_dtype=torch.float32, sched="decode")
-    ref = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], host(offs),
-                                     host(srt), k, act=act)["y"]
+    ref = oracle.grouped_gemm_qnvfp4(xb, "token", d["w1"], d["s1"], d["g1"], host(offs),
+                                     host(srt), k, act=act, x_dtype=xdt)["y"]
     assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 decode many items {act}")
 
 
@@ -537,3 +555,45 @@ def test_nvfp4_layer_with_fc2_pair_epilogue(sched):
                                 sched=sched)
     out2 = mq.moe_scatter_combine(ys, p2s, tw)
     assert_rows_close(host(out2), ref, what=f"layer, sorted FC2 {sched}")
+
+
+
+def test_cast_bf16_to_f16_every_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    x = dev(bits)
+    y = mq.cast_bf16_to_f16(x)
+    got = host(y.view(torch.int16)).view(np.uint16)
+    ref = oracle.bf16_to_f16_bits(bits)
+    nan = np.isnan(oracle.bf16_value(bits))
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all(np.isnan(oracle.f16_value(got[nan])))
+    # in place, on a 2-D tensor whose size is not a multiple of the 2048
+    # values one workgroup converts
+    x2 = dev(bits[: 8 * 1000].reshape(80, 100))
+    mq.cast_bf16_to_f16(x2, out=x2.view(torch.float16))
+    got2 = host(x2.view(torch.int16)).reshape(-1).view(np.uint16)
+    assert np.array_equal(got2[~nan[:8000]], ref[:8000][~nan[:8000]])
+
+
+@pytest.mark.parametrize("sched", ["prefill", "decode"])
+def test_nvfp4_f16_layer_with_gpu_cast(sched):
+    # bf16 x -> GPU cast -> FC1 (f16, SiLU, f16 h) -> FC2 (f16) -> combine:
+    # megamoe_rm.cu's fp16 activation path, against the oracle step by step
+    T, E, k, H, I = 100, 4, 2, 512, 256
+    d = synth.nvfp4_moe(65, T, E, k, H, I, routing="repeat")
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    xh = mq.cast_bf16_to_f16(dev(d["x"]))
+    xb = oracle.bf16_to_f16_bits(d["x"])
+    assert np.array_equal(host(xh.view(torch.int16)).view(np.uint16), xb)
+    h = mq.grouped_gemm_qnvfp4(xh, dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k, act="silu_mul",
+                               out_dtype=torch.float16, sched=sched)
+    ref_h = oracle.grouped_gemm_qnvfp4(xb, "token", d["w1"], d["s1"], d["g1"], host(offs), host(srt), k,
+                                       act="silu_mul", x_dtype="f16")["y"]
+    n = ref_h.shape[0]
+    assert_rows_close(host(h)[:n], ref_h, what=f"f16 FC1 {sched}")
+    y = mq.grouped_gemm_qnvfp4(h, dev(d["w2"]), dev(d["s2"]), dev(d["g2"]), offs, srt, k, a_row="sorted",
+                               sched=sched)
+    hb = host(h.view(torch.int16)).view(np.uint16)
+    ref_y = oracle.grouped_gemm_qnvfp4(hb, "sorted", d["w2"], d["s2"], d["g2"], host(offs), host(srt), k,
+                                       x_dtype="f16")["y"]
+    assert_rows_close(host(y)[:n], ref_y, what=f"f16 FC2 {sched}")

@@ -19,9 +19,9 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def _run(idx, fc2="sorted"):
+def _run(idx, fc2="sorted", act="f16"):
     import bench
-    wl = bench.Workload(idx, fc2)
+    wl = bench.Workload(idx, fc2, act)
     wl.step()
     torch.cuda.synchronize()
     return wl
@@ -79,12 +79,19 @@ def _nvfp4_checks(wl, n_per):
     off, srt, p2s, _ = _check_route(wl)
     d = wl.d
     rows = _sample_rows(off, n_per=n_per)
-    h_ref = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], off, srt, d["k"],
-                                       act="silu_mul", rows=rows)["y"]
+    xdt = wl.act
+    if xdt == "f16":
+        xb = oracle.bf16_to_f16_bits(d["x"])
+        assert np.array_equal(host(wl.xh.view(torch.int16)).view(np.uint16), xb)
+    else:
+        xb = d["x"]
+    h_ref = oracle.grouped_gemm_qnvfp4(xb, "token", d["w1"], d["s1"], d["g1"], off, srt, d["k"],
+                                       act="silu_mul", rows=rows, x_dtype=xdt)["y"]
     assert_rows_close(host(wl.h)[rows], h_ref, what="FC1 h")
-    hb = bf16_bits(wl.h)      # FC2 consumes the GPU's h (per-call parity)
+    # FC2 consumes the GPU's h (per-call parity)
+    hb = host(wl.h.view(torch.int16)).view(np.uint16) if xdt == "f16" else bf16_bits(wl.h)
     y_ref = oracle.grouped_gemm_qnvfp4(hb, "sorted", d["w2"], d["s2"], d["g2"], off, srt, d["k"],
-                                       rows=rows)["y"]
+                                       rows=rows, x_dtype=xdt)["y"]
     assert_rows_close(host(wl.y)[rows], y_ref, what="FC2 y")
     out_ref = oracle.scatter_combine(host(wl.y), p2s, d["topk_weights"])
     assert_rows_close(host(wl.out), out_ref, what="combine")
@@ -99,6 +106,12 @@ def test_workload3_nvfp4_prefill_zipf():
     sizes = np.diff(host(wl.route_out[0]))
     assert sizes.min() == 0 and sizes.max() > 1000      # skewed, with empty experts
     _nvfp4_checks(wl, n_per=2)
+
+
+@pytest.mark.parametrize("idx", [2, 3])
+def test_nvfp4_workloads_with_bf16_activations(idx):
+    wl = _run(idx, act="bf16")
+    _nvfp4_checks(wl, n_per=1 if idx == 2 else 2)
 
 
 @pytest.mark.parametrize("idx", [2, 3])
