@@ -16,6 +16,12 @@ processing, which that kernel reads in place:
 The repack below turns that layout into the library's linear one
 ([R][C] row-major scales, gate rows first when asked), one-shot, before the
 GEMMs run (SURVEY's cheapest path for the layout compatibility item).
+
+The library also reads a second scale layout of its own, "K-quad major":
+for each group of 4 consecutive block columns (a quad, 64 values of K),
+the 4 scale bytes of every row, rows consecutive: s_q[e, j, n, i] =
+s[e, n, 4j + i], stored [E][C/4][R][4].  One K step of 64 then finds the
+scales of many consecutive rows in one contiguous run.
 """
 import numpy as np
 
@@ -53,11 +59,28 @@ def swizzle_scales(s_lin: np.ndarray) -> np.ndarray:
     return out
 
 
-def repack_nvfp4(w: np.ndarray, s_swz: np.ndarray, swap_halves: bool):
+def quads_from_rows(s_lin: np.ndarray) -> np.ndarray:
+    """[.., R, C] row-major scales -> [.., C/4, R, 4] K-quad-major bytes."""
+    lead, (R, C) = s_lin.shape[:-2], s_lin.shape[-2:]
+    if C % 4:
+        raise ValueError("the quad layout needs C % 4 == 0")
+    q = np.asarray(s_lin).reshape(lead + (R, C // 4, 4))
+    return np.ascontiguousarray(np.swapaxes(q, -3, -2))
+
+
+def rows_from_quads(s_q: np.ndarray) -> np.ndarray:
+    """[.., C/4, R, 4] K-quad-major -> [.., R, C] row-major (the inverse)."""
+    lead, (Q, R, four) = s_q.shape[:-3], s_q.shape[-3:]
+    assert four == 4
+    return np.ascontiguousarray(np.swapaxes(np.asarray(s_q), -3, -2)).reshape(lead + (R, 4 * Q))
+
+
+def repack_nvfp4(w: np.ndarray, s_swz: np.ndarray, swap_halves: bool, out_layout: str = "rows"):
     """Weights w [E][R][K/2] and swizzled scales s_swz [E][R*K/16] in the
     megamoe_rm.cu layout -> (w_lin [E][R][K/2], s_lin [E][R][K/16]) in the
     library's layout.  swap_halves: the matrix is a w13 (up rows first); the
-    output puts the gate rows [R/2, R) first, then the up rows [0, R/2)."""
+    output puts the gate rows [R/2, R) first, then the up rows [0, R/2).
+    out_layout 'rows' returns scales [E][R][K/16], 'quads' [E][K/64][R][4]."""
     E, R, KB = w.shape
     C = KB // 8                                        # K/16 blocks = (K/2 bytes) / 8
     s_lin = unswizzle_scales(s_swz, R, C)
@@ -66,5 +89,11 @@ def repack_nvfp4(w: np.ndarray, s_swz: np.ndarray, swap_halves: bool):
             raise ValueError("swap_halves needs an even row count")
         h = R // 2
         order = np.concatenate([np.arange(h, R), np.arange(0, h)])
-        return w[:, order, :], s_lin[:, order, :]
-    return w.copy(), s_lin
+        w_out, s_out = w[:, order, :], s_lin[:, order, :]
+    else:
+        w_out, s_out = w.copy(), s_lin
+    if out_layout == "quads":
+        return w_out, quads_from_rows(s_out)
+    if out_layout != "rows":
+        raise ValueError(out_layout)
+    return w_out, s_out

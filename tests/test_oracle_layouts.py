@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
+import synth
 from oracle import layouts
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "nvfp4_scale_swizzle_offsets.txt")
@@ -92,3 +93,34 @@ def test_repacked_silu_layer_matches_the_page_layout_brute_force():
             g, u = acc["gate"], acc["up"]
             want = g / (1 + np.exp(-g)) * u
             assert abs(h[t, j] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+def test_quad_layout_hand_worked_offsets():
+    # R=3 rows, C=8 block columns: byte (n, c) of the row-major matrix sits
+    # at ((c // 4) * R + n) * 4 + c % 4 of the quad-major one
+    R, C = 3, 8
+    s = np.arange(R * C, dtype=np.uint8).reshape(1, R, C)           # value = n*C + c
+    q = oracle.quads_from_rows(s).reshape(-1)
+    for n, c in [(0, 0), (0, 5), (2, 3), (1, 7), (2, 4)]:
+        assert q[((c // 4) * R + n) * 4 + c % 4] == n * C + c
+    assert list(q[:12]) == [0, 1, 2, 3, 8, 9, 10, 11, 16, 17, 18, 19]  # quad 0 of rows 0, 1, 2
+    assert np.array_equal(oracle.rows_from_quads(oracle.quads_from_rows(s)), s)
+
+
+def test_repack_to_quads_and_gemm_on_quads():
+    rng = np.random.default_rng(5)
+    E, R, K = 2, 256, 128
+    w = rng.integers(0, 256, (E, R, K // 2), dtype=np.uint8)
+    s_lin = rng.integers(0x30, 0x48, (E, R, K // 16), dtype=np.uint8)
+    s_swz = oracle.swizzle_scales(s_lin)
+    w_r, s_r = oracle.repack_nvfp4(w, s_swz, True)
+    w_q, s_q = oracle.repack_nvfp4(w, s_swz, True, out_layout="quads")
+    assert np.array_equal(w_q, w_r) and s_q.shape == (E, K // 64, R, 4)
+    assert np.array_equal(oracle.rows_from_quads(s_q), s_r)
+    # the GEMM reads the quad layout as the same scales
+    x = synth.normal_bf16(rng, (5, K))
+    off = np.array([0, 3, 5], np.int32)
+    g = np.ones(E, np.float32)
+    y_r = oracle.grouped_gemm_qnvfp4(x, "sorted", w_r, s_r, g, off, None, 1)["y"]
+    y_q = oracle.grouped_gemm_qnvfp4(x, "sorted", w_q, s_q, g, off, None, 1, sf_layout="quads")["y"]
+    assert np.array_equal(y_r, y_q)
