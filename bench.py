@@ -82,11 +82,11 @@ def _traffic(kernel_tag, sources):
 class Workload:
     """Device buffers and the launch sequence of one step."""
 
-    def __init__(self, idx: int, fc2: str = "sorted", act: str = "f16"):
+    def __init__(self, idx: int, fc2: str = "sorted", act: str = "f16", sfl: str = "quads"):
         import torch
         import synth
         import quantized_moe_grouped_route_amd as mq
-        self.mq, self.idx, self.fc2, self.act = mq, idx, fc2, act
+        self.mq, self.idx, self.fc2, self.act, self.sfl = mq, idx, fc2, act, sfl
         self.cfg = synth.WORKLOADS[idx]
         self.d = d = synth.workload(idx)
         if self.cfg["kind"] == "repack":
@@ -145,8 +145,14 @@ class Workload:
         else:  # nvfp4
             H, I = d["H"], d["I"]
             self.x = _dev(d["x"])
-            self.w1, self.s1, self.g1 = _dev(d["w1"]), _dev(d["s1"]), _dev(d["g1"])
-            self.w2, self.s2, self.g2 = _dev(d["w2"]), _dev(d["s2"]), _dev(d["g2"])
+            # Scales in the library's K-quad-major layout by default: the seeded
+            # bytes are iid, so they are read directly in that stored order.
+            self.s1_host, self.s2_host = d["s1"], d["s2"]
+            if sfl == "quads":
+                self.s1_host = d["s1"].reshape(E, H // 64, 2 * I, 4)
+                self.s2_host = d["s2"].reshape(E, I // 64, H, 4)
+            self.w1, self.s1, self.g1 = _dev(d["w1"]), _dev(self.s1_host), _dev(d["g1"])
+            self.w2, self.s2, self.g2 = _dev(d["w2"]), _dev(self.s2_host), _dev(d["g2"])
             hdt = torch.float16 if act == "f16" else torch.bfloat16
             self.xh = torch.empty(T, H, dtype=torch.float16, device="cuda") if act == "f16" else None
             self.h = torch.empty(P, I, dtype=hdt, device="cuda")
@@ -527,6 +533,9 @@ def main():
     ap.add_argument("--act", choices=("bf16", "f16"), default="f16",
                     help="NVFP4 workloads: GEMMs on the bf16 activations, or on binary16 activations "
                          "(the bf16 input cast once, h kept in binary16; half the dequant work)")
+    ap.add_argument("--sf-layout", choices=("rows", "quads"), default="quads",
+                    help="NVFP4 workloads: block scales row-major [E][N][K/16] or K-quad-major "
+                         "[E][K/64][N][4] (the library's layout for the tiled schedule)")
     ap.add_argument("--fc2", choices=("sorted", "pair"), default="sorted",
                     help="NVFP4 workloads: FC2 writes sorted rows and the combine applies the top-k "
                          "weights (sorted), or FC2's epilogue applies them and writes pair-ordered "
@@ -563,7 +572,7 @@ def main():
         print(json.dumps({"copy_bytes_read_per_launch": src.numel() * 4,
                           "copy_bytes_written_per_launch": dst.numel() * 4}), flush=True)
         return
-    wl = Workload(args.workload, args.fc2, args.act)
+    wl = Workload(args.workload, args.fc2, args.act, args.sf_layout)
     torch.cuda.synchronize()
     host_s = []
     for _ in range(args.warmup):
@@ -618,6 +627,7 @@ def main():
     if cfg["kind"] == "nvfp4":
         config["fc2_epilogue"] = args.fc2
         config["activations"] = args.act
+        config["scale_layout"] = args.sf_layout
     if args.workload in (2, 6):
         config["active_experts"] = wl.active
         config["weight_bytes"] = wl.weight_bytes

@@ -78,6 +78,17 @@ typedef enum { MOEQ_ACT_NONE = 0, MOEQ_ACT_SILU_MUL = 1, MOEQ_ACT_SILU_MUL_LIMIT
 
 typedef enum { MOEQ_AROW_TOKEN = 0, MOEQ_AROW_SORTED = 1 } moeq_arow;
 
+/* Layout of NVFP4 block scales (C = K/16 per row).
+ * MOEQ_SF_ROWS   [E][N][C] row-major, the layout of [TLK].
+ * MOEQ_SF_KQUADS [E][C/4][N][4]: for each group of 4 block columns (64
+ *                values of K), the 4 scale bytes of every row, rows
+ *                consecutive.  A K step of 64 finds the scales of
+ *                consecutive weight rows in one contiguous run, which the
+ *                tiled schedule fetches as whole cache lines; byte (n, c) is
+ *                at ((c/4)*N + n)*4 + c%4 within an expert.
+ * moe_nvfp4_repack produces either one. */
+typedef enum { MOEQ_SF_ROWS = 0, MOEQ_SF_KQUADS = 1 } moeq_sf_layout;
+
 /* Schedule hint for the grouped GEMMs.  Both schedules compute the same
  * result for every input; AUTO picks by the average rows per expert
  * (P / E): the weight-streaming DECODE schedule for few rows per expert,
@@ -185,11 +196,11 @@ moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int6
  *             multiplied in fp16, at half the dequantization work; see
  *             moe_cast_bf16_to_f16)
  *   w         uint8 [E][N][K/2]       E2M1 codes
- *   w_sf      uint8 [E][N][K/16]      UE4M3 block scales (sign bit clear;
- *                                     0x7F is not a valid scale).  [TLK]'s
- *                                     uint32 [E][N][K/64] packing (block
- *                                     4g+j in bits 8j..8j+7 of word g) is
- *                                     the same bytes and may be passed as is
+ *   w_sf      uint8 UE4M3 block scales (sign bit clear; 0x7F is not a
+ *             valid scale) in sf_layout: [E][N][K/16] (ROWS) or
+ *             [E][K/64][N][4] (KQUADS, faster for the tiled schedule).
+ *             [TLK]'s uint32 [E][N][K/64] packing (block 4g+j in bits
+ *             8j..8j+7 of word g) is the ROWS bytes and may be passed as is
  *   w_gscale  f32   [E]               per-expert global scale
  *   act       NONE, SILU_MUL, or SILU_MUL_LIMIT with act_limit (host f32,
  *             > 0, +inf allowed; ignored for the other acts; a NaN, zero
@@ -211,7 +222,8 @@ moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int6
  * N % 256 != 0 falls back to it as well.
  * ---------------------------------------------------------------------- */
 moeq_status grouped_gemm_qnvfp4(const void* x, moeq_dtype x_dtype, int64_t rows_a, moeq_arow a_row,
-                                const uint8_t* w, const uint8_t* w_sf, const float* w_gscale,
+                                const uint8_t* w, const uint8_t* w_sf, moeq_sf_layout sf_layout,
+                                const float* w_gscale,
                                 const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
                                 int64_t P, int32_t topk, int32_t E, int64_t N, int64_t K,
                                 moeq_act act, float act_limit, const float* pair_weights,
@@ -303,9 +315,11 @@ moeq_status moe_sum_pairs(const void* y_pairs, moeq_dtype y_dtype, const int32_t
  *                1: the matrix is a w13 with the up rows [0, N/2) first
  *                   and the gate rows [N/2, N) second; the output puts the
  *                   gate rows first, the order of MOEQ_ACT_SILU_MUL
+ *   out_layout   MOEQ_SF_ROWS or MOEQ_SF_KQUADS: the layout of sf_out
  *   w_out   uint8 [E][N][K/2]   out: row n = input row n (swap 0) or
  *                               (n + N/2) mod N (swap 1)
- *   sf_out  uint8 [E][N][K/16]  out: row-major scales, rows as w_out
+ *   sf_out  uint8 [E][N*K/16]   out: the scales in out_layout, rows as
+ *                               w_out
  * A pure byte permutation: the outputs are bit-exact copies of input bytes.
  * Requires 1 <= E <= 1024, N % 128 == 0 and K % 64 == 0 (else MOEQ_EALIGN),
  * N*K < 2^36, all four pointers non-NULL and 16-byte aligned, and the two
@@ -313,7 +327,8 @@ moeq_status moe_sum_pairs(const void* y_pairs, moeq_dtype y_dtype, const int32_t
  * MOEQ_EINVAL).  The per-expert global scale needs no repack.
  * ---------------------------------------------------------------------- */
 moeq_status moe_nvfp4_repack(const uint8_t* w_in, const uint8_t* sf_in, int64_t E, int64_t N, int64_t K,
-                             int32_t swap_halves, uint8_t* w_out, uint8_t* sf_out, void* stream);
+                             int32_t swap_halves, moeq_sf_layout out_layout, uint8_t* w_out,
+                             uint8_t* sf_out, void* stream);
 
 #ifdef __cplusplus
 }

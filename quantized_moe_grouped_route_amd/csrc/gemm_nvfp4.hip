@@ -75,7 +75,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale,
     const int* __restrict__ offsets, const int* __restrict__ sorted_ids, int topk, int E, int P, int N,
-    int K, void* __restrict__ out, float limit, const float* __restrict__ pair_w) {
+    int K, void* __restrict__ out, float limit, const float* __restrict__ pair_w, int sf_quads) {
   static_assert(!(SILU && PAIR), "pair-ordered output is for act NONE");
   using namespace pf;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
@@ -127,7 +127,13 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
       const int rb = 64 * wn + 32 * j + (lane >> 1);
       pb[j] = w + grow(rb) * wrow_bytes + (((lane & 1) ^ ((rb >> 3) & 1)) << 4);
     }
-    const uint8_t* ps = w_sf + grow(64 * wn + lane) * srow_bytes;
+    // S: row 64wn + lane, its 4 scale bytes of the K step.  Row-major
+    // scales: 4 bytes at row stride K/16; K-quad-major ([K/64][N][4]): the
+    // step's bytes of consecutive rows are consecutive (a whole-line copy).
+    const int64_t s_row = grow(64 * wn + lane);
+    const uint8_t* ps = sf_quads ? w_sf + (int64_t)t.e * N * srow_bytes + (s_row - (int64_t)t.e * N) * 4
+                                 : w_sf + s_row * srow_bytes;
+    const int64_t s_step = sf_quads ? (int64_t)N * 4 : 4;
     const uint32_t lds_a = lds_addr(smem + wn * 4096);
     const uint32_t lds_b = lds_addr(smem + kABytes + wn * 2048);
     const uint32_t lds_s = lds_addr(smem + kABytes + kBBytes + wn * 256);
@@ -137,7 +143,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
       for (int j = 0; j < 4; ++j) dma16(pa[j] + (int64_t)g * 128, lds_a + st + j * 1024);
 #pragma unroll
       for (int j = 0; j < 2; ++j) dma16(pb[j] + (int64_t)g * 32, lds_b + st + j * 1024);
-      dma4(ps + (int64_t)g * 4, lds_s + st);
+      dma4(ps + (int64_t)g * s_step, lds_s + st);
     };
     constexpr int kPer = 7;  // loads per wave per stage
 
@@ -385,7 +391,7 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale, const int* __restrict__ offsets,
     const int* __restrict__ sorted_ids, int topk, int E, int P, int N, int K, void* __restrict__ out,
-    float limit, const float* __restrict__ pair_w) {
+    float limit, const float* __restrict__ pair_w, int sf_quads) {
   static_assert(!(SILU && PAIR), "pair-ordered output is for act NONE");
   constexpr int CPS = dc::cps<WIDE>();
   constexpr int D = dc::depth<WIDE>();
@@ -413,6 +419,8 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
   const int steps = K / (128 * CPS);                                 // per item
   const int nq = ((total - wid + active - 1) / active) * steps;     // steps of this wave
   const int64_t wrow = K / 2, srow = K / 16;
+  // scale bytes per copy step: a superchunk (WIDE, 8 quads) or a step (2 quads)
+  const int64_t s_adv = sf_quads ? (WIDE ? 8 : 2) * (int64_t)N * 4 : (WIDE ? 32 : 8);
   const int g = lane >> 4, l16 = lane & 15;
   uint8_t* myring = ring + wv * kWave;
   const uint32_t lb = lds_addr(myring);
@@ -463,7 +471,18 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
     }
     // scales: lane -> weight group lane/32, row (lane/2)%16, half lane%2
     const int sr = (lane >> 1) & 15;
-    ss = w_sf + (e0 + ((lane >> 5) ? b1 : b0) + sr) * srow + (lane & 1) * (WIDE ? 16 : 4);
+    if (sf_quads) {
+      // K-quad-major scales, LDS [group][quad][16 rows][4 bytes].  WIDE:
+      // lane -> group lane/32, quad (lane/4)%8 of the superchunk, rows
+      // 4(lane%4) .. +3 (16 bytes); otherwise lane -> group lane/32, quad
+      // (lane/16)%2 of the step, row lane%16 (4 bytes).
+      const int gb = (lane >> 5) ? b1 : b0;
+      const int64_t eb = (int64_t)t.e * N * srow;
+      ss = WIDE ? w_sf + eb + ((lane >> 2) & 7) * (int64_t)N * 4 + (int64_t)(gb + 4 * (lane & 3)) * 4
+                : w_sf + eb + ((lane >> 4) & 1) * (int64_t)N * 4 + (int64_t)(gb + (lane & 15)) * 4;
+    } else {
+      ss = w_sf + (e0 + ((lane >> 5) ? b1 : b0) + sr) * srow + (lane & 1) * (WIDE ? 16 : 4);
+    }
   };
   uint32_t ops_ring = 0;  // copies issued per slot, 4 bits each
   auto issue = [&](int slot) __attribute__((always_inline)) {
@@ -474,7 +493,7 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
       if ((is_st & 1) == 0) {  // first step of a superchunk
         const int bsel = is_sc & 1;
         const int64_t sc = is_st >> 1;
-        dma16(ss + sc * 32, lsb + bsel * 1024);
+        dma16(ss + sc * s_adv, lsb + bsel * 1024);
         const uint8_t* xs = reinterpret_cast<const uint8_t*>(x) + sc * 1024;
         for (int r = 0; r < is_rows; ++r) dma16(xs + xrow[r], lxb + bsel * 4096 + r * 1024);
         ops += 1 + is_rows;
@@ -491,7 +510,7 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
       dma16(wsrc[0] + o, l);
       dma16(wsrc[2] + o, l + 1024);
       dma16(sx + (int64_t)is_st * 256, l + 2048);
-      dma4(ss + (int64_t)is_st * 8, l + 3072);
+      dma4(ss + (int64_t)is_st * s_adv, l + 3072);
     }
     ops_ring = (ops_ring & ~(15u << (4 * slot))) | ((uint32_t)ops << (4 * slot));
     if (++is_st == steps) {
@@ -533,7 +552,8 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           xv[cp][j] = *reinterpret_cast<const u32x4*>(xb + (((16 * cc + 4 * g + j) ^ xr) << 4));
-        const uint8_t* sb = sbuf + cbuf * 1024 + l16 * 32 + cc * 8 + 2 * g;
+        const uint8_t* sb = sbuf + cbuf * 1024 +
+                            (sf_quads ? (2 * cc + (g >> 1)) * 64 + l16 * 4 + 2 * (g & 1) : l16 * 32 + cc * 8 + 2 * g);
         q0[cp] = *reinterpret_cast<const uint16_t*>(sb);
         q1[cp] = *reinterpret_cast<const uint16_t*>(sb + 512);
       }
@@ -543,8 +563,9 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         xv[0][j] = *reinterpret_cast<const u32x4*>(sp + 2048 + xr * 256 + (((4 * g + j) ^ xr) << 4));
-      q0[0] = *reinterpret_cast<const uint16_t*>(sp + 3072 + l16 * 8 + 2 * g);
-      q1[0] = *reinterpret_cast<const uint16_t*>(sp + 3072 + 128 + l16 * 8 + 2 * g);
+      const int so = sf_quads ? (g >> 1) * 64 + l16 * 4 + 2 * (g & 1) : l16 * 8 + 2 * g;
+      q0[0] = *reinterpret_cast<const uint16_t*>(sp + 3072 + so);
+      q1[0] = *reinterpret_cast<const uint16_t*>(sp + 3072 + 128 + so);
     }
     // the slot is refilled once its reads have landed
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -618,18 +639,18 @@ hipError_t go(const GroupedArgs& g, bool decode, const uint16_t* x, const uint8_
     if (g.K % 512 == 0)
       hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, true, PAIR, H16>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
                          g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N,
-                         g.K, g.out, g.act_limit, g.pair_weights);
+                         g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads);
     else
       hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, false, PAIR, H16>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
                          g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N,
-                         g.K, g.out, g.act_limit, g.pair_weights);
+                         g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads);
   } else {
     const int64_t mt_ub = (g.P + pf::kM - 1) / pf::kM + std::min<int64_t>(g.E, g.P);
     const int64_t items_ub = mt_ub * (g.N / pf::kN);
     const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus * 2);
     hipLaunchKernelGGL((nvfp4_prefill<OUT, SILU, PAIR, H16>), dim3(grid), dim3(pf::kThreads), 0, stream, x,
                        g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P,
-                       g.N, g.K, g.out, g.act_limit, g.pair_weights);
+                       g.N, g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads);
   }
   return hipGetLastError();
 }

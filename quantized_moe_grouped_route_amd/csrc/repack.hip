@@ -2,7 +2,7 @@
 // reads in place (the header comment of that file and its scale_off
 // function: w13 with the up rows first, UE4M3 block scales in 128x4 swizzled
 // tiles) into the layout of grouped_gemm_qnvfp4 (gate rows first, scales
-// [N][K/16] row-major).
+// [N][K/16] row-major, or K-quad-major [K/64][N][4 bytes]).
 //
 // Weights.  With the halves swapped, output rows [0, R/2) of an expert are
 // input rows [R/2, R) and the other way round; both halves are contiguous,
@@ -41,6 +41,7 @@ struct RepackArgs {
   uint32_t quads;       // 4-byte scale words per linear row = K / 64
   uint32_t groups;      // workgroups per 128-row block on the scales
   uint32_t half_rows;   // R / 2 when the halves swap, else 0
+  uint32_t out_quads;   // scales out as [K/64][R][4 bytes] (else [R][K/16])
 };
 
 __device__ __forceinline__ void weights_part(const RepackArgs& a, uint32_t bx) {
@@ -73,6 +74,21 @@ __device__ __forceinline__ void scales_part(const RepackArgs& a, uint32_t bx, ui
     }
   }
   __syncthreads();
+  if (a.out_quads) {
+    // quad-major: a quad's words of consecutive rows are consecutive, so
+    // 128 consecutive lanes write one quad's 128 rows (512 bytes)
+#pragma unroll
+    for (int u = 0; u < 128 * kTilesPerGroup / kThreads; ++u) {
+      const uint32_t m = threadIdx.x + u * kThreads;
+      const uint32_t col = m >> 7, row = m & 127;
+      if (cq0 + col < a.quads) {
+        uint32_t r = rb * 128 + row + a.half_rows;
+        if (r >= a.R) r -= a.R;
+        __builtin_nontemporal_store(t[row * kLdsStride + col], d + (size_t)(cq0 + col) * a.R + r);
+      }
+    }
+    return;
+  }
   // 128 rows x 16 words; 16 consecutive lanes write one row's words.
 #pragma unroll
   for (int u = 0; u < 128 * kTilesPerGroup / kThreads; ++u) {
@@ -99,7 +115,8 @@ __global__ __launch_bounds__(kThreads) void repack_nvfp4(RepackArgs a) {
 }  // namespace
 
 hipError_t launch_repack_nvfp4(const uint8_t* w_in, const uint8_t* sf_in, int64_t E, int64_t N, int64_t K,
-                               int swap_halves, uint8_t* w_out, uint8_t* sf_out, hipStream_t stream) {
+                               int swap_halves, int out_quads, uint8_t* w_out, uint8_t* sf_out,
+                               hipStream_t stream) {
   RepackArgs a;
   a.w_in = reinterpret_cast<const u32x4*>(w_in);
   a.w_out = reinterpret_cast<u32x4*>(w_out);
@@ -112,6 +129,7 @@ hipError_t launch_repack_nvfp4(const uint8_t* w_in, const uint8_t* sf_in, int64_
   a.quads = (uint32_t)(K / 64);
   a.groups = (a.quads + kTilesPerGroup - 1) / kTilesPerGroup;
   a.half_rows = swap_halves ? a.R / 2 : 0u;
+  a.out_quads = out_quads ? 1u : 0u;
   const uint32_t sblocks = (a.R / 128) * a.groups;
   hipLaunchKernelGGL(repack_nvfp4, dim3(a.wblocks + sblocks, (uint32_t)E), dim3(kThreads), 0, stream, a);
   return hipGetLastError();

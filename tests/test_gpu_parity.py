@@ -230,19 +230,27 @@ def _xin(x_bf16_bits, xdt):
     return dev_f16(bits), bits
 
 
+def _sf(s_rows, sfl):
+    """Scales in layout sfl ('rows' or 'quads'): (device tensor, oracle array)."""
+    a = s_rows if sfl == "rows" else oracle.quads_from_rows(s_rows)
+    return dev(a), a
+
+
+@pytest.mark.parametrize("sfl", ["rows", "quads"])
 @pytest.mark.parametrize("xdt", ["bf16", "f16"])
 @pytest.mark.parametrize("sched", ["prefill", "decode"])
 @pytest.mark.parametrize("act", ["none", "silu_mul"])
-def test_nvfp4(sched, act, xdt):
+def test_nvfp4(sched, act, xdt, sfl):
     T, E, k, H, I = 150, 5, 2, 256, 128
     d = synth.nvfp4_moe(41, T, E, k, H, I, routing="repeat")
     xg, xb = _xin(d["x"], xdt)
+    sg, sa = _sf(d["s1"], sfl)
     offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
-    y = mq.grouped_gemm_qnvfp4(xg, dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k,
+    y = mq.grouped_gemm_qnvfp4(xg, dev(d["w1"]), sg, dev(d["g1"]), offs, srt, k,
                                act=act, out_dtype=torch.float32, sched=sched)
-    ref = oracle.grouped_gemm_qnvfp4(xb, "token", d["w1"], d["s1"], d["g1"], host(offs),
-                                     host(srt), k, act=act, x_dtype=xdt)["y"]
-    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 {sched} {act} {xdt}")
+    ref = oracle.grouped_gemm_qnvfp4(xb, "token", d["w1"], sa, d["g1"], host(offs),
+                                     host(srt), k, act=act, x_dtype=xdt, sf_layout=sfl)["y"]
+    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 {sched} {act} {xdt} {sfl}")
 
 
 @pytest.mark.parametrize("xdt", ["bf16", "f16"])
@@ -261,20 +269,21 @@ def test_nvfp4_sorted_rows_full_code_range(sched, xdt):
     assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 sorted {sched} {xdt}")
 
 
-@pytest.mark.parametrize("xdt", ["bf16", "f16"])
+@pytest.mark.parametrize("xdt,sfl", [("bf16", "rows"), ("f16", "rows"), ("f16", "quads")])
 @pytest.mark.parametrize("H", [1024, 1536, 2176, 3200])
-def test_nvfp4_decode_chunk_counts(H, xdt):
+def test_nvfp4_decode_chunk_counts(H, xdt, sfl):
     # K / 128 = 8, 12, 17, 25 weight chunks per lane: exactly the in-flight
     # depth, a partial refill, one steady pass plus a tail, several passes
     # plus a ragged tail.
     T, E, k, I = 20, 3, 2, 128
     d = synth.nvfp4_moe(45, T, E, k, H, I, routing="repeat")
     xg, xb = _xin(d["x"], xdt)
+    sg, sa = _sf(d["s1"], sfl)
     offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
-    y = mq.grouped_gemm_qnvfp4(xg, dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k,
+    y = mq.grouped_gemm_qnvfp4(xg, dev(d["w1"]), sg, dev(d["g1"]), offs, srt, k,
                                act="silu_mul", out_dtype=torch.float32, sched="decode")
-    ref = oracle.grouped_gemm_qnvfp4(xb, "token", d["w1"], d["s1"], d["g1"], host(offs),
-                                     host(srt), k, act="silu_mul", x_dtype=xdt)["y"]
+    ref = oracle.grouped_gemm_qnvfp4(xb, "token", d["w1"], sa, d["g1"], host(offs),
+                                     host(srt), k, act="silu_mul", x_dtype=xdt, sf_layout=sfl)["y"]
     assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 decode H={H} {xdt}")
 
 
@@ -293,20 +302,21 @@ def test_nvfp4_n_not_multiple_of_prefill_tile(I, sched):
     assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 N={2 * I} {sched}")
 
 
-@pytest.mark.parametrize("xdt", ["bf16", "f16"])
+@pytest.mark.parametrize("xdt,sfl", [("bf16", "rows"), ("f16", "rows"), ("f16", "quads")])
 @pytest.mark.parametrize("act", ["silu_mul", "none"])
-def test_nvfp4_decode_several_items_per_wave(act, xdt):
+def test_nvfp4_decode_several_items_per_wave(act, xdt, sfl):
     # More 4-row tiles x column blocks than the streaming schedule has waves,
     # so each wave runs several items back to back, with K / 512 = 3 (an odd
     # number of 4-chunk groups per item) and ragged last tiles.
     T, E, k, H, I = 203, 4, 2, 1536, 512
     d = synth.nvfp4_moe(47, T, E, k, H, I, routing="repeat")
     xg, xb = _xin(d["x"], xdt)
+    sg, sa = _sf(d["s1"], sfl)
     offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
-    y = mq.grouped_gemm_qnvfp4(xg, dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k,
+    y = mq.grouped_gemm_qnvfp4(xg, dev(d["w1"]), sg, dev(d["g1"]), offs, srt, k,
                                act=act, out_dtype=torch.float32, sched="decode")
-    ref = oracle.grouped_gemm_qnvfp4(xb, "token", d["w1"], d["s1"], d["g1"], host(offs),
-                                     host(srt), k, act=act, x_dtype=xdt)["y"]
+    ref = oracle.grouped_gemm_qnvfp4(xb, "token", d["w1"], sa, d["g1"], host(offs),
+                                     host(srt), k, act=act, x_dtype=xdt, sf_layout=sfl)["y"]
     assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 decode many items {act}")
 
 
@@ -403,12 +413,13 @@ def test_w4a4_chain_with_quantized_activations():
 @pytest.mark.parametrize("E,N,K", [(1, 128, 64), (3, 256, 128), (2, 384, 1216), (2, 512, 2176),
                                    (1, 256, 4096)])
 @pytest.mark.parametrize("swap", [False, True])
-def test_nvfp4_repack_bit_exact(E, N, K, swap):
+@pytest.mark.parametrize("sfl", ["rows", "quads"])
+def test_nvfp4_repack_bit_exact(E, N, K, swap, sfl):
     # K/64 = 1, 2, 19, 34, 64 scale quads per row: a partial 16-tile group,
     # ragged tails and whole groups; N/128 = 1..4 row blocks.
     d = synth.nvfp4_stored_weights(60 + N + K, E, N, K)
-    w_out, sf_out = mq.nvfp4_repack(dev(d["w"]), dev(d["sf"]), swap_halves=swap)
-    rw, rs = oracle.repack_nvfp4(d["w"], d["sf"], swap)
+    w_out, sf_out = mq.nvfp4_repack(dev(d["w"]), dev(d["sf"]), swap_halves=swap, sf_layout=sfl)
+    rw, rs = oracle.repack_nvfp4(d["w"], d["sf"], swap, out_layout=sfl)
     assert np.array_equal(host(w_out), rw)
     assert np.array_equal(host(sf_out), rs)
 
