@@ -38,6 +38,6 @@ from .combine import scatter_combine, pair_rows, sum_pairs
 from .layer import int4_layer, nvfp4_layer, fp8_dense
 from .quant import quantize_int4_rows
 from .layouts import (scale_swizzle_offset, unswizzle_scales, swizzle_scales, repack_nvfp4,
-                      quads_from_rows, rows_from_quads)
+                      quads_from_rows, rows_from_quads, tiles_from_rows, rows_from_tiles)
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -117,14 +117,15 @@ def grouped_gemm_qfp8_block(a, a_scale, a_row, w, w_scale, offsets, sorted_pair_
 
 
 def grouped_gemm_qnvfp4(x, a_row, w, w_sf, w_gscale, offsets, sorted_pair_ids, topk,
-                        act="none", rows=None, limit=None, x_dtype="bf16", sf_layout="rows"):
+                        act="none", rows=None, limit=None, x_dtype="bf16", sf_layout="rows",
+                        w_layout="rows"):
     """NVFP4 W4A16 grouped GEMM (tilelang_kernels.py grouped_gemm_fp4, with the
     per-expert global scale of megamoe_rm.cu).
 
     x [rows_a][K] bf16 bits (x_dtype 'bf16') or IEEE binary16 bits ('f16',
     megamoe_rm.cu's fp16 activations); w [E][N][K/2] E2M1 codes packed two per byte;
-    w_sf in sf_layout 'rows' ([E][N][K/16]) or 'quads' ([E][K/64][N][4], see
-    oracle.layouts);
+    w_sf in sf_layout 'rows' ([E][N][K/16]) or 'quads' ([E][K/64][N][4]), w in
+    w_layout 'rows' or 'tiled' ([E][N/16][K/64][16][32]; see oracle.layouts);
     w_sf [E][N][K/16] UE4M3 per-16 block scales; w_gscale [E] f32.
       Wd[e, n, k] = e2m1(W[e, n, k]) * ue4m3(w_sf[e, n, k // 16])
       y[s, n]     = w_gscale[e] * sum_k x[r, k] * Wd[e, n, k]
@@ -132,7 +133,6 @@ def grouped_gemm_qnvfp4(x, a_row, w, w_sf, w_gscale, offsets, sorted_pair_ids, t
     act 'silu_mul' returns silu_mul(y, limit) (megamoe_rm.cu applies the
     global scale, then the clamp, then the product).  Returns dict(y=float64)."""
     s, e, r = gemm_rows(offsets, sorted_pair_ids, topk, a_row, rows)
-    N = w.shape[1]
     if x_dtype not in ("bf16", "f16"):
         raise ValueError(x_dtype)
     if sf_layout == "quads":                       # [E][K/64][N][4] -> [E][N][K/16]
@@ -140,6 +140,12 @@ def grouped_gemm_qnvfp4(x, a_row, w, w_sf, w_gscale, offsets, sorted_pair_ids, t
         w_sf = rows_from_quads(np.asarray(w_sf))
     elif sf_layout != "rows":
         raise ValueError(sf_layout)
+    if w_layout == "tiled":                        # [E][N/16][K/64][16][32] -> [E][N][K/2]
+        from .layouts import rows_from_tiles
+        w = rows_from_tiles(np.asarray(w))
+    elif w_layout != "rows":
+        raise ValueError(w_layout)
+    N = w.shape[1]
     X = (bf16_value if x_dtype == "bf16" else f16_value)(np.asarray(x)[r])
     y = np.zeros((s.size, N), np.float64)
     for ex in np.unique(e):

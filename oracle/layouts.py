@@ -22,6 +22,11 @@ for each group of 4 consecutive block columns (a quad, 64 values of K),
 the 4 scale bytes of every row, rows consecutive: s_q[e, j, n, i] =
 s[e, n, 4j + i], stored [E][C/4][R][4].  One K step of 64 then finds the
 scales of many consecutive rows in one contiguous run.
+
+And a weight layout of its own, "tiled": each expert's [R][K/2] code bytes
+cut into blocks of 16 rows x 32 bytes (64 values of K), a 16-row group's
+blocks consecutive along K: byte (n, b) at
+((n // 16) * (K/64) + b // 32) * 512 + (n % 16) * 32 + b % 32.
 """
 import numpy as np
 
@@ -75,12 +80,30 @@ def rows_from_quads(s_q: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(np.swapaxes(np.asarray(s_q), -3, -2)).reshape(lead + (R, 4 * Q))
 
 
-def repack_nvfp4(w: np.ndarray, s_swz: np.ndarray, swap_halves: bool, out_layout: str = "rows"):
+def tiles_from_rows(w: np.ndarray) -> np.ndarray:
+    """[.., R, K/2] row-major codes -> [.., R/16, K/64, 16, 32] tiled bytes."""
+    lead, (R, KB) = w.shape[:-2], w.shape[-2:]
+    if R % 16 or KB % 32:
+        raise ValueError("the tiled layout needs R % 16 == 0 and K % 64 == 0")
+    t = np.asarray(w).reshape(lead + (R // 16, 16, KB // 32, 32))
+    return np.ascontiguousarray(np.swapaxes(t, -3, -2))
+
+
+def rows_from_tiles(w_t: np.ndarray) -> np.ndarray:
+    """[.., R/16, K/64, 16, 32] tiled -> [.., R, K/2] row-major (the inverse)."""
+    lead, (G, Q, sixteen, thirtytwo) = w_t.shape[:-4], w_t.shape[-4:]
+    assert sixteen == 16 and thirtytwo == 32
+    return np.ascontiguousarray(np.swapaxes(np.asarray(w_t), -3, -2)).reshape(lead + (16 * G, 32 * Q))
+
+
+def repack_nvfp4(w: np.ndarray, s_swz: np.ndarray, swap_halves: bool, out_layout: str = "rows",
+                 w_layout: str = "rows"):
     """Weights w [E][R][K/2] and swizzled scales s_swz [E][R*K/16] in the
     megamoe_rm.cu layout -> (w_lin [E][R][K/2], s_lin [E][R][K/16]) in the
     library's layout.  swap_halves: the matrix is a w13 (up rows first); the
     output puts the gate rows [R/2, R) first, then the up rows [0, R/2).
-    out_layout 'rows' returns scales [E][R][K/16], 'quads' [E][K/64][R][4]."""
+    out_layout 'rows' returns scales [E][R][K/16], 'quads' [E][K/64][R][4];
+    w_layout 'rows' returns codes [E][R][K/2], 'tiled' [E][R/16][K/64][16][32]."""
     E, R, KB = w.shape
     C = KB // 8                                        # K/16 blocks = (K/2 bytes) / 8
     s_lin = unswizzle_scales(s_swz, R, C)
@@ -92,6 +115,10 @@ def repack_nvfp4(w: np.ndarray, s_swz: np.ndarray, swap_halves: bool, out_layout
         w_out, s_out = w[:, order, :], s_lin[:, order, :]
     else:
         w_out, s_out = w.copy(), s_lin
+    if w_layout == "tiled":
+        w_out = tiles_from_rows(w_out)
+    elif w_layout != "rows":
+        raise ValueError(w_layout)
     if out_layout == "quads":
         return w_out, quads_from_rows(s_out)
     if out_layout != "rows":

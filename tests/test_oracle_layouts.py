@@ -124,3 +124,34 @@ def test_repack_to_quads_and_gemm_on_quads():
     y_r = oracle.grouped_gemm_qnvfp4(x, "sorted", w_r, s_r, g, off, None, 1)["y"]
     y_q = oracle.grouped_gemm_qnvfp4(x, "sorted", w_q, s_q, g, off, None, 1, sf_layout="quads")["y"]
     assert np.array_equal(y_r, y_q)
+
+
+def test_tiled_weight_layout_hand_worked_offsets():
+    # R=32 rows, K/2=96 bytes (K=192, 3 blocks of 32 bytes per row): byte
+    # (n, b) sits at ((n // 16) * 3 + b // 32) * 512 + (n % 16) * 32 + b % 32
+    R, KB = 32, 96
+    n_ = np.arange(R)[:, None]
+    b_ = np.arange(KB)[None, :]
+    w = ((n_ * 7 + b_ * 3) % 251).astype(np.uint8)[None]          # distinct enough to locate
+    t = oracle.tiles_from_rows(w).reshape(-1)
+    for n, b in [(0, 0), (0, 33), (15, 31), (16, 0), (17, 95), (31, 64), (5, 70)]:
+        assert t[((n // 16) * 3 + b // 32) * 512 + (n % 16) * 32 + b % 32] == w[0, n, b]
+    assert np.array_equal(t[32:64], w[0, 1, :32])                    # row 1 follows row 0 in block 0
+    assert np.array_equal(t[512:544], w[0, 0, 32:64])                # block 1 is row 0's next 32 bytes
+    assert np.array_equal(oracle.rows_from_tiles(oracle.tiles_from_rows(w)), w)
+    with pytest.raises(ValueError):
+        oracle.tiles_from_rows(np.zeros((1, 24, 32), np.uint8))
+
+
+def test_gemm_on_tiled_weights_and_quad_scales():
+    rng = np.random.default_rng(6)
+    d = synth.nvfp4_moe(16, T=7, E=2, k=1, H=128, I=64)
+    off, srt, inv, _ = oracle.route_prep(d["topk_ids"], 2)
+    y = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], off, srt, 1)["y"]
+    y2 = oracle.grouped_gemm_qnvfp4(d["x"], "token", oracle.tiles_from_rows(d["w1"]),
+                                    oracle.quads_from_rows(d["s1"]), d["g1"], off, srt, 1,
+                                    sf_layout="quads", w_layout="tiled")["y"]
+    assert np.array_equal(y, y2)
+    w_t, s_q = oracle.repack_nvfp4(d["w1"], oracle.swizzle_scales(d["s1"]), False, out_layout="quads",
+                                   w_layout="tiled")
+    assert np.array_equal(oracle.rows_from_tiles(w_t), d["w1"])
