@@ -82,11 +82,12 @@ def _traffic(kernel_tag, sources):
 class Workload:
     """Device buffers and the launch sequence of one step."""
 
-    def __init__(self, idx: int, fc2: str = "sorted", act: str = "f16", sfl: str = "quads"):
+    def __init__(self, idx: int, fc2: str = "sorted", act: str = "f16", sfl: str = "quads",
+                 wl: str = "tiled"):
         import torch
         import synth
         import quantized_moe_grouped_route_amd as mq
-        self.mq, self.idx, self.fc2, self.act, self.sfl = mq, idx, fc2, act, sfl
+        self.mq, self.idx, self.fc2, self.act, self.sfl, self.wl = mq, idx, fc2, act, sfl, wl
         self.cfg = synth.WORKLOADS[idx]
         self.d = d = synth.workload(idx)
         if self.cfg["kind"] == "repack":
@@ -151,8 +152,13 @@ class Workload:
             if sfl == "quads":
                 self.s1_host = d["s1"].reshape(E, H // 64, 2 * I, 4)
                 self.s2_host = d["s2"].reshape(E, I // 64, H, 4)
-            self.w1, self.s1, self.g1 = _dev(d["w1"]), _dev(self.s1_host), _dev(d["g1"])
-            self.w2, self.s2, self.g2 = _dev(d["w2"]), _dev(self.s2_host), _dev(d["g2"])
+            # codes in the tiled layout by default: iid bytes, read in that order
+            self.w1_host, self.w2_host = d["w1"], d["w2"]
+            if wl == "tiled":
+                self.w1_host = d["w1"].reshape(E, 2 * I // 16, H // 64, 16, 32)
+                self.w2_host = d["w2"].reshape(E, H // 16, I // 64, 16, 32)
+            self.w1, self.s1, self.g1 = _dev(self.w1_host), _dev(self.s1_host), _dev(d["g1"])
+            self.w2, self.s2, self.g2 = _dev(self.w2_host), _dev(self.s2_host), _dev(d["g2"])
             hdt = torch.float16 if act == "f16" else torch.bfloat16
             self.xh = torch.empty(T, H, dtype=torch.float16, device="cuda") if act == "f16" else None
             self.h = torch.empty(P, I, dtype=hdt, device="cuda")
@@ -536,6 +542,9 @@ def main():
     ap.add_argument("--sf-layout", choices=("rows", "quads"), default="quads",
                     help="NVFP4 workloads: block scales row-major [E][N][K/16] or K-quad-major "
                          "[E][K/64][N][4] (the library's layout for the tiled schedule)")
+    ap.add_argument("--w-layout", choices=("rows", "tiled"), default="tiled",
+                    help="NVFP4 workloads: E2M1 codes row-major [E][N][K/2] or tiled in 16-row x "
+                         "64-K blocks (the library's layout for the tiled schedule)")
     ap.add_argument("--fc2", choices=("sorted", "pair"), default="sorted",
                     help="NVFP4 workloads: FC2 writes sorted rows and the combine applies the top-k "
                          "weights (sorted), or FC2's epilogue applies them and writes pair-ordered "
@@ -572,7 +581,7 @@ def main():
         print(json.dumps({"copy_bytes_read_per_launch": src.numel() * 4,
                           "copy_bytes_written_per_launch": dst.numel() * 4}), flush=True)
         return
-    wl = Workload(args.workload, args.fc2, args.act, args.sf_layout)
+    wl = Workload(args.workload, args.fc2, args.act, args.sf_layout, args.w_layout)
     torch.cuda.synchronize()
     host_s = []
     for _ in range(args.warmup):
@@ -628,6 +637,7 @@ def main():
         config["fc2_epilogue"] = args.fc2
         config["activations"] = args.act
         config["scale_layout"] = args.sf_layout
+        config["code_layout"] = args.w_layout
     if args.workload in (2, 6):
         config["active_experts"] = wl.active
         config["weight_bytes"] = wl.weight_bytes

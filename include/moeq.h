@@ -89,6 +89,17 @@ typedef enum { MOEQ_AROW_TOKEN = 0, MOEQ_AROW_SORTED = 1 } moeq_arow;
  * moe_nvfp4_repack produces either one. */
 typedef enum { MOEQ_SF_ROWS = 0, MOEQ_SF_KQUADS = 1 } moeq_sf_layout;
 
+/* Layout of NVFP4 E2M1 codes.
+ * MOEQ_W_ROWS  [E][N][K/2] row-major.
+ * MOEQ_W_TILED each expert's [N][K/2] bytes in blocks of 16 rows x 32
+ *              bytes (64 values of K), 512 bytes each, a 16-row group's
+ *              blocks consecutive along K: byte (n, b) of an expert at
+ *              ((n/16)*(K/64) + b/32)*512 + (n%16)*32 + b%32.  The tiled
+ *              schedule then reads whole lines of codes, and a row group's
+ *              codes stay one contiguous run for the streaming schedule.
+ * moe_nvfp4_repack produces either one. */
+typedef enum { MOEQ_W_ROWS = 0, MOEQ_W_TILED = 1 } moeq_w_layout;
+
 /* Schedule hint for the grouped GEMMs.  Both schedules compute the same
  * result for every input; AUTO picks by the average rows per expert
  * (P / E): the weight-streaming DECODE schedule for few rows per expert,
@@ -195,7 +206,8 @@ moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int6
  *             fp16 activations; the weights are then dequantized and
  *             multiplied in fp16, at half the dequantization work; see
  *             moe_cast_bf16_to_f16)
- *   w         uint8 [E][N][K/2]       E2M1 codes
+ *   w         uint8 E2M1 codes in w_layout: [E][N][K/2] (ROWS) or tiled
+ *             (TILED, faster for the tiled schedule), E*N*K/2 bytes
  *   w_sf      uint8 UE4M3 block scales (sign bit clear; 0x7F is not a
  *             valid scale) in sf_layout: [E][N][K/16] (ROWS) or
  *             [E][K/64][N][4] (KQUADS, faster for the tiled schedule).
@@ -222,8 +234,8 @@ moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int6
  * N % 256 != 0 falls back to it as well.
  * ---------------------------------------------------------------------- */
 moeq_status grouped_gemm_qnvfp4(const void* x, moeq_dtype x_dtype, int64_t rows_a, moeq_arow a_row,
-                                const uint8_t* w, const uint8_t* w_sf, moeq_sf_layout sf_layout,
-                                const float* w_gscale,
+                                const uint8_t* w, moeq_w_layout w_layout, const uint8_t* w_sf,
+                                moeq_sf_layout sf_layout, const float* w_gscale,
                                 const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
                                 int64_t P, int32_t topk, int32_t E, int64_t N, int64_t K,
                                 moeq_act act, float act_limit, const float* pair_weights,
@@ -315,9 +327,11 @@ moeq_status moe_sum_pairs(const void* y_pairs, moeq_dtype y_dtype, const int32_t
  *                1: the matrix is a w13 with the up rows [0, N/2) first
  *                   and the gate rows [N/2, N) second; the output puts the
  *                   gate rows first, the order of MOEQ_ACT_SILU_MUL
+ *   w_out_layout MOEQ_W_ROWS or MOEQ_W_TILED: the layout of w_out
  *   out_layout   MOEQ_SF_ROWS or MOEQ_SF_KQUADS: the layout of sf_out
- *   w_out   uint8 [E][N][K/2]   out: row n = input row n (swap 0) or
- *                               (n + N/2) mod N (swap 1)
+ *   w_out   uint8 [E*N*K/2]     out: the codes in w_out_layout, row n =
+ *                               input row n (swap 0) or (n + N/2) mod N
+ *                               (swap 1)
  *   sf_out  uint8 [E][N*K/16]   out: the scales in out_layout, rows as
  *                               w_out
  * A pure byte permutation: the outputs are bit-exact copies of input bytes.
@@ -327,8 +341,8 @@ moeq_status moe_sum_pairs(const void* y_pairs, moeq_dtype y_dtype, const int32_t
  * MOEQ_EINVAL).  The per-expert global scale needs no repack.
  * ---------------------------------------------------------------------- */
 moeq_status moe_nvfp4_repack(const uint8_t* w_in, const uint8_t* sf_in, int64_t E, int64_t N, int64_t K,
-                             int32_t swap_halves, moeq_sf_layout out_layout, uint8_t* w_out,
-                             uint8_t* sf_out, void* stream);
+                             int32_t swap_halves, moeq_w_layout w_out_layout, moeq_sf_layout out_layout,
+                             uint8_t* w_out, uint8_t* sf_out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,6 +27,7 @@ ACT_SILU_MUL_LIMIT = 2
 AROW = {"token": 0, "sorted": 1}
 SCHED = {"auto": 0, "decode": 1, "prefill": 2}
 SF_LAYOUT = {"rows": 0, "quads": 1}
+W_LAYOUT = {"rows": 0, "tiled": 1}
 
 _DTYPE_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32, torch.int32: I32}
 
@@ -63,11 +64,11 @@ def lib():
                                      i32, i32, vp, i32, vp]),
         "grouped_gemm_qfp8_block": (i32, [vp, vp, i64, i32, vp, vp, vp, vp, i64, i32, i32, i64,
                                           i64, i32, vp, i32, vp]),
-        "grouped_gemm_qnvfp4": (i32, [vp, i32, i64, i32, vp, vp, i32, vp, vp, vp, i64, i32, i32, i64, i64,
+        "grouped_gemm_qnvfp4": (i32, [vp, i32, i64, i32, vp, i32, vp, i32, vp, vp, vp, i64, i32, i32, i64, i64,
                                       i32, C.c_float, vp, i32, vp, i32, vp]),
         "moe_scatter_combine": (i32, [vp, i32, vp, vp, i64, i32, i64, i32, vp, vp]),
         "moe_quantize_int4": (i32, [vp, i32, i64, i64, vp, vp, vp]),
-        "moe_nvfp4_repack": (i32, [vp, vp, i64, i64, i64, i32, i32, vp, vp, vp]),
+        "moe_nvfp4_repack": (i32, [vp, vp, i64, i64, i64, i32, i32, i32, vp, vp, vp]),
         "moe_sum_pairs": (i32, [vp, i32, vp, i64, i32, i64, i32, vp, vp]),
         "moe_cast_bf16_to_f16": (i32, [vp, i64, vp, vp]),
     }
@@ -213,6 +214,7 @@ def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, t
                         out_dtype=torch.bfloat16, out=None, P=None, sched="auto"):
     """NVFP4 W4A16 grouped GEMM: x bf16 or f16 [rows_a][K] (f16: dequant and
     MFMA in binary16, megamoe_rm.cu's fp16 activations), w uint8 [E][N][K/2]
+    (row-major) or [E][N/16][K/64][16][32] (tiled)
     (E2M1), w_sf uint8 [E][N][K/16] (UE4M3, row-major), uint8 [E][K/64][N][4]
     (K-quad-major, faster for the tiled schedule) or int32 [E][N][K/64] (four
     UE4M3 per word, block 4g+j in bits 8j..8j+7: the row-major bytes), w_gscale
@@ -221,7 +223,15 @@ def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, t
     pair_weights (f32, T*topk values, e.g. topk_weights): megamoe_rm.cu's
     fc2_rm epilogue, out row p = w[p] * y of pair p, in pair order."""
     _need(x, "x", (torch.bfloat16, torch.float16), 2)
-    _need(w, "w", torch.uint8, 3)
+    _need(w, "w", torch.uint8)
+    if w.dim() == 5 and tuple(w.shape[3:]) == (16, 32):
+        w_tiled = True
+        En, N, K = w.shape[0], 16 * w.shape[1], 64 * w.shape[2]
+    elif w.dim() == 3:
+        w_tiled = False
+        En, N, K = w.shape[0], w.shape[1], 2 * w.shape[2]
+    else:
+        raise ValueError("w must be [E][N][K/2] or [E][N/16][K/64][16][32]")
     if isinstance(w_sf, torch.Tensor) and w_sf.dtype == torch.int32 and w_sf.dim() == 3:
         _need(w_sf, "w_sf", torch.int32, 3)
         w_sf = w_sf.view(torch.uint8)                   # [E][N][K/64] words -> [E][N][K/16] bytes
@@ -229,8 +239,6 @@ def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, t
     quads = w_sf.dim() == 4
     _need(w_gscale, "w_gscale", torch.float32, 1)
     E, P, arow = _grouped_common(x, expert_offsets, sorted_pair_ids, a_row, P)
-    En, N, Kh = w.shape
-    K = 2 * Kh
     sf_shape = (E, K // 64, N, 4) if quads else (E, N, K // 16)
     if En != E or x.shape[1] != K or tuple(w_sf.shape) != sf_shape or w_gscale.numel() != E:
         raise ValueError("inconsistent NVFP4 operand shapes")
@@ -242,7 +250,8 @@ def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, t
         if sorted_pair_ids is None or pair_weights.numel() != sorted_pair_ids.numel():
             raise ValueError("pair_weights needs sorted_pair_ids and one weight per pair")
     out = _out(out, P, N // 2 if act == "silu_mul" else N, out_dtype, x.device)
-    st = lib().grouped_gemm_qnvfp4(_ptr(x), _DTYPE_CODE[x.dtype], x.shape[0], arow, _ptr(w), _ptr(w_sf),
+    st = lib().grouped_gemm_qnvfp4(_ptr(x), _DTYPE_CODE[x.dtype], x.shape[0], arow, _ptr(w),
+                                   W_LAYOUT["tiled" if w_tiled else "rows"], _ptr(w_sf),
                                    SF_LAYOUT["quads" if quads else "rows"], _ptr(w_gscale),
                                    _ptr(expert_offsets), _ptr(sorted_pair_ids), P, topk, E, N, K,
                                    act_code, 0.0 if limit is None else float(limit), _ptr(pair_weights),
@@ -327,11 +336,13 @@ def quantize_int4_rows(x, *, q=None, scale=None):
     return q, scale
 
 
-def nvfp4_repack(w, sf_swizzled, *, swap_halves: bool, sf_layout="rows", w_out=None, sf_out=None):
+def nvfp4_repack(w, sf_swizzled, *, swap_halves: bool, sf_layout="rows", w_layout="rows", w_out=None,
+                 sf_out=None):
     """Convert NVFP4 expert weights from the in-place layout of megamoe_rm.cu
     (w uint8 [E][N][K/2]; sf_swizzled uint8 [E][N*K/16] in 128x4 tiles;
     swap_halves for a w13 stored up rows first) to grouped_gemm_qnvfp4's
-    layout.  Returns (w_out [E][N][K/2], sf_out [E][N][K/16] for sf_layout
+    layout.  Returns (w_out [E][N][K/2] for w_layout 'rows' or
+    [E][N/16][K/64][16][32] for 'tiled', sf_out [E][N][K/16] for sf_layout
     'rows' or [E][K/64][N][4] for 'quads')."""
     _need(w, "w", torch.uint8, 3)
     _need(sf_swizzled, "sf_swizzled", torch.uint8, 2)
@@ -339,16 +350,18 @@ def nvfp4_repack(w, sf_swizzled, *, swap_halves: bool, sf_layout="rows", w_out=N
     K = 2 * Kh
     if tuple(sf_swizzled.shape) != (E, N * K // 16):
         raise ValueError("sf_swizzled must be [E][N*K/16]")
+    w_shape = (E, N // 16, K // 64, 16, 32) if w_layout == "tiled" else (E, N, Kh)
     if w_out is None:
-        w_out = torch.empty_like(w)
+        w_out = torch.empty(w_shape, dtype=torch.uint8, device=w.device)
     sf_shape = (E, K // 64, N, 4) if sf_layout == "quads" else (E, N, K // 16)
     if sf_out is None:
         sf_out = torch.empty(sf_shape, dtype=torch.uint8, device=w.device)
-    _need(w_out, "w_out", torch.uint8, 3)
+    _need(w_out, "w_out", torch.uint8)
     _need(sf_out, "sf_out", torch.uint8)
-    if tuple(w_out.shape) != (E, N, Kh) or tuple(sf_out.shape) != sf_shape:
-        raise ValueError(f"w_out must be [E][N][K/2] and sf_out {sf_shape}")
+    if tuple(w_out.shape) != w_shape or tuple(sf_out.shape) != sf_shape:
+        raise ValueError(f"w_out must be {w_shape} and sf_out {sf_shape}")
     st = lib().moe_nvfp4_repack(_ptr(w), _ptr(sf_swizzled), E, N, K, int(bool(swap_halves)),
-                                SF_LAYOUT[sf_layout], _ptr(w_out), _ptr(sf_out), _stream())
+                                W_LAYOUT[w_layout], SF_LAYOUT[sf_layout], _ptr(w_out), _ptr(sf_out),
+                                _stream())
     _check("moe_nvfp4_repack", st)
     return w_out, sf_out

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale,
     const int* __restrict__ offsets, const int* __restrict__ sorted_ids, int topk, int E, int P, int N,
-    int K, void* __restrict__ out, float limit, const float* __restrict__ pair_w, int sf_quads) {
+    int K, void* __restrict__ out, float limit, const float* __restrict__ pair_w, int sf_quads, int w_tiled) {
   static_assert(!(SILU && PAIR), "pair-ordered output is for act NONE");
   using namespace pf;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
@@ -121,12 +121,21 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
     };
     // B: wave wn moves rows 64wn + 32j + lane/2 (chunk position lane%2);
     // S: rows 64wn + lane.
+    // Row-major codes: 32 bytes at row stride K/2.  Tiled codes (16-row x
+    // 64-K blocks of 512 bytes, a row group's blocks consecutive along K):
+    // the K step's 32 bytes of a row sit in its group's block, so a wave's
+    // 32 rows read two whole 512-byte blocks.
     const uint8_t* pb[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int rb = 64 * wn + 32 * j + (lane >> 1);
-      pb[j] = w + grow(rb) * wrow_bytes + (((lane & 1) ^ ((rb >> 3) & 1)) << 4);
+      const int64_t wr = grow(rb);
+      const int c16 = (((lane & 1) ^ ((rb >> 3) & 1)) << 4);
+      const int64_t n = wr - (int64_t)t.e * N;
+      pb[j] = w_tiled ? w + (int64_t)t.e * N * wrow_bytes + ((n >> 4) * (K / 64)) * 512 + (n & 15) * 32 + c16
+                      : w + wr * wrow_bytes + c16;
     }
+    const int64_t b_step = w_tiled ? 512 : 32;
     // S: row 64wn + lane, its 4 scale bytes of the K step.  Row-major
     // scales: 4 bytes at row stride K/16; K-quad-major ([K/64][N][4]): the
     // step's bytes of consecutive rows are consecutive (a whole-line copy).
@@ -142,7 +151,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
 #pragma unroll
       for (int j = 0; j < 4; ++j) dma16(pa[j] + (int64_t)g * 128, lds_a + st + j * 1024);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) dma16(pb[j] + (int64_t)g * 32, lds_b + st + j * 1024);
+      for (int j = 0; j < 2; ++j) dma16(pb[j] + (int64_t)g * b_step, lds_b + st + j * 1024);
       dma4(ps + (int64_t)g * s_step, lds_s + st);
     };
     constexpr int kPer = 7;  // loads per wave per stage
@@ -391,7 +400,7 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale, const int* __restrict__ offsets,
     const int* __restrict__ sorted_ids, int topk, int E, int P, int N, int K, void* __restrict__ out,
-    float limit, const float* __restrict__ pair_w, int sf_quads) {
+    float limit, const float* __restrict__ pair_w, int sf_quads, int w_tiled) {
   static_assert(!(SILU && PAIR), "pair-ordered output is for act NONE");
   constexpr int CPS = dc::cps<WIDE>();
   constexpr int D = dc::depth<WIDE>();
@@ -421,6 +430,9 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
   const int64_t wrow = K / 2, srow = K / 16;
   // scale bytes per copy step: a superchunk (WIDE, 8 quads) or a step (2 quads)
   const int64_t s_adv = sf_quads ? (WIDE ? 8 : 2) * (int64_t)N * 4 : (WIDE ? 32 : 8);
+  // code bytes per copy step and row group: 128 or 64 per row (row-major),
+  // 4 or 2 blocks of 512 bytes (tiled)
+  const int64_t w_adv = w_tiled ? (WIDE ? 2048 : 1024) : (WIDE ? 128 : 64);
   const int g = lane >> 4, l16 = lane & 15;
   uint8_t* myring = ring + wv * kWave;
   const uint32_t lb = lds_addr(myring);
@@ -444,10 +456,21 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int r = 8 * h + (lane >> 3);
-        const int off = (((lane & 7) ^ ((r >> 1) & 7)) << 4);
-        wsrc[h] = w + (e0 + b0 + r) * wrow + off;
-        wsrc[2 + h] = w + (e0 + b1 + r) * wrow + off;
+        const int p = (lane & 7) ^ ((r >> 1) & 7);
+        if (w_tiled) {
+          // piece p of the step's 128 bytes: block p/2 of the step, half p%2
+          const int64_t in = (int64_t)(p >> 1) * 512 + r * 32 + (p & 1) * 16;
+          wsrc[h] = w + e0 * wrow + (int64_t)(b0 >> 4) * (K / 64) * 512 + in;
+          wsrc[2 + h] = w + e0 * wrow + (int64_t)(b1 >> 4) * (K / 64) * 512 + in;
+        } else {
+          wsrc[h] = w + (e0 + b0 + r) * wrow + (p << 4);
+          wsrc[2 + h] = w + (e0 + b1 + r) * wrow + (p << 4);
+        }
       }
+    } else if (w_tiled) {
+      const int64_t in = (int64_t)(g >> 1) * 512 + l16 * 32 + (g & 1) * 16;
+      wsrc[0] = w + e0 * wrow + (int64_t)(b0 >> 4) * (K / 64) * 512 + in;
+      wsrc[2] = w + e0 * wrow + (int64_t)(b1 >> 4) * (K / 64) * 512 + in;
     } else {
       wsrc[0] = w + (e0 + b0 + l16) * wrow + g * 16;
       wsrc[2] = w + (e0 + b1 + l16) * wrow + g * 16;
@@ -499,14 +522,14 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
         ops += 1 + is_rows;
         ++is_sc;
       }
-      const int64_t o = (int64_t)is_st * 128;
+      const int64_t o = (int64_t)is_st * w_adv;
       dma16(wsrc[0] + o, l);
       dma16(wsrc[1] + o, l + 1024);
       dma16(wsrc[2] + o, l + 2048);
       dma16(wsrc[3] + o, l + 3072);
     } else {
       ops = 4;
-      const int64_t o = (int64_t)is_st * 64;
+      const int64_t o = (int64_t)is_st * w_adv;
       dma16(wsrc[0] + o, l);
       dma16(wsrc[2] + o, l + 1024);
       dma16(sx + (int64_t)is_st * 256, l + 2048);
@@ -639,18 +662,18 @@ hipError_t go(const GroupedArgs& g, bool decode, const uint16_t* x, const uint8_
     if (g.K % 512 == 0)
       hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, true, PAIR, H16>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
                          g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N,
-                         g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads);
+                         g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads, g.w_tiled);
     else
       hipLaunchKernelGGL((nvfp4_decode<OUT, SILU, false, PAIR, H16>), dim3(grid), dim3(dc::kWaves * 64), 0, stream, x,
                          g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N,
-                         g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads);
+                         g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads, g.w_tiled);
   } else {
     const int64_t mt_ub = (g.P + pf::kM - 1) / pf::kM + std::min<int64_t>(g.E, g.P);
     const int64_t items_ub = mt_ub * (g.N / pf::kN);
     const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus * 2);
     hipLaunchKernelGGL((nvfp4_prefill<OUT, SILU, PAIR, H16>), dim3(grid), dim3(pf::kThreads), 0, stream, x,
                        g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P,
-                       g.N, g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads);
+                       g.N, g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads, g.w_tiled);
   }
   return hipGetLastError();
 }

@@ -39,6 +39,7 @@ struct GroupedArgs {
   const float* pair_weights;  // [P] or null: write w[p] * y to row p = sorted_ids[s] (NVFP4 only)
   int x_f16;                // NVFP4: activations are binary16 (else bf16)
   int sf_quads;             // NVFP4: scales [E][K/64][N][4] (else [E][N][K/16])
+  int w_tiled;              // NVFP4: codes in 16-row x 64-K blocks (else [E][N][K/2])
   int out_kind;             // OutKind
   void* out;
   int sched;                // 0 auto, 1 decode, 2 prefill
@@ -58,6 +59,7 @@ hipError_t launch_cast_bf16_f16(const uint16_t* x, int64_t n, uint16_t* y, int n
 // NVFP4 weight repack: megamoe_rm.cu layout (swizzled scales, optionally up
 // rows first) -> grouped_gemm_qnvfp4's, E experts of N rows and K columns.
 hipError_t launch_repack_nvfp4(const uint8_t* w_in, const uint8_t* sf_in, int64_t E, int64_t N, int64_t K,
-                               int swap_halves, int out_quads, uint8_t* w_out, uint8_t* sf_out, hipStream_t stream);
+                               int swap_halves, int w_tiled, int out_quads, uint8_t* w_out, uint8_t* sf_out,
+                               hipStream_t stream);
 
 }  // namespace moeq

@@ -89,6 +89,7 @@ moeq::GroupedArgs make_args(const int32_t* offsets, const int32_t* sorted, int64
   g.pair_weights = nullptr;
   g.x_f16 = 0;
   g.sf_quads = 0;
+  g.w_tiled = 0;
   g.out_kind = (int)od;
   g.out = out;
   g.sched = (int)sched;
@@ -178,7 +179,8 @@ moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int6
 }
 
 moeq_status grouped_gemm_qnvfp4(const void* x, moeq_dtype x_dtype, int64_t rows_a, moeq_arow a_row, const uint8_t* w,
-                                const uint8_t* w_sf, moeq_sf_layout sf_layout, const float* w_gscale,
+                                moeq_w_layout w_layout, const uint8_t* w_sf, moeq_sf_layout sf_layout,
+                                const float* w_gscale,
                                 const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
                                 int64_t P, int32_t topk, int32_t E, int64_t N, int64_t K,
                                 moeq_act act, float act_limit, const float* pair_weights,
@@ -191,6 +193,7 @@ moeq_status grouped_gemm_qnvfp4(const void* x, moeq_dtype x_dtype, int64_t rows_
   if (x_dtype != MOEQ_BF16 && x_dtype != MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "%s: x dtype %d", fn, x_dtype);
   if (sf_layout != MOEQ_SF_ROWS && sf_layout != MOEQ_SF_KQUADS)
     return fail(MOEQ_EINVAL, "%s: sf_layout %d", fn, sf_layout);
+  if (w_layout != MOEQ_W_ROWS && w_layout != MOEQ_W_TILED) return fail(MOEQ_EINVAL, "%s: w_layout %d", fn, w_layout);
   if (act != MOEQ_ACT_NONE && act != MOEQ_ACT_SILU_MUL && act != MOEQ_ACT_SILU_MUL_LIMIT)
     return fail(MOEQ_EUNSUPPORTED, "%s: act %d", fn, act);
   if (act == MOEQ_ACT_SILU_MUL_LIMIT && !(act_limit > 0.0f))
@@ -211,6 +214,7 @@ moeq_status grouped_gemm_qnvfp4(const void* x, moeq_dtype x_dtype, int64_t rows_
   g.pair_weights = pair_weights;
   g.x_f16 = x_dtype == MOEQ_F16 ? 1 : 0;
   g.sf_quads = sf_layout == MOEQ_SF_KQUADS ? 1 : 0;
+  g.w_tiled = w_layout == MOEQ_W_TILED ? 1 : 0;
   return hip_status(moeq::launch_gemm_nvfp4(g, static_cast<const uint16_t*>(x), w, w_sf, w_gscale,
                                             (hipStream_t)stream),
                     fn);
@@ -285,8 +289,8 @@ moeq_status moe_quantize_int4(const void* x, moeq_dtype x_dtype, int64_t rows, i
 }
 
 moeq_status moe_nvfp4_repack(const uint8_t* w_in, const uint8_t* sf_in, int64_t E, int64_t N, int64_t K,
-                             int32_t swap_halves, moeq_sf_layout out_layout, uint8_t* w_out, uint8_t* sf_out,
-                             void* stream) {
+                             int32_t swap_halves, moeq_w_layout w_out_layout, moeq_sf_layout out_layout,
+                             uint8_t* w_out, uint8_t* sf_out, void* stream) {
   const char* fn = "moe_nvfp4_repack";
   if (E < 1 || E > kMaxE) return fail(MOEQ_EINVAL, "%s: E=%lld outside [1, %d]", fn, (long long)E, kMaxE);
   if (N <= 0 || K <= 0 || N > (1 << 20) || K > (1 << 17))
@@ -298,6 +302,8 @@ moeq_status moe_nvfp4_repack(const uint8_t* w_in, const uint8_t* sf_in, int64_t 
   if (swap_halves != 0 && swap_halves != 1) return fail(MOEQ_EINVAL, "%s: swap_halves=%d", fn, swap_halves);
   if (out_layout != MOEQ_SF_ROWS && out_layout != MOEQ_SF_KQUADS)
     return fail(MOEQ_EINVAL, "%s: out_layout %d", fn, out_layout);
+  if (w_out_layout != MOEQ_W_ROWS && w_out_layout != MOEQ_W_TILED)
+    return fail(MOEQ_EINVAL, "%s: w_out_layout %d", fn, w_out_layout);
   if (!w_in || !sf_in || !w_out || !sf_out) return fail(MOEQ_EINVAL, "%s: null pointer", fn);
   if (!aligned(w_in, 16) || !aligned(sf_in, 16) || !aligned(w_out, 16) || !aligned(sf_out, 16))
     return fail(MOEQ_EALIGN, "%s: pointers must be 16-byte aligned", fn);
@@ -309,7 +315,8 @@ moeq_status moe_nvfp4_repack(const uint8_t* w_in, const uint8_t* sf_in, int64_t 
   if (overlap(w_out, wb, w_in, wb) || overlap(w_out, wb, sf_in, sb) || overlap(w_out, wb, sf_out, sb) ||
       overlap(sf_out, sb, w_in, wb) || overlap(sf_out, sb, sf_in, sb))
     return fail(MOEQ_EINVAL, "%s: an output overlaps an input or the other output (no in-place repack)", fn);
-  return hip_status(moeq::launch_repack_nvfp4(w_in, sf_in, E, N, K, swap_halves, out_layout == MOEQ_SF_KQUADS,
+  return hip_status(moeq::launch_repack_nvfp4(w_in, sf_in, E, N, K, swap_halves, w_out_layout == MOEQ_W_TILED,
+                                              out_layout == MOEQ_SF_KQUADS,
                                               w_out, sf_out,
                                               (hipStream_t)stream),
                     fn);

@@ -7,7 +7,9 @@
 // Weights.  With the halves swapped, output rows [0, R/2) of an expert are
 // input rows [R/2, R) and the other way round; both halves are contiguous,
 // so the copy of one expert is a rotation of its bytes by half their count.
-// Each thread moves one 16-byte vector.
+// Each thread moves one 16-byte vector.  Tiled output (16-row x 64-K blocks
+// of 512 bytes, a row group's blocks consecutive along K) gathers each
+// block's 16 rows x 32 bytes instead.
 //
 // Scales.  The swizzled matrix of an expert is a run of 512-byte tiles, one
 // per (128-row block, 4-column quad), row block major.  The 16-byte group i
@@ -42,16 +44,27 @@ struct RepackArgs {
   uint32_t groups;      // workgroups per 128-row block on the scales
   uint32_t half_rows;   // R / 2 when the halves swap, else 0
   uint32_t out_quads;   // scales out as [K/64][R][4 bytes] (else [R][K/16])
+  uint32_t w_tiled;     // codes out in 16-row x 64-K blocks of 512 bytes (else [R][K/2])
+  uint32_t kblocks;     // 64-K blocks per row = K / 64
 };
 
 __device__ __forceinline__ void weights_part(const RepackArgs& a, uint32_t bx) {
   const size_t base = (size_t)blockIdx.y * a.chunks;
   const uint32_t j = bx * kThreads + threadIdx.x;
-  if (j < a.chunks) {
-    uint32_t s = j + a.rot;
+  if (j >= a.chunks) return;
+  uint32_t s;
+  if (a.w_tiled) {
+    // output chunk j: block j/32 = (row group, 64-K block), row j%32/2 of
+    // the group, half j%2 of the row's 32 bytes
+    const uint32_t blk = j >> 5, rg = blk / a.kblocks, kb = blk - rg * a.kblocks;
+    uint32_t r = rg * 16 + ((j & 31) >> 1) + a.half_rows;
+    if (r >= a.R) r -= a.R;
+    s = r * (a.kblocks * 2) + kb * 2 + (j & 1);
+  } else {
+    s = j + a.rot;
     if (s >= a.chunks) s -= a.chunks;
-    __builtin_nontemporal_store(__builtin_nontemporal_load(a.w_in + base + s), a.w_out + base + j);
   }
+  __builtin_nontemporal_store(__builtin_nontemporal_load(a.w_in + base + s), a.w_out + base + j);
 }
 
 __device__ __forceinline__ void scales_part(const RepackArgs& a, uint32_t bx, uint32_t* t) {
@@ -115,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void repack_nvfp4(RepackArgs a) {
 }  // namespace
 
 hipError_t launch_repack_nvfp4(const uint8_t* w_in, const uint8_t* sf_in, int64_t E, int64_t N, int64_t K,
-                               int swap_halves, int out_quads, uint8_t* w_out, uint8_t* sf_out,
+                               int swap_halves, int w_tiled, int out_quads, uint8_t* w_out, uint8_t* sf_out,
                                hipStream_t stream) {
   RepackArgs a;
   a.w_in = reinterpret_cast<const u32x4*>(w_in);
@@ -130,6 +143,8 @@ hipError_t launch_repack_nvfp4(const uint8_t* w_in, const uint8_t* sf_in, int64_
   a.groups = (a.quads + kTilesPerGroup - 1) / kTilesPerGroup;
   a.half_rows = swap_halves ? a.R / 2 : 0u;
   a.out_quads = out_quads ? 1u : 0u;
+  a.w_tiled = w_tiled ? 1u : 0u;
+  a.kblocks = (uint32_t)(K / 64);
   const uint32_t sblocks = (a.R / 128) * a.groups;
   hipLaunchKernelGGL(repack_nvfp4, dim3(a.wblocks + sblocks, (uint32_t)E), dim3(kThreads), 0, stream, a);
   return hipGetLastError();

@@ -109,11 +109,11 @@ def test_fp8_rejects(L, kw, status):
 
 
 def _nvfp4(L, **kw):
-    a = dict(x=A16, xd=mq.BF16, rows=16, arow=0, w=A16, sf=A16, sfl=0, gs=A16, off=A16, srt=A16, P=16,
+    a = dict(x=A16, xd=mq.BF16, rows=16, arow=0, w=A16, wl=0, sf=A16, sfl=0, gs=A16, off=A16, srt=A16, P=16,
              topk=2, E=4, N=256, K=256, act=0, lim=0.0, pw=None, od=mq.BF16, out=A16, sched=0)
     a.update(kw)
-    return L.grouped_gemm_qnvfp4(a["x"], a["xd"], a["rows"], a["arow"], a["w"], a["sf"], a["sfl"], a["gs"],
-                                 a["off"],
+    return L.grouped_gemm_qnvfp4(a["x"], a["xd"], a["rows"], a["arow"], a["w"], a["wl"], a["sf"], a["sfl"],
+                                 a["gs"], a["off"],
                                  a["srt"], a["P"], a["topk"], a["E"], a["N"], a["K"], a["act"],
                                  a["lim"], a["pw"], a["od"], a["out"], a["sched"], None)
 
@@ -126,7 +126,7 @@ def _nvfp4(L, **kw):
     (dict(act=2, lim=float("nan")), mq.EINVAL),
     (dict(pw=A16, act=1), mq.EUNSUPPORTED), (dict(pw=A16, srt=None), mq.EINVAL),
     (dict(pw=ODD), mq.EALIGN), (dict(xd=mq.F32), mq.EUNSUPPORTED), (dict(xd=mq.I32), mq.EUNSUPPORTED),
-    (dict(sfl=2), mq.EINVAL), (dict(sfl=-1), mq.EINVAL),
+    (dict(sfl=2), mq.EINVAL), (dict(sfl=-1), mq.EINVAL), (dict(wl=2), mq.EINVAL),
 ])
 def test_nvfp4_rejects(L, kw, status):
     assert _nvfp4(L, **kw) == status
@@ -175,10 +175,10 @@ def test_binding_raises_without_gpu_tensors():
 
 
 def _repack(L, **kw):
-    a = dict(w=A16, sf=0x20000, E=2, N=256, K=128, swap=1, lay=0, wo=0x40000, so=0x80000)
+    a = dict(w=A16, sf=0x20000, E=2, N=256, K=128, swap=1, wlay=0, lay=0, wo=0x40000, so=0x80000)
     a.update(kw)
-    return L.moe_nvfp4_repack(a["w"], a["sf"], a["E"], a["N"], a["K"], a["swap"], a["lay"], a["wo"], a["so"],
-                              None)
+    return L.moe_nvfp4_repack(a["w"], a["sf"], a["E"], a["N"], a["K"], a["swap"], a["wlay"], a["lay"], a["wo"],
+                              a["so"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -190,7 +190,7 @@ def _repack(L, **kw):
     (dict(so=0x40000 + 0x7000), mq.EINVAL),             # overlaps w_out
     (dict(so=0x20000), mq.EINVAL),                      # scales in place
     (dict(N=1 << 20, K=1 << 17), mq.EINVAL),            # N*K too large
-    (dict(lay=3), mq.EINVAL),
+    (dict(lay=3), mq.EINVAL), (dict(wlay=5), mq.EINVAL),
 ])
 def test_repack_rejects(L, kw, status):
     assert _repack(L, **kw) == status

@@ -236,21 +236,28 @@ def _sf(s_rows, sfl):
     return dev(a), a
 
 
-@pytest.mark.parametrize("sfl", ["rows", "quads"])
+def _w(w_rows, wl):
+    """Codes in layout wl ('rows' or 'tiled'): (device tensor, oracle array)."""
+    a = w_rows if wl == "rows" else oracle.tiles_from_rows(w_rows)
+    return dev(a), a
+
+
+@pytest.mark.parametrize("wl,sfl", [("rows", "rows"), ("rows", "quads"), ("tiled", "quads")])
 @pytest.mark.parametrize("xdt", ["bf16", "f16"])
 @pytest.mark.parametrize("sched", ["prefill", "decode"])
 @pytest.mark.parametrize("act", ["none", "silu_mul"])
-def test_nvfp4(sched, act, xdt, sfl):
+def test_nvfp4(sched, act, xdt, wl, sfl):
     T, E, k, H, I = 150, 5, 2, 256, 128
     d = synth.nvfp4_moe(41, T, E, k, H, I, routing="repeat")
     xg, xb = _xin(d["x"], xdt)
     sg, sa = _sf(d["s1"], sfl)
+    wg, wa = _w(d["w1"], wl)
     offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
-    y = mq.grouped_gemm_qnvfp4(xg, dev(d["w1"]), sg, dev(d["g1"]), offs, srt, k,
+    y = mq.grouped_gemm_qnvfp4(xg, wg, sg, dev(d["g1"]), offs, srt, k,
                                act=act, out_dtype=torch.float32, sched=sched)
-    ref = oracle.grouped_gemm_qnvfp4(xb, "token", d["w1"], sa, d["g1"], host(offs),
-                                     host(srt), k, act=act, x_dtype=xdt, sf_layout=sfl)["y"]
-    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 {sched} {act} {xdt} {sfl}")
+    ref = oracle.grouped_gemm_qnvfp4(xb, "token", wa, sa, d["g1"], host(offs),
+                                     host(srt), k, act=act, x_dtype=xdt, sf_layout=sfl, w_layout=wl)["y"]
+    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 {sched} {act} {xdt} {wl} {sfl}")
 
 
 @pytest.mark.parametrize("xdt", ["bf16", "f16"])
@@ -269,9 +276,10 @@ def test_nvfp4_sorted_rows_full_code_range(sched, xdt):
     assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 sorted {sched} {xdt}")
 
 
-@pytest.mark.parametrize("xdt,sfl", [("bf16", "rows"), ("f16", "rows"), ("f16", "quads")])
+@pytest.mark.parametrize("xdt,sfl,wl", [("bf16", "rows", "rows"), ("f16", "rows", "rows"), ("f16", "quads", "rows"),
+                                        ("f16", "quads", "tiled")])
 @pytest.mark.parametrize("H", [1024, 1536, 2176, 3200])
-def test_nvfp4_decode_chunk_counts(H, xdt, sfl):
+def test_nvfp4_decode_chunk_counts(H, xdt, sfl, wl):
     # K / 128 = 8, 12, 17, 25 weight chunks per lane: exactly the in-flight
     # depth, a partial refill, one steady pass plus a tail, several passes
     # plus a ragged tail.
@@ -279,11 +287,12 @@ def test_nvfp4_decode_chunk_counts(H, xdt, sfl):
     d = synth.nvfp4_moe(45, T, E, k, H, I, routing="repeat")
     xg, xb = _xin(d["x"], xdt)
     sg, sa = _sf(d["s1"], sfl)
+    wg, wa = _w(d["w1"], wl)
     offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
-    y = mq.grouped_gemm_qnvfp4(xg, dev(d["w1"]), sg, dev(d["g1"]), offs, srt, k,
+    y = mq.grouped_gemm_qnvfp4(xg, wg, sg, dev(d["g1"]), offs, srt, k,
                                act="silu_mul", out_dtype=torch.float32, sched="decode")
-    ref = oracle.grouped_gemm_qnvfp4(xb, "token", d["w1"], sa, d["g1"], host(offs),
-                                     host(srt), k, act="silu_mul", x_dtype=xdt, sf_layout=sfl)["y"]
+    ref = oracle.grouped_gemm_qnvfp4(xb, "token", wa, sa, d["g1"], host(offs),
+                                     host(srt), k, act="silu_mul", x_dtype=xdt, sf_layout=sfl, w_layout=wl)["y"]
     assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 decode H={H} {xdt}")
 
 
@@ -302,9 +311,10 @@ def test_nvfp4_n_not_multiple_of_prefill_tile(I, sched):
     assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 N={2 * I} {sched}")
 
 
-@pytest.mark.parametrize("xdt,sfl", [("bf16", "rows"), ("f16", "rows"), ("f16", "quads")])
+@pytest.mark.parametrize("xdt,sfl,wl", [("bf16", "rows", "rows"), ("f16", "rows", "rows"), ("f16", "quads", "rows"),
+                                        ("f16", "quads", "tiled")])
 @pytest.mark.parametrize("act", ["silu_mul", "none"])
-def test_nvfp4_decode_several_items_per_wave(act, xdt, sfl):
+def test_nvfp4_decode_several_items_per_wave(act, xdt, sfl, wl):
     # More 4-row tiles x column blocks than the streaming schedule has waves,
     # so each wave runs several items back to back, with K / 512 = 3 (an odd
     # number of 4-chunk groups per item) and ragged last tiles.
@@ -312,11 +322,12 @@ def test_nvfp4_decode_several_items_per_wave(act, xdt, sfl):
     d = synth.nvfp4_moe(47, T, E, k, H, I, routing="repeat")
     xg, xb = _xin(d["x"], xdt)
     sg, sa = _sf(d["s1"], sfl)
+    wg, wa = _w(d["w1"], wl)
     offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
-    y = mq.grouped_gemm_qnvfp4(xg, dev(d["w1"]), sg, dev(d["g1"]), offs, srt, k,
+    y = mq.grouped_gemm_qnvfp4(xg, wg, sg, dev(d["g1"]), offs, srt, k,
                                act=act, out_dtype=torch.float32, sched="decode")
-    ref = oracle.grouped_gemm_qnvfp4(xb, "token", d["w1"], sa, d["g1"], host(offs),
-                                     host(srt), k, act=act, x_dtype=xdt, sf_layout=sfl)["y"]
+    ref = oracle.grouped_gemm_qnvfp4(xb, "token", wa, sa, d["g1"], host(offs),
+                                     host(srt), k, act=act, x_dtype=xdt, sf_layout=sfl, w_layout=wl)["y"]
     assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 decode many items {act}")
 
 
@@ -413,13 +424,13 @@ def test_w4a4_chain_with_quantized_activations():
 @pytest.mark.parametrize("E,N,K", [(1, 128, 64), (3, 256, 128), (2, 384, 1216), (2, 512, 2176),
                                    (1, 256, 4096)])
 @pytest.mark.parametrize("swap", [False, True])
-@pytest.mark.parametrize("sfl", ["rows", "quads"])
-def test_nvfp4_repack_bit_exact(E, N, K, swap, sfl):
+@pytest.mark.parametrize("wl,sfl", [("rows", "rows"), ("rows", "quads"), ("tiled", "quads")])
+def test_nvfp4_repack_bit_exact(E, N, K, swap, wl, sfl):
     # K/64 = 1, 2, 19, 34, 64 scale quads per row: a partial 16-tile group,
     # ragged tails and whole groups; N/128 = 1..4 row blocks.
     d = synth.nvfp4_stored_weights(60 + N + K, E, N, K)
-    w_out, sf_out = mq.nvfp4_repack(dev(d["w"]), dev(d["sf"]), swap_halves=swap, sf_layout=sfl)
-    rw, rs = oracle.repack_nvfp4(d["w"], d["sf"], swap, out_layout=sfl)
+    w_out, sf_out = mq.nvfp4_repack(dev(d["w"]), dev(d["sf"]), swap_halves=swap, sf_layout=sfl, w_layout=wl)
+    rw, rs = oracle.repack_nvfp4(d["w"], d["sf"], swap, out_layout=sfl, w_layout=wl)
     assert np.array_equal(host(w_out), rw)
     assert np.array_equal(host(sf_out), rs)
 

@@ -19,9 +19,9 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def _run(idx, fc2="sorted", act="f16", sfl="quads"):
+def _run(idx, fc2="sorted", act="f16", sfl="quads", wlay="tiled"):
     import bench
-    wl = bench.Workload(idx, fc2, act, sfl)
+    wl = bench.Workload(idx, fc2, act, sfl, wlay)
     wl.step()
     torch.cuda.synchronize()
     return wl
@@ -85,13 +85,14 @@ def _nvfp4_checks(wl, n_per):
         assert np.array_equal(host(wl.xh.view(torch.int16)).view(np.uint16), xb)
     else:
         xb = d["x"]
-    h_ref = oracle.grouped_gemm_qnvfp4(xb, "token", d["w1"], wl.s1_host, d["g1"], off, srt, d["k"],
-                                       act="silu_mul", rows=rows, x_dtype=xdt, sf_layout=wl.sfl)["y"]
+    h_ref = oracle.grouped_gemm_qnvfp4(xb, "token", wl.w1_host, wl.s1_host, d["g1"], off, srt, d["k"],
+                                       act="silu_mul", rows=rows, x_dtype=xdt, sf_layout=wl.sfl,
+                                       w_layout=wl.wl)["y"]
     assert_rows_close(host(wl.h)[rows], h_ref, what="FC1 h")
     # FC2 consumes the GPU's h (per-call parity)
     hb = host(wl.h.view(torch.int16)).view(np.uint16) if xdt == "f16" else bf16_bits(wl.h)
-    y_ref = oracle.grouped_gemm_qnvfp4(hb, "sorted", d["w2"], wl.s2_host, d["g2"], off, srt, d["k"],
-                                       rows=rows, x_dtype=xdt, sf_layout=wl.sfl)["y"]
+    y_ref = oracle.grouped_gemm_qnvfp4(hb, "sorted", wl.w2_host, wl.s2_host, d["g2"], off, srt, d["k"],
+                                       rows=rows, x_dtype=xdt, sf_layout=wl.sfl, w_layout=wl.wl)["y"]
     assert_rows_close(host(wl.y)[rows], y_ref, what="FC2 y")
     out_ref = oracle.scatter_combine(host(wl.y), p2s, d["topk_weights"])
     assert_rows_close(host(wl.out), out_ref, what="combine")
@@ -110,7 +111,7 @@ def test_workload3_nvfp4_prefill_zipf():
 
 @pytest.mark.parametrize("idx", [2, 3])
 def test_nvfp4_workloads_with_bf16_activations_rows_scales(idx):
-    wl = _run(idx, act="bf16", sfl="rows")
+    wl = _run(idx, act="bf16", sfl="rows", wlay="rows")
     _nvfp4_checks(wl, n_per=1 if idx == 2 else 2)
 
 
@@ -123,8 +124,8 @@ def test_nvfp4_workloads_with_fc2_pair_epilogue(idx):
     d = wl.d
     rows = _sample_rows(off, n_per=1 if idx == 2 else 2)
     hb = host(wl.h.view(torch.int16)).view(np.uint16)
-    y_ref = oracle.grouped_gemm_qnvfp4(hb, "sorted", d["w2"], wl.s2_host, d["g2"], off, srt, d["k"], rows=rows,
-                                       x_dtype="f16", sf_layout="quads")["y"]
+    y_ref = oracle.grouped_gemm_qnvfp4(hb, "sorted", wl.w2_host, wl.s2_host, d["g2"], off, srt, d["k"], rows=rows,
+                                       x_dtype="f16", sf_layout="quads", w_layout="tiled")["y"]
     pairs = srt[rows]
     w = d["topk_weights"].reshape(-1)[pairs]
     assert_rows_close(host(wl.y)[pairs], w[:, None] * y_ref, what="FC2 pair rows")
