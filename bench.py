@@ -1,6 +1,6 @@
 """Throughput of the quantized MoE grouped-GEMM path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload {0,1,2,3,4,5,6,7}]
+    python bench.py [--steps K] [--warmup W] [--workload {0,1,...,8}]
 
 One step is one pass of the whole hot path over one batch of seeded
 synthetic input already resident in HBM:
@@ -17,6 +17,8 @@ synthetic input already resident in HBM:
      of 4 in a full W4A4 chain)
   6  FP8 block-scaled MoE projection, decode: 8 tokens, E=256, top-8,
      N=4096 K=7168: route + FP8 GEMM (weight-streaming schedule)
+  8  the complete W4A4 layer at 4's sizes from fp16 x: per-token int4 of
+     x + FC1 (SiLU) + per-row int4 of h + FC2 + combine
   7  one-shot NVFP4 weight repack of 2's gate+up weights (E=256, 4096 rows,
      K=7168) from the up-first, 128x4-swizzled-scale layout of megamoe_rm.cu
 Prints ONE JSON line: whole-path throughput, the dominant kernel's roofline
@@ -110,7 +112,24 @@ class Workload:
         nws = mq.route_workspace_bytes(T, k, E)
         self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else None
         kind = self.cfg["kind"]
-        if kind == "fp8":
+        if kind == "int4chain":
+            H, I = d["H"], d["I"]
+            self.x = _dev(d["x"])
+            self.w, self.sw = _dev(d["w"]), _dev(d["w_scale"])
+            self.w2, self.sw2 = _dev(d["w2"]), _dev(d["w2_scale"])
+            f16, u8, f32 = torch.float16, torch.uint8, torch.float32
+            self.qx = torch.empty(T, H // 2, dtype=u8, device="cuda")
+            self.sx = torch.empty(T, dtype=f32, device="cuda")
+            self.h = torch.empty(P, I, dtype=f16, device="cuda")
+            self.qh = torch.empty(P, I // 2, dtype=u8, device="cuda")
+            self.sh = torch.empty(P, dtype=f32, device="cuda")
+            self.y = torch.empty(P, H, dtype=f16, device="cuda")
+            self.out = torch.empty(T, H, dtype=f16, device="cuda")
+            self.flops = 2.0 * P * (2 * I * H + H * I)
+            self.weight_bytes = None
+            self.dtype = "int4_via_int8_mfma"
+            self.dom = ("int4_prefill", ["gemm_int4.hip", "common.h", "tile.h"], "mfma", PEAK["int8"])
+        elif kind == "fp8":
             self.a, self.sa = _dev(d["a"]), _dev(d["a_scale"])
             self.w, self.sw = _dev(d["w"]), _dev(d["w_scale"])
             self.y = torch.empty(P, d["N"], dtype=torch.bfloat16, device="cuda")
@@ -218,7 +237,17 @@ class Workload:
             if ev: ev[1].record()
             return
         offs, srt, p2s, _ = mq.moe_route_prep(self.ids, self.E, out=self.route_out, workspace=self.ws)
-        if kind == "fp8":
+        if kind == "int4chain":
+            mq.quantize_int4_rows(self.x, q=self.qx, scale=self.sx)
+            if ev: ev[0].record()
+            mq.grouped_gemm_qint4(self.qx, self.sx, self.w, self.sw, offs, srt, self.k, act="silu_mul",
+                                  out=self.h)
+            if ev: ev[1].record()
+            mq.quantize_int4_rows(self.h, q=self.qh, scale=self.sh)
+            mq.grouped_gemm_qint4(self.qh, self.sh, self.w2, self.sw2, offs, srt, self.k, a_row="sorted",
+                                  out=self.y)
+            mq.moe_scatter_combine(self.y, p2s, self.tw, out=self.out)
+        elif kind == "fp8":
             if ev: ev[0].record()
             mq.grouped_gemm_qfp8_block(self.a, self.sa, self.w, self.sw, offs, srt, self.k, out=self.y)
             if ev: ev[1].record()
@@ -269,7 +298,7 @@ class Workload:
         if kind == "fp8":
             N, K = d["N"], d["K"]
             return float(P * K + self.weight_bytes + d["a_scale"].size * 4 + P * N * 2)
-        if kind == "int4":
+        if kind in ("int4", "int4chain"):
             N, K = d["N"], d["K"]
             out = N * 2 if self.idx == 0 else N  # f16 y, or f16 h = N/2 columns
             return float(P * K // 2 + P * 4 + d["w"].size + d["w_scale"].size * 4 + P * out)
@@ -287,7 +316,7 @@ class Workload:
             return self.weight_bytes, "byte"
         if kind == "fp8":
             return 2.0 * self.T * self.k * d["N"] * d["K"], "flop"
-        if kind == "int4":
+        if kind in ("int4", "int4chain"):
             return 2.0 * self.T * self.k * d["N"] * d["K"], "flop"
         if self.idx == 2:
             return self.fc1_bytes, "byte"
@@ -311,7 +340,7 @@ def cpu_baseline(idx: int, d, budget_s: float = 10.0):
     except Exception:
         cores = os.cpu_count()
     kind = {0: "int4", 1: "fp8", 2: "nvfp4", 3: "nvfp4", 4: "int4", 5: "quant", 6: "fp8",
-            7: "repack"}[idx]
+            7: "repack", 8: "int4"}[idx]
     times = []
     if kind == "repack":
         ne = 64
@@ -361,6 +390,9 @@ def cpu_baseline(idx: int, d, budget_s: float = 10.0):
         rows = np.arange(n) if idx == 0 else np.arange(0, n, max(1, n // 64))
         sample = "the whole workload" if idx == 0 else f"{rows.size} sorted rows of FC1 (gate+up, K={d['K']})"
         work = 2.0 * rows.size * d["N"] * d["K"]
+        if idx == 8:                      # FC1 reads the oracle's own codes of x
+            d = dict(d)
+            d["a"], d["a_scale"] = oracle.quantize_int4_rows(d["x"])
         while sum(times) < budget_s and len(times) < 5:
             t = time.perf_counter()
             oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], off, srt,
@@ -434,7 +466,7 @@ def summarize_profiles(idx: int, pdir: str, steps: int = 50, warmup: int = 10):
         wl.T, wl.k, wl.E = wl.d["T"], wl.d["k"], wl.d["E"]
     d = wl.d
     tag = ("fp8_decode" if idx == 6 else None) or \
-        {"fp8": "fp8_prefill", "int4": "int4_prefill", "quant": "quant_int4_rows_reg",
+        {"fp8": "fp8_prefill", "int4": "int4_prefill", "int4chain": "int4_prefill", "quant": "quant_int4_rows_reg",
          "repack": "repack_nvfp4"}.get(cfg["kind"]) or \
         ("nvfp4_decode" if idx == 2 else "nvfp4_prefill")
     srcs = {"fp8_prefill": ["gemm_fp8.hip", "common.h", "tile.h", "pipeline.h"],

@@ -224,6 +224,33 @@ def nvfp4_moe(seed: int, T: int, E: int, k: int, H: int, I: int, *, routing="dis
     return d
 
 
+# RMS of an int4 code uniform over [-8, 7]: sqrt(mean of c^2) = sqrt(21.5)
+INT4_RMS = 4.637
+
+
+def int4_chain(seed: int, T: int, E: int, k: int, H: int, I: int):
+    """The full W4A4 layer from fp16 activations: x [T][H] fp16 from N(0,1)
+    times a per-row factor U[0.5, 2]; gate+up weights [E][2I][H/2] and down
+    weights [E][H][I/2], int4 codes uniform over [-8, 7].  Per-channel
+    weight scales are U[0.5, 1.5] / (sqrt(K) * INT4_RMS), so each GEMM keeps
+    its input's magnitude and h and y stay well inside fp16 (the U[0.005,
+    0.05] scales of the raw-int4 workloads grow activations about tenfold per
+    GEMM on random codes, which overflows fp16 by the second one).  Distinct
+    uniform ids, softmax top-k weights."""
+    r = streams(seed)
+    x = r[ROLE_ACT].standard_normal((T, H), dtype=np.float32)
+    x *= r[ROLE_ACT_SCALE].uniform(0.5, 2.0, (T, 1)).astype(np.float32)
+    s1 = 1.0 / (np.sqrt(H) * INT4_RMS)
+    s2 = 1.0 / (np.sqrt(I) * INT4_RMS)
+    return dict(x=x.astype(np.float16), topk_ids=distinct_uniform_ids(r[ROLE_ROUTING], T, k, E),
+                topk_weights=softmax_weights(r[ROLE_LOGITS], T, k),
+                w=uniform_bytes(r[ROLE_W1], (E, 2 * I, H // 2)),
+                w_scale=uniform_f32(r[ROLE_S1], (E, 2 * I), 0.5 * s1, 1.5 * s1),
+                w2=uniform_bytes(r[ROLE_W2], (E, H, I // 2)),
+                w2_scale=uniform_f32(r[ROLE_S2], (E, H), 0.5 * s2, 1.5 * s2),
+                T=T, E=E, k=k, H=H, I=I, N=2 * I, K=H)
+
+
 def nvfp4_stored_weights(seed: int, E: int, N: int, K: int):
     """NVFP4 expert weights as another runtime stores them (megamoe_rm.cu's
     in-place layout): w [E][N][K/2] uniform E2M1 code bytes and the UE4M3
@@ -255,6 +282,9 @@ WORKLOADS = {
     # 2I = 4096 rows, K = H = 7168) from the up-first, 128x4-swizzled-scale
     # layout of megamoe_rm.cu
     7: dict(name="nvfp4_repack_w13_E256_N4096_K7168", kind="repack", E=256, N=4096, K=7168, swap=1),
+    # the complete W4A4 layer at config 4's sizes from fp16 activations:
+    # per-token int4 of x, FC1 (SiLU), per-row int4 of h, FC2, combine
+    8: dict(name="w4a4_int4_chain_mixtral_T8192", kind="int4chain", T=8192, E=8, k=2, H=4096, I=14336),
 }
 
 
@@ -282,4 +312,6 @@ def workload(idx: int):
         return fp8_moe(seed, c["T"], c["E"], c["k"], c["N"], c["K"])
     if idx == 7:
         return nvfp4_stored_weights(seed, c["E"], c["N"], c["K"])
+    if idx == 8:
+        return int4_chain(seed, c["T"], c["E"], c["k"], c["H"], c["I"])
     raise KeyError(idx)

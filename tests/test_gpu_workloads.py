@@ -183,3 +183,26 @@ def test_workload7_nvfp4_repack_sampled_experts():
         rw, rs = oracle.repack_nvfp4(d["w"][e:e + 1], d["sf"][e:e + 1], bool(wl.cfg["swap"]))
         assert np.array_equal(host(wl.w_out[int(e)]), rw[0]), e
         assert np.array_equal(host(wl.sf_out[int(e)]), rs[0]), e
+
+
+def test_workload8_w4a4_chain_from_fp16():
+    # every step of the chain against the oracle applied to the GPU's own
+    # input of that step; both quantizations bit-exact on sampled rows
+    wl = _run(8)
+    off, srt, p2s, _ = _check_route(wl)
+    d = wl.d
+    rows = _sample_rows(off, n_per=2, max_experts=3)
+    toks = np.unique(np.concatenate([[0, wl.T - 1], srt[rows] // wl.k]))
+    ref_q, ref_s = oracle.quantize_int4_rows(d["x"][toks])
+    assert np.array_equal(host(wl.qx)[toks], ref_q) and np.array_equal(host(wl.sx)[toks], ref_s)
+    qx, sx = host(wl.qx), host(wl.sx)
+    h_ref = oracle.grouped_gemm_qint4(qx, sx, "token", d["w"], d["w_scale"], off, srt, d["k"],
+                                      act="silu_mul", rows=rows)["y"]
+    assert_rows_close(host(wl.h)[rows], h_ref, what="FC1 h")
+    hq_ref, hs_ref = oracle.quantize_int4_rows(host(wl.h)[rows].astype(np.float16))
+    assert np.array_equal(host(wl.qh)[rows], hq_ref) and np.array_equal(host(wl.sh)[rows], hs_ref)
+    y_ref = oracle.grouped_gemm_qint4(host(wl.qh), host(wl.sh), "sorted", d["w2"], d["w2_scale"], off, srt,
+                                      d["k"], rows=rows)["y"]
+    assert_rows_close(host(wl.y)[rows], y_ref, what="FC2 y")
+    assert_rows_close(host(wl.out), oracle.scatter_combine(host(wl.y), p2s, d["topk_weights"]),
+                      what="combine")
