@@ -7,9 +7,10 @@
 //   offsets[e] + (pairs of e in earlier chunks) + (pairs of e earlier in the
 //   same chunk),
 // which is the pair's rank among all earlier pairs of its expert: the unique
-// stable order.  Inside a chunk the rank is built per wave with ballots
-// (one round per distinct expert in the wave) plus the counts of earlier
-// waves.  One chunk needs one workgroup:
+// stable order.  Inside a chunk the rank is built per wave (ballots, one
+// round per distinct expert, for E <= 16; otherwise a 64-step comparison
+// with every lane's expert) plus the counts of earlier waves.  One chunk
+// needs one workgroup:
 //   * P <= kChunk: a single fused kernel counts, scans and scatters.
 //   * otherwise:   route_count writes per-chunk counts to the workspace and
 //                  route_scatter (one workgroup per chunk) derives every
@@ -40,6 +41,25 @@ __device__ __forceinline__ int wave_rank(int e, bool valid, unsigned char* wcnt_
     if (lane == leader) wcnt_w[le] = (unsigned char)__popcll(m);
     active &= ~m;
   }
+  return rank;
+}
+
+// The same rank and counts by comparing the lane's expert with every lane's
+// expert, read as a wave-uniform value: 64 steps whatever the number of
+// distinct experts in the wave, where the ballot form takes one round (with
+// a cross-lane shuffle) per distinct expert.  The first lane of each expert
+// writes its count.
+__device__ __forceinline__ int wave_rank_scan(int e, bool valid, unsigned char* wcnt_w, int lane) {
+  const int key = valid ? e : -1;
+  int rank = 0, cnt = 0;
+#pragma unroll 16
+  for (int j = 0; j < 64; ++j) {
+    const int ej = __builtin_amdgcn_readlane(key, j);
+    const int same = ej == key;
+    rank += (j < lane) & same;
+    cnt += same;
+  }
+  if (valid && rank == 0) wcnt_w[e] = (unsigned char)cnt;
   return rank;
 }
 
@@ -153,7 +173,9 @@ __global__ __launch_bounds__(kChunk) void route_scatter(const int* __restrict__ 
   }
 
   // Rank inside the chunk: rank in the wave plus the counts of earlier waves.
-  const int r_wave = wave_rank(e, valid, wcnt + wid * E, lane);
+  // few experts: one ballot round each; many: the fixed 64-step scan
+  const int r_wave = E <= 16 ? wave_rank(e, valid, wcnt + wid * E, lane)
+                             : wave_rank_scan(e, valid, wcnt + wid * E, lane);
   __syncthreads();
   if (i < P) {
     int pos = -1;
