@@ -38,18 +38,21 @@ __device__ __forceinline__ float swiglu(float g, float u, float limit) {
 }
 
 // ------------------------------------------------------------------ prefill
-// CU work unit: a workgroup of 4 waves owns a 128 (activation rows) x 256
-// (weight rows; for SILU_MUL 128 gate rows + the 128 matching up rows)
-// tile and walks K in steps of 64 through a 3-stage LDS ring (75 KB), so
-// two workgroups share a CU and their phases (dequantization on the VALU,
-// MFMAs) interleave.  Stage layout (25 KB):
+// CU work unit: a workgroup of NW waves owns a 128 (activation rows) x
+// 64*NW (weight rows; for SILU_MUL 32*NW gate rows + the matching up rows)
+// tile and walks K in steps of 64 through an LDS ring.  Stage layout:
 //   A  128 rows x 128 bytes (64 bf16), 16-byte chunks swizzled as in the
 //      FP8 kernel;
-//   B  256 rows x 32 packed bytes (64 E2M1 codes), the 16-byte chunk c of
-//      row r at position c ^ ((r >> 3) & 1);
-//   S  256 rows x 4 scale bytes.
+//   B  64*NW rows x 32 packed bytes (64 E2M1 codes), the 16-byte chunk c
+//      of row r at position c ^ ((r >> 3) & 1);
+//   S  64*NW rows x 4 scale bytes.
 // Wave wn owns 64 weight rows (two 32-row MFMA operands) against all 128
 // activation rows, so every weight code is dequantized once per tile.
+//   NW = 8 (N % 512 == 0): 512 weight rows, a 4-stage ring (136 KB), one
+//          workgroup per CU.  The gathered activation tile, two thirds of
+//          a 256-row tile's copy stream, feeds twice the MFMA work.
+//   NW = 4: 256 weight rows, a 3-stage ring (75 KB), two workgroups per CU
+//          whose phases (dequantization on the VALU, MFMAs) interleave.
 //
 // K slots: in a K step, MFMA lane l (slice l/32) takes the codes
 // [32*slice, +32) of its weight row - one 16-byte LDS read, two scale bytes
@@ -57,34 +60,46 @@ __device__ __forceinline__ float swiglu(float g, float u, float limit) {
 // uses the same slots: slice `slice`, sub-step s = logical chunk 4*slice+s
 // of the row's 128 bytes.
 namespace pf {
-constexpr int kM = 128, kN = 256;
-constexpr int kStages = 3;
+constexpr int kM = 128;
 constexpr int kABytes = kM * 128;
-constexpr int kBBytes = kN * 32;
-constexpr int kSBytes = kN * 4;
-constexpr int kStageBytes = kABytes + kBBytes + kSBytes;
-constexpr int kThreads = 256;
+template <int NW> struct Geo {
+  static constexpr int kN = 64 * NW;
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kStages = NW == 8 ? 4 : 3;
+  static constexpr int kBBytes = kN * 32;
+  static constexpr int kSBytes = kN * 4;
+  static constexpr int kStageBytes = kABytes + kBBytes + kSBytes;
+  static constexpr int kACopies = 16 / NW;  // A copies (8 rows each) per wave and stage
+  static constexpr int kPer = kACopies + 3;  // copies per wave and stage
+};
 }  // namespace pf
 
 // PAIR (act NONE only): megamoe_rm.cu's fc2_rm epilogue.  Sorted row s is
 // scaled by the top-k weight of its pair p = sorted_ids[s] and written to
 // output row p instead of s.
 // H16: the activations are binary16 (dequant and MFMA in fp16), else bf16.
-template <int OUT, bool SILU, bool PAIR, bool H16>
-__global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
+template <int OUT, bool SILU, bool PAIR, bool H16, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void nvfp4_prefill(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale,
     const int* __restrict__ offsets, const int* __restrict__ sorted_ids, int topk, int E, int P, int N,
     int K, void* __restrict__ out, float limit, const float* __restrict__ pair_w, int sf_quads, int w_tiled) {
   static_assert(!(SILU && PAIR), "pair-ordered output is for act NONE");
-  using namespace pf;
+  static_assert(NW == 4 || NW == 8, "tile widths");
+  using pf::kM;
+  using pf::kABytes;
+  using G_ = pf::Geo<NW>;
+  constexpr int kN = G_::kN, kThreads = G_::kThreads, kStages = G_::kStages;
+  constexpr int kBBytes = G_::kBBytes, kStageBytes = G_::kStageBytes;
+  constexpr int kACopies = G_::kACopies, kPer = G_::kPer;
+  constexpr int kHalf = kN / 2;  // SILU_MUL: gate rows of the tile
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
   __shared__ int tile_start[kMaxExperts + 1];
   __shared__ int sched_scratch[2 * kMaxWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wn = tid >> 6;
   const int I = N / 2;
-  const int n_tiles = SILU ? I / 128 : N / kN;
+  const int n_tiles = SILU ? I / kHalf : N / kN;
   const int G = K / 64;
   const int64_t xrow_bytes = (int64_t)K * 2, wrow_bytes = K / 2, srow_bytes = K / 16;
   sched_build(tile_start, sched_scratch, offsets, E, P, kM, n_tiles);
@@ -94,7 +109,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
   const int key = frag_key(lane);
   // Weight rows of this lane's two operands (row index in the B tile).
   const int brow0 = SILU ? 32 * wn + l32 : 64 * wn + l32;
-  const int brow1 = SILU ? 128 + 32 * wn + l32 : 64 * wn + 32 + l32;
+  const int brow1 = SILU ? kHalf + 32 * wn + l32 : 64 * wn + 32 + l32;
   const int boff0 = kABytes + brow0 * 32 + ((slice ^ ((brow0 >> 3) & 1)) << 4);
   const int boff1 = kABytes + brow1 * 32 + ((slice ^ ((brow1 >> 3) & 1)) << 4);
   const int soff0 = kABytes + kBBytes + brow0 * 4 + slice * 2;
@@ -105,11 +120,11 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
 
   for (int item = xcd_logical_id(blockIdx.x, gridDim.x); item < total; item += gridDim.x) {
     const Tile t = sched_tile<4>(tile_start, offsets, E, P, kM, n_tiles, item);
-    // DMA sources.  A: wave wn moves rows 8q + lane/8 for q = 4wn + j.
-    const uint8_t* pa[4];
+    // DMA sources.  A: wave wn moves rows 8q + lane/8 for q = kACopies*wn + j.
+    const uint8_t* pa[kACopies];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = 4 * wn + j;
+    for (int j = 0; j < kACopies; ++j) {
+      const int q = kACopies * wn + j;
       const int r = 8 * q + (lane >> 3);
       const int s = t.row0 + min(r, t.rows - 1);
       pa[j] = reinterpret_cast<const uint8_t*>(x) + a_row_of(s, sorted_ids, a_sorted, topk, rows_a) * xrow_bytes +
@@ -117,7 +132,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
     }
     auto grow = [&](int r) __attribute__((always_inline)) {
       if (!SILU) return (int64_t)t.e * N + (int64_t)t.nt * kN + r;
-      return (int64_t)t.e * N + (r < 128 ? (int64_t)t.nt * 128 + r : (int64_t)I + t.nt * 128 + (r - 128));
+      return (int64_t)t.e * N + (r < kHalf ? (int64_t)t.nt * kHalf + r : (int64_t)I + t.nt * kHalf + (r - kHalf));
     };
     // B: wave wn moves rows 64wn + 32j + lane/2 (chunk position lane%2);
     // S: rows 64wn + lane.
@@ -143,18 +158,17 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
     const uint8_t* ps = sf_quads ? w_sf + (int64_t)t.e * N * srow_bytes + (s_row - (int64_t)t.e * N) * 4
                                  : w_sf + s_row * srow_bytes;
     const int64_t s_step = sf_quads ? (int64_t)N * 4 : 4;
-    const uint32_t lds_a = lds_addr(smem + wn * 4096);
+    const uint32_t lds_a = lds_addr(smem + wn * (kACopies * 1024));
     const uint32_t lds_b = lds_addr(smem + kABytes + wn * 2048);
     const uint32_t lds_s = lds_addr(smem + kABytes + kBBytes + wn * 256);
     auto issue = [&](int g) __attribute__((always_inline)) {
       const uint32_t st = (uint32_t)((g % kStages) * kStageBytes);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma16(pa[j] + (int64_t)g * 128, lds_a + st + j * 1024);
+      for (int j = 0; j < kACopies; ++j) dma16(pa[j] + (int64_t)g * 128, lds_a + st + j * 1024);
 #pragma unroll
       for (int j = 0; j < 2; ++j) dma16(pb[j] + (int64_t)g * b_step, lds_b + st + j * 1024);
       dma4(ps + (int64_t)g * s_step, lds_s + st);
     };
-    constexpr int kPer = 7;  // loads per wave per stage
 
     v16f acc[2][4];
 #pragma unroll
@@ -175,7 +189,9 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
     auto k_loop = [&](auto ny_c) __attribute__((always_inline)) {
       constexpr int NY = decltype(ny_c)::value;
       for (int g = 0; g < G; ++g) {
-        if (last_issued - g >= 1) wait_vmcnt<kPer>();
+        // stage g has landed once at most the stages issued after it remain
+        if (kStages > 3 && last_issued - g >= 2) wait_vmcnt<2 * kPer>();
+        else if (last_issued - g >= 1) wait_vmcnt<kPer>();
         else wait_vmcnt<0>();
         raw_barrier();  // stage g visible to all waves; stage g-1 is free
         if (g + kStages - 1 < G) {
@@ -228,7 +244,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void nvfp4_prefill(
     // Epilogue: global scale (and the SiLU-gated product), output tile
     // through LDS, then 16-byte stores along output rows.
     typedef typename OutT<OUT>::T T;
-    constexpr int kCols = SILU ? 128 : 256;
+    constexpr int kCols = SILU ? kHalf : kN;
     constexpr int kOutPitch = kCols * (int)sizeof(T) + 16;
     constexpr bool kStaged = kM * kOutPitch <= kStages * kStageBytes;  // else: f32, direct stores
     raw_barrier();  // all waves are done with the ring
@@ -668,12 +684,22 @@ hipError_t go(const GroupedArgs& g, bool decode, const uint16_t* x, const uint8_
                          g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P, g.N,
                          g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads, g.w_tiled);
   } else {
+    // 512-row tiles (one 8-wave workgroup per CU) when N allows, else
+    // 256-row tiles (two 4-wave workgroups per CU)
     const int64_t mt_ub = (g.P + pf::kM - 1) / pf::kM + std::min<int64_t>(g.E, g.P);
-    const int64_t items_ub = mt_ub * (g.N / pf::kN);
-    const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus * 2);
-    hipLaunchKernelGGL((nvfp4_prefill<OUT, SILU, PAIR, H16>), dim3(grid), dim3(pf::kThreads), 0, stream, x,
-                       g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P,
-                       g.N, g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads, g.w_tiled);
+    if (g.N % pf::Geo<8>::kN == 0) {
+      const int64_t items_ub = mt_ub * (g.N / pf::Geo<8>::kN);
+      const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus);
+      hipLaunchKernelGGL((nvfp4_prefill<OUT, SILU, PAIR, H16, 8>), dim3(grid), dim3(pf::Geo<8>::kThreads), 0, stream,
+                         x, g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P,
+                         g.N, g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads, g.w_tiled);
+    } else {
+      const int64_t items_ub = mt_ub * (g.N / pf::Geo<4>::kN);
+      const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus * 2);
+      hipLaunchKernelGGL((nvfp4_prefill<OUT, SILU, PAIR, H16, 4>), dim3(grid), dim3(pf::Geo<4>::kThreads), 0, stream,
+                         x, g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P,
+                         g.N, g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads, g.w_tiled);
+    }
   }
   return hipGetLastError();
 }
@@ -684,7 +710,7 @@ hipError_t dispatch(const GroupedArgs& g, const uint16_t* x, const uint8_t* w, c
   // The streaming schedule when asked for, under AUTO while experts average
   // fewer than 16 rows, and whenever N is not a multiple of the prefill
   // tile (256), which the prefill schedule cannot cover.
-  const bool decode = g.sched == 1 || g.N % pf::kN != 0 || (g.sched == 0 && g.P < (int64_t)16 * g.E);
+  const bool decode = g.sched == 1 || g.N % pf::Geo<4>::kN != 0 || (g.sched == 0 && g.P < (int64_t)16 * g.E);
   if (g.silu_mul) {
     switch (g.out_kind) {
       case OUT_F16: return go<OUT_F16, true, false, H16>(g, decode, x, w, w_sf, w_gscale, stream);

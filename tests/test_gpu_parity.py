@@ -242,12 +242,14 @@ def _w(w_rows, wl):
     return dev(a), a
 
 
+@pytest.mark.parametrize("I", [128, 256])
 @pytest.mark.parametrize("wl,sfl", [("rows", "rows"), ("rows", "quads"), ("tiled", "quads")])
 @pytest.mark.parametrize("xdt", ["bf16", "f16"])
 @pytest.mark.parametrize("sched", ["prefill", "decode"])
 @pytest.mark.parametrize("act", ["none", "silu_mul"])
-def test_nvfp4(sched, act, xdt, wl, sfl):
-    T, E, k, H, I = 150, 5, 2, 256, 128
+def test_nvfp4(sched, act, xdt, wl, sfl, I):
+    # N = 2I = 256: the 256-row prefill tile; N = 512: the 512-row tile
+    T, E, k, H = 150, 5, 2, 256
     d = synth.nvfp4_moe(41, T, E, k, H, I, routing="repeat")
     xg, xb = _xin(d["x"], xdt)
     sg, sa = _sf(d["s1"], sfl)
