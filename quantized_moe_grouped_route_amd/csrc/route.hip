@@ -135,19 +135,37 @@ __global__ __launch_bounds__(kChunk) void route_scatter(const int* __restrict__ 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = blockIdx.x, nchunks = (P + kChunk - 1) / kChunk;
 
+  __shared__ int winv[kWaves];  // per wave: ids outside [0, E) other than -1
   for (int j = tid; j < kWaves * E; j += kChunk) wcnt[j] = 0;
   const int i = b * kChunk + tid;
   const int e = i < P ? ids[i] : -1;
   const bool valid = i < P && valid_id(e, E);
+  __syncthreads();  // wcnt cleared
+
+  // Rank in the wave and the wave's count of each expert (few experts: one
+  // ballot round each; many: the fixed 64-step scan), and the wave's
+  // invalid ids.
+  const int r_wave = E <= 16 ? wave_rank(e, valid, wcnt + wid * E, lane)
+                             : wave_rank_scan(e, valid, wcnt + wid * E, lane);
+  const unsigned long long bad = __ballot(!valid && e != -1);
+  if (lane == 0) winv[wid] = (int)__popcll(bad);
+  __syncthreads();  // wcnt and winv complete
 
   if (FUSED) {
-    for (int x = tid; x <= E; x += kChunk) {
-      tot[x] = 0;
+    // Expert counts as sums of the wave counts: no atomics on shared
+    // counters (with one expert every pair would hit the same one).
+    for (int x = tid; x < E; x += kChunk) {
+      int sum = 0;
+      for (int w = 0; w < kWaves; ++w) sum += wcnt[w * E + x];
+      tot[x] = sum;
       base[x] = 0;  // no earlier chunks
     }
-    __syncthreads();
-    if (valid) atomicAdd(&tot[e], 1);
-    else if (i < P && e != -1) atomicAdd(&tot[E], 1);
+    if (tid == 0) {
+      int sum = 0;
+      for (int w = 0; w < kWaves; ++w) sum += winv[w];
+      tot[E] = sum;
+      base[E] = 0;
+    }
   } else {
     // tot[x] = sum over all chunks, base[x] = sum over chunks before b.
     for (int x = tid; x <= E; x += kChunk) {
@@ -173,9 +191,6 @@ __global__ __launch_bounds__(kChunk) void route_scatter(const int* __restrict__ 
   }
 
   // Rank inside the chunk: rank in the wave plus the counts of earlier waves.
-  // few experts: one ballot round each; many: the fixed 64-step scan
-  const int r_wave = E <= 16 ? wave_rank(e, valid, wcnt + wid * E, lane)
-                             : wave_rank_scan(e, valid, wcnt + wid * E, lane);
   __syncthreads();
   if (i < P) {
     int pos = -1;
