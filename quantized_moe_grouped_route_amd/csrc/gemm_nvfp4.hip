@@ -338,8 +338,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void nvfp4_prefill(
 //   otherwise, a step is one chunk: 16 rows x 64 weight bytes per group,
 //     4 rows x 256 activation bytes (rows past the tile repeat its last
 //     row), 32 rows x 8 scale bytes.
-// The stream runs across item boundaries; tile lookups are wave-uniform
-// scalar loads, so they never wait on the vector memory counter.
+// The stream runs across item boundaries.  Item metadata is looked up for
+// 64 items at a time (one per lane) and read from a lane at each switch.
 //
 // MFMA 16x16x32 bf16 with the weights as the 16-row operand: lane l holds
 // weight row l%16, K slots [8(l/16), +8) of each sub-step; the activation
@@ -356,37 +356,6 @@ template <bool WIDE> constexpr int slot_bytes() { return WIDE ? 4096 : 3328; }
 template <bool WIDE>
 constexpr int wave_bytes() { return depth<WIDE>() * slot_bytes<WIDE>() + (WIDE ? 8192 + 2048 : 0); }
 }  // namespace dc
-
-typedef __attribute__((address_space(4))) const int cint_t;
-typedef __attribute__((address_space(4))) const float cfloat_t;
-// Wave-uniform reads through the constant address space: scalar loads.
-__device__ __forceinline__ int ld_uniform(const int* p, int i) { return ((cint_t*)(p))[i]; }
-__device__ __forceinline__ float ld_uniform(const float* p, int i) { return ((cfloat_t*)(p))[i]; }
-
-struct UTile {
-  int e, row0, rows, nt;
-};
-// Work item -> tile, every field wave-uniform (same numbering as sched_tile
-// with one m-tile per group: m-tile major, then n-blocks).
-__device__ __forceinline__ UTile uniform_tile(const int* tile_start, const int* __restrict__ offsets,
-                                              int E, int P, int bm, int n_tiles, int w) {
-  int bl = 0, bh = E - 1;
-  while (bl < bh) {
-    const int mid = (bl + bh + 1) >> 1;
-    if (__builtin_amdgcn_readfirstlane(tile_start[mid]) <= w) bl = mid; else bh = mid - 1;
-  }
-  const int e = __builtin_amdgcn_readfirstlane(bl);
-  const int local = w - __builtin_amdgcn_readfirstlane(tile_start[e]);
-  const int lo = min(max(ld_uniform(offsets, e), 0), P);
-  const int hi = min(max(ld_uniform(offsets, e + 1), lo), P);
-  const int mt = local / n_tiles;
-  UTile t;
-  t.e = e;
-  t.nt = local - mt * n_tiles;
-  t.row0 = lo + mt * bm;
-  t.rows = min(bm, hi - lo - mt * bm);
-  return t;
-}
 
 // s_waitcnt vmcnt(n) for a run-time n in [0, 15]
 __device__ __forceinline__ void wait_vm(int n) {
@@ -442,7 +411,8 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
   const int wid = blockIdx.x * dc::kWaves + wv;
   if (wid >= active) return;
   const int steps = K / (128 * CPS);                                 // per item
-  const int nq = ((total - wid + active - 1) / active) * steps;     // steps of this wave
+  const int n_items = (total - wid + active - 1) / active;          // items of this wave
+  const int nq = n_items * steps;                                    // steps of this wave
   const int64_t wrow = K / 2, srow = K / 16;
   // scale bytes per copy step: a superchunk (WIDE, 8 quads) or a step (2 quads)
   const int64_t s_adv = sf_quads ? (WIDE ? 8 : 2) * (int64_t)N * 4 : (WIDE ? 32 : 8);
@@ -456,14 +426,75 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
   const uint8_t* sbuf = xbuf + 8192;          // WIDE: [2][1 KB]
   const uint32_t lxb = lb + D * kSlot, lsb = lxb + 8192;
 
+  // ---- item metadata.  The wave's j-th item is wid + j * active.  Lane l
+  // of table (b & 1) holds item 64b + l: its expert, first sorted row, row
+  // count, column block, activation rows and global scale, found by all
+  // lanes at once (a binary search over tile_start, then vector loads).  An
+  // item switch then reads one lane instead of waiting on a search and
+  // dependent loads while the copy ring drains.  The copy cursor runs
+  // at most D steps (so at most D items) ahead of the compute cursor, so two
+  // tables suffice; a wave with more than 64 items reloads one per 64.
+  struct Meta {
+    int e, row0, rows, nt, ar[dc::kM];
+    float gs;
+  };
+  Meta tab0, tab1;
+  auto load_meta = [&](int b) __attribute__((always_inline)) {
+    Meta m;
+    m.e = 0, m.row0 = 0, m.rows = 1, m.nt = 0, m.gs = 0.f;
+#pragma unroll
+    for (int r = 0; r < dc::kM; ++r) m.ar[r] = 0;
+    const int j = 64 * b + lane;
+    if (j < n_items) {
+      const int item = wid + j * active;
+      int bl = 0, bh = E - 1;
+      while (bl < bh) {
+        const int mid = (bl + bh + 1) >> 1;
+        if (tile_start[mid] <= item) bl = mid; else bh = mid - 1;
+      }
+      const int local = item - tile_start[bl];
+      const int lo = min(max(offsets[bl], 0), P);
+      const int hi = min(max(offsets[bl + 1], lo), P);
+      const int mt = local / n_blocks;
+      m.e = bl;
+      m.nt = local - mt * n_blocks;
+      m.row0 = lo + mt * dc::kM;
+      m.rows = min(dc::kM, hi - lo - mt * dc::kM);
+#pragma unroll
+      for (int r = 0; r < dc::kM; ++r) {
+        const int sp = m.row0 + (r < m.rows ? r : m.rows - 1);
+        const int64_t a = (a_sorted || sorted_ids == nullptr) ? (int64_t)sp : (int64_t)(sorted_ids[sp] / topk);
+        m.ar[r] = (a < 0 || a >= rows_a) ? 0 : (int)a;
+      }
+      m.gs = w_gscale[bl];
+    }
+    if (b & 1) tab1 = m; else tab0 = m;
+  };
+  // item j's metadata, wave-uniform
+  auto meta = [&](int j) __attribute__((always_inline)) {
+    const int l = j & 63;
+    const bool odd = (j >> 6) & 1;
+    Meta m;
+    m.e = __builtin_amdgcn_readlane(odd ? tab1.e : tab0.e, l);
+    m.row0 = __builtin_amdgcn_readlane(odd ? tab1.row0 : tab0.row0, l);
+    m.rows = __builtin_amdgcn_readlane(odd ? tab1.rows : tab0.rows, l);
+    m.nt = __builtin_amdgcn_readlane(odd ? tab1.nt : tab0.nt, l);
+#pragma unroll
+    for (int r = 0; r < dc::kM; ++r) m.ar[r] = __builtin_amdgcn_readlane(odd ? tab1.ar[r] : tab0.ar[r], l);
+    m.gs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, odd ? tab1.gs : tab0.gs), l));
+    return m;
+  };
+  load_meta(0);
+
   // ---- copy cursor: sources of the next (item, step) to copy
-  int is_item = wid, is_st = 0, is_rows = 0, is_sc = 0;
+  int is_j = 0, is_st = 0, is_rows = 0, is_sc = 0;
   // WIDE: weight row base of group grp, half h at wsrc[2 grp + h]
   const uint8_t* wsrc[4];
   const uint8_t *sx = nullptr, *ss = nullptr;
   int64_t xrow[dc::kM];
-  auto set_sources = [&](int item) __attribute__((always_inline)) {
-    const UTile t = uniform_tile(tile_start, offsets, E, P, dc::kM, n_blocks, item);
+  auto set_sources = [&](int j) __attribute__((always_inline)) {
+    if (j > 0 && (j & 63) == 0) load_meta(j >> 6);
+    const Meta t = meta(j);
     const int b0 = SILU ? t.nt * 16 : t.nt * 32;
     const int b1 = SILU ? I + t.nt * 16 : t.nt * 32 + 16;
     const int64_t e0 = (int64_t)t.e * N;
@@ -491,14 +522,7 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
       wsrc[0] = w + (e0 + b0 + l16) * wrow + g * 16;
       wsrc[2] = w + (e0 + b1 + l16) * wrow + g * 16;
     }
-    int ar[dc::kM];
-#pragma unroll
-    for (int r = 0; r < dc::kM; ++r) {
-      const int sp = t.row0 + (r < t.rows ? r : t.rows - 1);
-      const int64_t a = (a_sorted || sorted_ids == nullptr) ? (int64_t)sp
-                                                            : (int64_t)(ld_uniform(sorted_ids, sp) / topk);
-      ar[r] = (a < 0 || a >= rows_a) ? 0 : (int)a;
-    }
+    const int* ar = t.ar;
     is_rows = t.rows;
     if (WIDE) {
 #pragma unroll
@@ -554,17 +578,16 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
     ops_ring = (ops_ring & ~(15u << (4 * slot))) | ((uint32_t)ops << (4 * slot));
     if (++is_st == steps) {
       is_st = 0;
-      is_item += active;
-      if (is_item < total) set_sources(is_item);
+      if (++is_j < n_items) set_sources(is_j);
     }
   };
 
-  set_sources(is_item);
+  set_sources(is_j);
   const int npre = nq < D ? nq : D;
   for (int i = 0; i < npre; ++i) issue(i);
 
   // ---- compute cursor
-  int cs_item = wid, st = 0, cs_sc = 0, cbuf = 0;
+  int cs_j = 0, st = 0, cs_sc = 0, cbuf = 0;
   v4f acc0 = v4f{}, acc1 = v4f{};
   const int xr = l16 & 3;                 // activation row of MFMA column l16
   const int wkey = (l16 >> 1) & 7;        // WIDE weight swizzle of row l16
@@ -636,8 +659,8 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
     if (++st == steps) {
       // acc value i of lane l: weight row 4(l/16)+i of each 16-row group,
       // routed row l%16 of the tile.
-      const UTile t = uniform_tile(tile_start, offsets, E, P, dc::kM, n_blocks, cs_item);
-      const float gs = ld_uniform(w_gscale, t.e);
+      const Meta t = meta(cs_j);
+      const float gs = t.gs;
       typedef typename OutT<OUT>::T T;
       T* o = static_cast<T*>(out);
       if (l16 < t.rows) {
@@ -663,7 +686,7 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
       acc0 = v4f{};
       acc1 = v4f{};
       st = 0;
-      cs_item += active;
+      ++cs_j;
     }
   }
 }
