@@ -429,7 +429,15 @@ def profile_commands(idx: int, pdir: str):
         "write": pmc.format(c="WRITE_SIZE", d=f"{pdir}/write_w{idx}", r=short),
         "copy_fetch": pmc.format(c="FETCH_SIZE", d=f"{pdir}/fetch_copy", r=copy),
         "copy_write": pmc.format(c="WRITE_SIZE", d=f"{pdir}/write_copy", r=copy),
+        "counters": pmc.format(c=" ".join(COUNTERS), d=f"{pdir}/counters_w{idx}", r=short),
     }
+
+
+# One rocprofv3 pass (at most 8 SQ and 2 GRBM counters): matrix-core busy
+# cycles, the shader clock, and where the waves spend their time.
+COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY",
+            "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "GRBM_GUI_ACTIVE")
+NOMINAL_GHZ = 2.4
 
 
 def _csv_rows(path):
@@ -559,6 +567,55 @@ def summarize_profiles(idx: int, pdir: str, steps: int = 50, warmup: int = 10):
     with open(os.path.join(ROOT, "profiles", f"{name}_traffic.txt"), "w") as f:
         f.write("\n".join(txt) + "\n")
     print(f"wrote profiles/{name}_kernel_stats.md and profiles/{name}_traffic.txt")
+
+    # counters (optional pass): matrix-core utilisation and clock of the
+    # dominant kernel, per launch
+    cdir = os.path.join(pdir, f"counters_w{idx}")
+    if not os.path.isdir(cdir):
+        return
+    agent = [r for r in _csv_rows(find(f"counters_w{idx}", "agent_info")) if r.get("Name", "").startswith("gfx")][0]
+    simds, xcc = int(agent["Simd_Count"]), int(agent["Num_Xcc"])
+    by = {}
+    for r in _csv_rows(find(f"counters_w{idx}", "counter_collection")):
+        if _short_name(r["Kernel_Name"]) != tag:
+            continue
+        d = by.setdefault(int(r["Dispatch_Id"]), {"_r": r})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    disp = [by[k] for k in sorted(by)]
+    disp = [d for i, d in enumerate(disp) if i % per_step == which]
+    if not disp:
+        raise SystemExit(f"no {tag} launches in {cdir}")
+
+    def avg(key):
+        return float(np.mean([d[key] for d in disp]))
+    dur_s = float(np.mean([(int(d["_r"]["End_Timestamp"]) - int(d["_r"]["Start_Timestamp"])) * 1e-9 for d in disp]))
+    gui = avg("GRBM_GUI_ACTIVE") / xcc          # shader cycles of one XCD over the launch
+    busy = avg("SQ_VALU_MFMA_BUSY_CYCLES") / simds
+    ctxt = [f"kernel: {tag}", f"workload: {cfg['name']}",
+            f"kernel_sources: {' '.join(srcs)}",
+            f"kernel_sources_sha256_16: {_sources_digest(srcs)}",
+            f"launches_counted: {len(disp)}; launch {which + 1} of {per_step} per step",
+            f"agent: {agent['Name']}, {simds} SIMDs, {xcc} XCDs",
+            f"duration_us_per_launch: {dur_s * 1e6:.1f} (counter run)"]
+    ctxt += [f"{k.lower()}_per_launch: {avg(k):.0f}" for k in COUNTERS]
+    trace_s = float(np.mean(dur_us)) * 1e-6  # timed launches of the kernel-trace run
+    ctxt += [f"duration_us_per_launch_kernel_trace: {trace_s * 1e6:.1f}",
+             f"mfma_busy_cycles_per_simd: {busy:.0f}",
+             f"mfma_busy_fraction_at_{NOMINAL_GHZ}ghz: {busy / (trace_s * NOMINAL_GHZ * 1e9):.3f} "
+             f"(busy cycles per SIMD / (kernel-trace duration x nominal clock))",
+             "GRBM_GUI_ACTIVE counts the whole counter window; the next two figures hold only where the "
+             "launch is much longer than the counter run's dispatch overhead:",
+             f"shader_clock_ghz: {gui / dur_s / 1e9:.3f} (GRBM_GUI_ACTIVE / XCDs / counter-run duration)",
+             f"mfma_busy_fraction_of_active_cycles: {busy / gui:.3f} "
+             f"(SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / GRBM_GUI_ACTIVE per XCD)",
+             f"wave_time_waiting_fraction: {avg('SQ_WAIT_INST_ANY') / avg('SQ_WAVE_CYCLES'):.3f} "
+             f"(SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)",
+             f"wave_time_valu_fraction: {avg('SQ_ACTIVE_INST_VALU') / avg('SQ_WAVE_CYCLES'):.3f}",
+             f"wave_time_lds_fraction: {avg('SQ_ACTIVE_INST_LDS') / avg('SQ_WAVE_CYCLES'):.3f}",
+             "command (from the repository root, TMPDIR=/tmp):", f"  {cmds['counters']}"]
+    with open(os.path.join(ROOT, "profiles", f"{name}_counters.txt"), "w") as f:
+        f.write("\n".join(ctxt) + "\n")
+    print(f"wrote profiles/{name}_counters.txt")
 
 
 def main():
