@@ -333,6 +333,25 @@ def test_nvfp4_decode_several_items_per_wave(act, xdt, sfl, wl):
     assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 decode many items {act}")
 
 
+@pytest.mark.parametrize("H", [512, 384])
+def test_nvfp4_decode_more_than_64_items_per_wave(H):
+    # 8192 pairs over 8 experts x 128 column blocks: about 128 items per
+    # streaming wave, so each wave reloads its per-lane item metadata table
+    # (64 items per table) while its copy ring is running.  H = 512 takes
+    # the 512-K stream, H = 384 the 128-K one.
+    T, E, k, I = 4096, 8, 2, 2048
+    d = synth.nvfp4_moe(48, T, E, k, H, I, routing="repeat")
+    xg, xb = _xin(d["x"], "f16")
+    sg, sa = _sf(d["s1"], "quads")
+    wg, wa = _w(d["w1"], "tiled")
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    y = mq.grouped_gemm_qnvfp4(xg, wg, sg, dev(d["g1"]), offs, srt, k,
+                               act="silu_mul", out_dtype=torch.float32, sched="decode")
+    ref = oracle.grouped_gemm_qnvfp4(xb, "token", wa, sa, d["g1"], host(offs), host(srt), k,
+                                     act="silu_mul", x_dtype="f16", sf_layout="quads", w_layout="tiled")["y"]
+    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"nvfp4 decode >64 items H={H}")
+
+
 def test_both_schedules_meet_tolerance():
     # decode and prefill both sum exact bf16 products in fp32; they may round
     # differently, but both must meet the tolerance on the same input.
