@@ -15,7 +15,7 @@ processing, which that kernel reads in place:
     16*i + 4*q + (c % 4).
 The repack below turns that layout into the library's linear one
 ([R][C] row-major scales, gate rows first when asked), one-shot, before the
-GEMMs run (SURVEY's cheapest path for the layout compatibility item).
+GEMMs run: a load-time conversion instead of a second set of GEMM kernels.
 
 The library also reads a second scale layout of its own, "K-quad major":
 for each group of 4 consecutive block columns (a quad, 64 values of K),
