@@ -43,6 +43,12 @@ ROUTE_CASES = [
     ("zipf_T4096", lambda r: synth.zipf_ids(r, 4096, 8, 256), 256),
     ("mixtral_T8192", lambda r: synth.distinct_uniform_ids(r, 8192, 2, 8), 8),
     ("decode_T8", lambda r: synth.distinct_uniform_ids(r, 8, 8, 256), 256),
+    # E > 16 ranks by the 64-step scan: with -1 and out-of-range ids, and
+    # with every pair of a wave on one expert
+    ("minus1_and_invalid_E64", lambda r: np.where(r.random((333, 3)) < 0.2, -1,
+                                                  r.integers(-3, 70, size=(333, 3))).astype(np.int32), 64),
+    ("one_expert_E256", lambda r: np.full((300, 3), 17, np.int32), 256),
+    ("one_expert_E256_multi_chunk", lambda r: np.full((700, 3), 200, np.int32), 256),
 ]
 
 
