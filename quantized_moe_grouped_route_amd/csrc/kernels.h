@@ -10,7 +10,6 @@ namespace moeq {
 
 // Route prep.
 size_t route_workspace_bytes(int64_t P, int E);
-size_t route_lds_bytes(int E);
 hipError_t launch_route(const int* ids, int P, int E, int* offsets, int* sorted_ids,
                         int* pair_to_sorted, int* n_invalid, void* ws, hipStream_t stream);
 

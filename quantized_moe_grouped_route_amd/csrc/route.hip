@@ -11,7 +11,8 @@
 // round per distinct expert, for E <= 16; otherwise a 64-step comparison
 // with every lane's expert) plus the counts of earlier waves.  One chunk
 // needs one workgroup:
-//   * P <= kChunk: a single fused kernel counts, scans and scatters.
+//   * P <= kChunk: a single fused kernel counts, scans and scatters (with
+//                  4 waves when P <= 256).
 //   * otherwise:   route_count writes per-chunk counts to the workspace and
 //                  route_scatter (one workgroup per chunk) derives every
 //                  prefix it needs from them.
@@ -63,11 +64,13 @@ __device__ __forceinline__ int wave_rank_scan(int e, bool valid, unsigned char* 
   return rank;
 }
 
-// Exclusive scan over E values held in LDS `v` (E <= kChunk*4), result in
-// `out`; returns the total.  All threads must call.
+// Exclusive scan over E values held in LDS `v`, result in `out`; returns the
+// total.  All NT threads of the workgroup must call.
+template <int NT>
 __device__ int block_exclusive_scan(const int* v, int* out, int E, int* scratch) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int per = (E + kChunk - 1) / kChunk;
+  const int per = (E + NT - 1) / NT;
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
   int local = 0;
   for (int e = e0; e < e1; ++e) local += v[e];
@@ -81,20 +84,20 @@ __device__ int block_exclusive_scan(const int* v, int* out, int E, int* scratch)
   __syncthreads();
   if (tid == 0) {
     int s = 0;
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const int t = scratch[w];
-      scratch[kWaves + w] = s;
+      scratch[NW + w] = s;
       s += t;
     }
-    scratch[2 * kWaves] = s;
+    scratch[2 * NW] = s;
   }
   __syncthreads();
-  int run = incl - local + scratch[kWaves + wid];
+  int run = incl - local + scratch[NW + wid];
   for (int e = e0; e < e1; ++e) {
     out[e] = run;
     run += v[e];
   }
-  const int total = scratch[2 * kWaves];
+  const int total = scratch[2 * NW];
   __syncthreads();
   return total;
 }
@@ -117,10 +120,11 @@ __global__ __launch_bounds__(kChunk) void route_count(const int* __restrict__ id
   for (int e = threadIdx.x; e <= E; e += kChunk) dst[e] = cnt[e];
 }
 
-// FUSED: one workgroup, P <= kChunk, counts computed here.
-// Otherwise: workgroup b handles chunk b and reads all chunk counts from ws.
-template <bool FUSED>
-__global__ __launch_bounds__(kChunk) void route_scatter(const int* __restrict__ ids, int P, int E,
+// FUSED: one workgroup of NT threads, P <= NT, counts computed here.
+// Otherwise (NT == kChunk): workgroup b handles chunk b and reads all chunk
+// counts from ws.
+template <bool FUSED, int NT>
+__global__ __launch_bounds__(NT) void route_scatter(const int* __restrict__ ids, int P, int E,
                                                         const int* __restrict__ ws,
                                                         int* __restrict__ offsets,
                                                         int* __restrict__ sorted_ids,
@@ -130,14 +134,16 @@ __global__ __launch_bounds__(kChunk) void route_scatter(const int* __restrict__ 
   int* base = sm;                        // [E+1] first sorted position of e in this chunk
   int* tot = base + (E + 1);             // [E+1] pairs per expert (+ invalid count at E)
   int* offs = tot + (E + 1);             // [E]   exclusive scan of tot
-  int* scratch = offs + E;               // [2*kWaves+1]
-  unsigned char* wcnt = reinterpret_cast<unsigned char*>(scratch + 2 * kWaves + 1);  // [kWaves][E]
+  constexpr int NW = NT / 64;
+  static_assert(FUSED || NT == kChunk, "chunks of kChunk pairs");
+  int* scratch = offs + E;               // [2*NW+1]
+  unsigned char* wcnt = reinterpret_cast<unsigned char*>(scratch + 2 * NW + 1);  // [NW][E]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int b = blockIdx.x, nchunks = (P + kChunk - 1) / kChunk;
+  const int b = blockIdx.x, nchunks = (P + NT - 1) / NT;
 
-  __shared__ int winv[kWaves];  // per wave: ids outside [0, E) other than -1
-  for (int j = tid; j < kWaves * E; j += kChunk) wcnt[j] = 0;
-  const int i = b * kChunk + tid;
+  __shared__ int winv[NW];  // per wave: ids outside [0, E) other than -1
+  for (int j = tid; j < NW * E; j += NT) wcnt[j] = 0;
+  const int i = b * NT + tid;
   const int e = i < P ? ids[i] : -1;
   const bool valid = i < P && valid_id(e, E);
   __syncthreads();  // wcnt cleared
@@ -154,21 +160,21 @@ __global__ __launch_bounds__(kChunk) void route_scatter(const int* __restrict__ 
   if (FUSED) {
     // Expert counts as sums of the wave counts: no atomics on shared
     // counters (with one expert every pair would hit the same one).
-    for (int x = tid; x < E; x += kChunk) {
+    for (int x = tid; x < E; x += NT) {
       int sum = 0;
-      for (int w = 0; w < kWaves; ++w) sum += wcnt[w * E + x];
+      for (int w = 0; w < NW; ++w) sum += wcnt[w * E + x];
       tot[x] = sum;
       base[x] = 0;  // no earlier chunks
     }
     if (tid == 0) {
       int sum = 0;
-      for (int w = 0; w < kWaves; ++w) sum += winv[w];
+      for (int w = 0; w < NW; ++w) sum += winv[w];
       tot[E] = sum;
       base[E] = 0;
     }
   } else {
     // tot[x] = sum over all chunks, base[x] = sum over chunks before b.
-    for (int x = tid; x <= E; x += kChunk) {
+    for (int x = tid; x <= E; x += NT) {
       int all = 0, before = 0;
       for (int c = 0; c < nchunks; ++c) {
         const int v = ws[(size_t)c * (E + 1) + x];
@@ -180,8 +186,8 @@ __global__ __launch_bounds__(kChunk) void route_scatter(const int* __restrict__ 
     }
   }
   __syncthreads();
-  const int nvalid = block_exclusive_scan(tot, offs, E, scratch);
-  for (int x = tid; x < E; x += kChunk) {
+  const int nvalid = block_exclusive_scan<NT>(tot, offs, E, scratch);
+  for (int x = tid; x < E; x += NT) {
     base[x] += offs[x];
     if (b == 0) offsets[x] = offs[x];
   }
@@ -214,15 +220,23 @@ size_t route_workspace_bytes(int64_t P, int E) {
   return (size_t)(nchunks * (E + 1) * sizeof(int));
 }
 
-size_t route_lds_bytes(int E) {
-  return sizeof(int) * (size_t)(2 * (E + 1) + E + 2 * kWaves + 1) + (size_t)kWaves * E;
+// dynamic LDS of route_scatter with nw waves
+static size_t route_lds_bytes(int E, int nw) {
+  return sizeof(int) * (size_t)(2 * (E + 1) + E + 2 * nw + 1) + (size_t)nw * E;
 }
 
 hipError_t launch_route(const int* ids, int P, int E, int* offsets, int* sorted_ids,
                         int* pair_to_sorted, int* n_invalid, void* ws, hipStream_t stream) {
-  const size_t lds = route_lds_bytes(E);
+  // P <= 256 (decode batches): one 4-wave workgroup, so fewer waves meet
+  // at each barrier; P <= kChunk: one 16-wave workgroup
+  if (P <= 256) {
+    hipLaunchKernelGGL((route_scatter<true, 256>), dim3(1), dim3(256), route_lds_bytes(E, 4), stream, ids, P, E,
+                       (const int*)nullptr, offsets, sorted_ids, pair_to_sorted, n_invalid);
+    return hipGetLastError();
+  }
+  const size_t lds = route_lds_bytes(E, kWaves);
   if (P <= kChunk) {
-    hipLaunchKernelGGL(route_scatter<true>, dim3(1), dim3(kChunk), lds, stream, ids, P, E,
+    hipLaunchKernelGGL((route_scatter<true, kChunk>), dim3(1), dim3(kChunk), lds, stream, ids, P, E,
                        (const int*)nullptr, offsets, sorted_ids, pair_to_sorted, n_invalid);
     return hipGetLastError();
   }
@@ -231,7 +245,7 @@ hipError_t launch_route(const int* ids, int P, int E, int* offsets, int* sorted_
                      P, E, (int*)ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(route_scatter<false>, dim3(nchunks), dim3(kChunk), lds, stream, ids, P, E,
+  hipLaunchKernelGGL((route_scatter<false, kChunk>), dim3(nchunks), dim3(kChunk), lds, stream, ids, P, E,
                      (const int*)ws, offsets, sorted_ids, pair_to_sorted, n_invalid);
   return hipGetLastError();
 }
