@@ -49,6 +49,11 @@ ROUTE_CASES = [
                                                   r.integers(-3, 70, size=(333, 3))).astype(np.int32), 64),
     ("one_expert_E256", lambda r: np.full((300, 3), 17, np.int32), 256),
     ("one_expert_E256_multi_chunk", lambda r: np.full((700, 3), 200, np.int32), 256),
+    # the 4-wave workgroup (P <= 256) and its boundary
+    ("minus1_and_invalid_P240_E40", lambda r: np.where(r.random((80, 3)) < 0.2, -1,
+                                                       r.integers(-3, 45, size=(80, 3))).astype(np.int32), 40),
+    ("boundary_P256", lambda r: synth.uniform_ids_with_repeats(r, 128, 2, 20), 20),
+    ("boundary_P257", lambda r: synth.uniform_ids_with_repeats(r, 257, 1, 20), 20),
 ]
 
 
