@@ -520,10 +520,12 @@ def test_nvfp4_u32_packed_scales_are_the_same_bytes():
 
 
 @pytest.mark.parametrize("sched", ["prefill", "decode"])
-def test_nvfp4_silu_mul_limit(sched):
+@pytest.mark.parametrize("I", [128, 256])
+def test_nvfp4_silu_mul_limit(sched, I):
     # megamoe_rm.cu's clamped SwiGLU: a limit of 0.15 clamps about a quarter
-    # of the gates and half of the up values of this input
-    T, E, k, H, I = 150, 5, 2, 256, 128
+    # of the gates and half of the up values of this input (I = 256: the
+    # 512-row prefill tile)
+    T, E, k, H = 150, 5, 2, 256
     lim = float(np.float32(0.15))
     d = synth.nvfp4_moe(41, T, E, k, H, I, routing="repeat")
     offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
@@ -551,10 +553,12 @@ def _pair_case(seed, T, E, k, H, I, drop=0.1):
 
 @pytest.mark.parametrize("sched", ["prefill", "decode"])
 @pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
-def test_nvfp4_fc2_pair_weighted_epilogue(sched, odt):
+@pytest.mark.parametrize("H", [256, 512])
+def test_nvfp4_fc2_pair_weighted_epilogue(sched, odt, H):
     # megamoe_rm.cu's fc2_rm epilogue: w[p] * y in pair row p; rows of pairs
-    # without an expert keep their previous contents
-    T, E, k, H, I = 120, 5, 3, 256, 256
+    # without an expert keep their previous contents.  H = 512 takes the
+    # 512-row prefill tile.
+    T, E, k, I = 120, 5, 3, 256
     d = _pair_case(63, T, E, k, H, I)
     offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
     P = T * k
@@ -567,7 +571,7 @@ def test_nvfp4_fc2_pair_weighted_epilogue(sched, odt):
     ypart, valid = oracle.pair_rows(y, host(srt), d["topk_weights"])
     got = host(out)
     assert valid.sum() < P and np.all(np.isnan(got[~valid]))
-    assert_rows_close(got[valid], ypart[valid], what=f"fc2 pair epilogue {sched}")
+    assert_rows_close(got[valid], ypart[valid], what=f"fc2 pair epilogue {sched} H={H}")
 
 
 @pytest.mark.parametrize("ydt,odt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.float32),
