@@ -157,8 +157,11 @@ moeq_status moe_route_prep(const int32_t* topk_ids, int64_t T, int32_t topk, int
  *                I32: the raw accumulator acc (act NONE only), bit-exact
  * Computed exactly in integers (int8 MFMA on nibbles scaled by 16), then
  * scaled in fp32 and rounded to nearest even.
- * Requires K % 128 == 0 and N % 128 == 0 (else MOEQ_EALIGN), all
- * pointers 16-byte aligned, 1 <= E <= 1024, 1 <= topk <= 64.
+ * Requires K % 128 == 0 and N % 32 == 0 (else MOEQ_EALIGN; [W4A4]'s
+ * launcher checks K and N against 32; SILU_MUL then writes I = N/2 columns,
+ * a multiple of 16), K < 131072 so that the int32 accumulator cannot wrap
+ * (else MOEQ_EINVAL), all pointers 16-byte aligned, 1 <= E <= 1024,
+ * 1 <= topk <= 64.
  * ---------------------------------------------------------------------- */
 moeq_status grouped_gemm_qint4(const uint8_t* a, const float* a_scale, int64_t rows_a,
                                moeq_arow a_row, const uint8_t* w, const float* w_scale,
@@ -228,10 +231,11 @@ moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int6
  *   out       [P][N] (NONE) or [P][N/2] (SILU_MUL*), BF16 | F16 | F32
  *   y[s][n] = w_gscale[e] * sum_k x[r][k] * e2m1(w[e][n][k])
  *                                  * ue4m3(w_sf[e][n][k/16])
- * Requires K % 128 == 0 and N % 128 == 0 (else MOEQ_EALIGN), 16-byte
- * aligned pointers, 1 <= E <= 1024, 1 <= topk <= 64.  sched AUTO takes the
- * weight-streaming schedule when P < 16 * E or N % 256 != 0; PREFILL with
- * N % 256 != 0 falls back to it as well.
+ * Requires K % 128 == 0 and N % 32 == 0 (else MOEQ_EALIGN; SILU_MUL then
+ * writes I = N/2 columns, a multiple of 16), 16-byte aligned pointers,
+ * 1 <= E <= 1024, 1 <= topk <= 64.  sched AUTO takes the weight-streaming
+ * schedule when P < 16 * E or N % 256 != 0; PREFILL with N % 256 != 0
+ * falls back to it as well.
  * ---------------------------------------------------------------------- */
 moeq_status grouped_gemm_qnvfp4(const void* x, moeq_dtype x_dtype, int64_t rows_a, moeq_arow a_row,
                                 const uint8_t* w, moeq_w_layout w_layout, const uint8_t* w_sf,

@@ -92,7 +92,9 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
-def _need(t, name, dtype=None, ndim=None, device=True):
+def _need(t, name, dtype=None, ndim=None):
+    """Type, dtype, rank and contiguity of one tensor argument (where it
+    lives is checked by _gpu, after every shape check)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
@@ -101,8 +103,13 @@ def _need(t, name, dtype=None, ndim=None, device=True):
         raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if device and not t.is_cuda:
-        raise ValueError(f"{name} must be on the GPU")
+
+
+def _gpu(**tensors):
+    """Every tensor argument (None: absent) must be in GPU memory."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
 
 
 def route_workspace_bytes(T: int, topk: int, E: int) -> int:
@@ -135,6 +142,8 @@ def moe_route_prep(topk_ids, E: int, *, out=None, workspace=None):
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _gpu(topk_ids=topk_ids, expert_offsets=offs, sorted_pair_ids=srt, pair_to_sorted=p2s, n_invalid=ninv,
+         workspace=workspace)
     st = lib().moe_route_prep(_ptr(topk_ids), T, k, E, _ptr(offs), _ptr(srt), _ptr(p2s),
                               _ptr(ninv), _ptr(workspace), wsb, _stream())
     _check("moe_route_prep", st)
@@ -177,6 +186,8 @@ def grouped_gemm_qint4(a, a_scale, w, w_scale, expert_offsets, sorted_pair_ids, 
     if En != E or a.shape[1] != Kh or tuple(w_scale.shape) != (E, N) or a_scale.numel() != a.shape[0]:
         raise ValueError("inconsistent INT4 operand shapes")
     out = _out(out, P, N // 2 if act == "silu_mul" else N, out_dtype, a.device)
+    _gpu(a=a, a_scale=a_scale, w=w, w_scale=w_scale, expert_offsets=expert_offsets,
+         sorted_pair_ids=sorted_pair_ids, out=out)
     st = lib().grouped_gemm_qint4(_ptr(a), _ptr(a_scale), a.shape[0], arow, _ptr(w), _ptr(w_scale),
                                   _ptr(expert_offsets), _ptr(sorted_pair_ids), P, topk, E, N, K,
                                   ACT[act], _DTYPE_CODE[out_dtype], _ptr(out), SCHED[sched],
@@ -201,6 +212,8 @@ def grouped_gemm_qfp8_block(a, a_scale, w, w_scale, expert_offsets, sorted_pair_
             or tuple(w_scale.shape) != (E, N // 128, K // 128)):
         raise ValueError("inconsistent FP8 operand shapes")
     out = _out(out, P, N, out_dtype, a.device)
+    _gpu(a=a, a_scale=a_scale, w=w, w_scale=w_scale, expert_offsets=expert_offsets,
+         sorted_pair_ids=sorted_pair_ids, out=out)
     st = lib().grouped_gemm_qfp8_block(_ptr(a), _ptr(a_scale), a.shape[0], arow, _ptr(w),
                                        _ptr(w_scale), _ptr(expert_offsets), _ptr(sorted_pair_ids),
                                        P, topk, E, N, K, _DTYPE_CODE[out_dtype], _ptr(out),
@@ -249,7 +262,12 @@ def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, t
         _need(pair_weights, "pair_weights", torch.float32)
         if sorted_pair_ids is None or pair_weights.numel() != sorted_pair_ids.numel():
             raise ValueError("pair_weights needs sorted_pair_ids and one weight per pair")
+        if P < sorted_pair_ids.numel():
+            # rows are written at pair ids, which run up to sorted_pair_ids.numel() - 1
+            raise ValueError("with pair_weights, P must be at least the number of pairs")
     out = _out(out, P, N // 2 if act == "silu_mul" else N, out_dtype, x.device)
+    _gpu(x=x, w=w, w_sf=w_sf, w_gscale=w_gscale, expert_offsets=expert_offsets,
+         sorted_pair_ids=sorted_pair_ids, pair_weights=pair_weights, out=out)
     st = lib().grouped_gemm_qnvfp4(_ptr(x), _DTYPE_CODE[x.dtype], x.shape[0], arow, _ptr(w),
                                    W_LAYOUT["tiled" if w_tiled else "rows"], _ptr(w_sf),
                                    SF_LAYOUT["quads" if quads else "rows"], _ptr(w_gscale),
@@ -276,6 +294,9 @@ def moe_scatter_combine(y, pair_to_sorted, topk_weights, *, out_dtype=None, out=
     if out is None:
         out = torch.empty(T, N, dtype=out_dtype, device=y.device)
     _need(out, "out", out_dtype, 2)
+    if tuple(out.shape) != (T, N):
+        raise ValueError(f"out must be [{T}][{N}], got {tuple(out.shape)}")
+    _gpu(y=y, pair_to_sorted=pair_to_sorted, topk_weights=topk_weights, out=out)
     st = lib().moe_scatter_combine(_ptr(y), _DTYPE_CODE[y.dtype], _ptr(pair_to_sorted),
                                    _ptr(topk_weights), T, k, N, _DTYPE_CODE[out_dtype], _ptr(out),
                                    _stream())
@@ -296,6 +317,9 @@ def moe_sum_pairs(y_pairs, pair_to_sorted, T: int, topk: int, *, out_dtype=None,
     if out is None:
         out = torch.empty(T, N, dtype=out_dtype, device=y_pairs.device)
     _need(out, "out", out_dtype, 2)
+    if tuple(out.shape) != (T, N):
+        raise ValueError(f"out must be [{T}][{N}], got {tuple(out.shape)}")
+    _gpu(y_pairs=y_pairs, pair_to_sorted=pair_to_sorted, out=out)
     st = lib().moe_sum_pairs(_ptr(y_pairs), _DTYPE_CODE[y_pairs.dtype], _ptr(pair_to_sorted), T, topk, N,
                              _DTYPE_CODE[out_dtype], _ptr(out), _stream())
     _check("moe_sum_pairs", st)
@@ -312,6 +336,7 @@ def cast_bf16_to_f16(x, *, out=None):
     _need(out, "out", torch.float16)
     if out.numel() != x.numel():
         raise ValueError("out must have as many elements as x")
+    _gpu(x=x, out=out)
     st = lib().moe_cast_bf16_to_f16(_ptr(x), x.numel(), _ptr(out), _stream())
     _check("moe_cast_bf16_to_f16", st)
     return out
@@ -331,6 +356,7 @@ def quantize_int4_rows(x, *, q=None, scale=None):
     _need(scale, "scale", (torch.float32,), 1)
     if tuple(q.shape) != (rows, K // 2) or tuple(scale.shape) != (rows,):
         raise ValueError("quantize_int4_rows: q must be [rows][K/2] and scale [rows]")
+    _gpu(x=x, q=q, scale=scale)
     st = lib().moe_quantize_int4(_ptr(x), _DTYPE_CODE[x.dtype], rows, K, _ptr(q), _ptr(scale), _stream())
     _check("moe_quantize_int4", st)
     return q, scale
@@ -360,6 +386,7 @@ def nvfp4_repack(w, sf_swizzled, *, swap_halves: bool, sf_layout="rows", w_layou
     _need(sf_out, "sf_out", torch.uint8)
     if tuple(w_out.shape) != w_shape or tuple(sf_out.shape) != sf_shape:
         raise ValueError(f"w_out must be {w_shape} and sf_out {sf_shape}")
+    _gpu(w=w, sf_swizzled=sf_swizzled, w_out=w_out, sf_out=sf_out)
     st = lib().moe_nvfp4_repack(_ptr(w), _ptr(sf_swizzled), E, N, K, int(bool(swap_halves)),
                                 W_LAYOUT[w_layout], SF_LAYOUT[sf_layout], _ptr(w_out), _ptr(sf_out),
                                 _stream())

@@ -7,8 +7,8 @@
 // split into two int8 words: (w << 4) & 0xF0F0F0F0 holds the even elements
 // and w & 0xF0F0F0F0 the odd ones, each byte being 16 * value as a signed
 // int8.  A and W get the same split, so the int8 MFMA sums the same
-// products, each scaled by 256; |acc| <= K * 64 * 256 < 2^31 for K <= 2^17,
-// and acc >> 8 is the exact int4 dot product.
+// products, each scaled by 256; |acc| <= K * 64 * 256 < 2^31 for K < 2^17
+// (the host rejects larger K), and acc >> 8 is the exact int4 dot product.
 //
 // Data movement.  A workgroup of 8 waves owns a tile of 256 routed rows x
 // 256 weight rows.  K advances in stages of 128 int4 values (64 packed

@@ -51,10 +51,14 @@ moeq_status hip_status(hipError_t e, const char* what) {
   return fail(MOEQ_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
 }
 
-// Checks shared by the three grouped GEMMs.
+// Checks shared by the three grouped GEMMs.  n_align is the multiple N
+// must be: 32 for INT4 and NVFP4 (CUTLASS discussion #2855's launcher
+// checks N % 32; the INT4 epilogue masks partial column tiles and the NVFP4
+// streaming schedule works in 16- and 32-row weight blocks), 128 for FP8,
+// whose weight scales cover 128 x 128 blocks.
 moeq_status check_grouped(const char* fn, const void* a, int64_t rows_a, int a_row, const void* w,
                           const int32_t* offsets, int64_t P, int32_t topk, int32_t E, int64_t N,
-                          int64_t K, const void* out) {
+                          int64_t K, const void* out, int64_t n_align) {
   if (E < 1 || E > kMaxE) return fail(MOEQ_EINVAL, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
   if (topk < 1 || topk > kMaxTopk) return fail(MOEQ_EINVAL, "%s: topk=%d outside [1, %d]", fn, topk, kMaxTopk);
   if (P < 0 || P >= (int64_t(1) << 31)) return fail(MOEQ_EINVAL, "%s: P=%lld out of range", fn, (long long)P);
@@ -63,7 +67,8 @@ moeq_status check_grouped(const char* fn, const void* a, int64_t rows_a, int a_r
   if (N <= 0 || K <= 0 || N > (1 << 20) || K > (1 << 17))
     return fail(MOEQ_EINVAL, "%s: N=%lld K=%lld out of range", fn, (long long)N, (long long)K);
   if (K % 128 != 0) return fail(MOEQ_EALIGN, "%s: K=%lld must be a multiple of 128", fn, (long long)K);
-  if (N % 128 != 0) return fail(MOEQ_EALIGN, "%s: N=%lld must be a multiple of 128", fn, (long long)N);
+  if (N % n_align != 0)
+    return fail(MOEQ_EALIGN, "%s: N=%lld must be a multiple of %lld", fn, (long long)N, (long long)n_align);
   if (a_row != MOEQ_AROW_TOKEN && a_row != MOEQ_AROW_SORTED) return fail(MOEQ_EINVAL, "%s: bad a_row %d", fn, a_row);
   if (!a || !w || !offsets || !out) return fail(MOEQ_EINVAL, "%s: null pointer", fn);
   if (!aligned(a, 16) || !aligned(w, 16) || !aligned(out, 16) || !aligned(offsets, 4))
@@ -140,8 +145,12 @@ moeq_status grouped_gemm_qint4(const uint8_t* a, const float* a_scale, int64_t r
                                moeq_act act, moeq_dtype out_dtype, void* out, moeq_sched sched,
                                void* stream) {
   const char* fn = "grouped_gemm_qint4";
-  moeq_status st = check_grouped(fn, a, rows_a, a_row, w, expert_offsets, P, topk, E, N, K, out);
+  moeq_status st = check_grouped(fn, a, rows_a, a_row, w, expert_offsets, P, topk, E, N, K, out, 32);
   if (st != MOEQ_OK) return st;
+  // The int8 MFMA sums products of nibbles scaled by 16, at most 2^14 each:
+  // K < 2^17 keeps every int32 partial sum below 2^31.
+  if (K >= (int64_t(1) << 17))
+    return fail(MOEQ_EINVAL, "%s: K=%lld must be below 131072 (int32 accumulator range)", fn, (long long)K);
   if (!a_scale || !w_scale) return fail(MOEQ_EINVAL, "%s: null scale pointer", fn);
   if (!aligned(a_scale, 4) || !aligned(w_scale, 4)) return fail(MOEQ_EALIGN, "%s: scales must be 4-byte aligned", fn);
   if (act != MOEQ_ACT_NONE && act != MOEQ_ACT_SILU_MUL) return fail(MOEQ_EUNSUPPORTED, "%s: act %d", fn, act);
@@ -164,7 +173,7 @@ moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int6
                                     int32_t E, int64_t N, int64_t K, moeq_dtype out_dtype,
                                     void* out, moeq_sched sched, void* stream) {
   const char* fn = "grouped_gemm_qfp8_block";
-  moeq_status st = check_grouped(fn, a, rows_a, a_row, w, expert_offsets, P, topk, E, N, K, out);
+  moeq_status st = check_grouped(fn, a, rows_a, a_row, w, expert_offsets, P, topk, E, N, K, out, 128);
   if (st != MOEQ_OK) return st;
   if (!a_scale || !w_scale) return fail(MOEQ_EINVAL, "%s: null scale pointer", fn);
   if (!aligned(a_scale, 4) || !aligned(w_scale, 4)) return fail(MOEQ_EALIGN, "%s: scales must be 4-byte aligned", fn);
@@ -186,7 +195,7 @@ moeq_status grouped_gemm_qnvfp4(const void* x, moeq_dtype x_dtype, int64_t rows_
                                 moeq_act act, float act_limit, const float* pair_weights,
                                 moeq_dtype out_dtype, void* out, moeq_sched sched, void* stream) {
   const char* fn = "grouped_gemm_qnvfp4";
-  moeq_status st = check_grouped(fn, x, rows_a, a_row, w, expert_offsets, P, topk, E, N, K, out);
+  moeq_status st = check_grouped(fn, x, rows_a, a_row, w, expert_offsets, P, topk, E, N, K, out, 32);
   if (st != MOEQ_OK) return st;
   if (!w_sf || !w_gscale) return fail(MOEQ_EINVAL, "%s: null scale pointer", fn);
   if (!aligned(w_sf, 16) || !aligned(w_gscale, 4)) return fail(MOEQ_EALIGN, "%s: scales misaligned", fn);

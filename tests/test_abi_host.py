@@ -79,13 +79,16 @@ def _int4(L, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(K=192), mq.EALIGN), (dict(N=96), mq.EALIGN), (dict(E=0), mq.EINVAL),
+    (dict(K=192), mq.EALIGN), (dict(N=80), mq.EALIGN), (dict(N=48, act=1), mq.EALIGN), (dict(E=0), mq.EINVAL),
     (dict(E=2000), mq.EINVAL), (dict(topk=0), mq.EINVAL), (dict(P=-1), mq.EINVAL),
     (dict(a=None), mq.EINVAL), (dict(w=ODD), mq.EALIGN), (dict(out=ODD), mq.EALIGN),
     (dict(sa=None), mq.EINVAL), (dict(act=7), mq.EUNSUPPORTED), (dict(od=9), mq.EUNSUPPORTED),
     (dict(od=mq.I32, act=1), mq.EUNSUPPORTED), (dict(arow=5), mq.EINVAL), (dict(act=2), mq.EUNSUPPORTED),
     (dict(srt=None, rows=8, P=16), mq.EINVAL), (dict(sched=9), mq.EINVAL),
     (dict(rows=0), mq.EINVAL), (dict(K=1 << 18), mq.EINVAL),
+    # K = 2^17 with every code -8 would sum 2^17 products of 2^14 to 2^31 in
+    # the int32 accumulator; the largest accepted K is 2^17 - 128
+    (dict(K=1 << 17), mq.EINVAL),
 ])
 def test_int4_rejects(L, kw, status):
     assert _int4(L, **kw) == status
@@ -119,7 +122,7 @@ def _nvfp4(L, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(K=96), mq.EALIGN), (dict(N=32), mq.EALIGN), (dict(sf=ODD), mq.EALIGN),
+    (dict(K=96), mq.EALIGN), (dict(N=48), mq.EALIGN), (dict(N=16, act=1), mq.EALIGN), (dict(sf=ODD), mq.EALIGN),
     (dict(gs=None), mq.EINVAL), (dict(od=mq.I32), mq.EUNSUPPORTED), (dict(act=3), mq.EUNSUPPORTED),
     (dict(x=None), mq.EINVAL), (dict(act=2, lim=0.0, K=96), mq.EALIGN),
     (dict(act=2, lim=0.0), mq.EINVAL), (dict(act=2, lim=-1.0), mq.EINVAL),
@@ -170,8 +173,60 @@ def test_error_text_names_the_call(L):
 
 def test_binding_raises_without_gpu_tensors():
     import torch
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError, match="on the GPU"):
         mq.moe_route_prep(torch.zeros(4, 2, dtype=torch.int32), 4)
+
+
+def test_n_alignment_of_each_gemm(L):
+    # INT4 and NVFP4 take N % 32 == 0 (the W4A4 launcher's check); FP8 keeps
+    # N % 128 == 0 for its 128 x 128 weight-scale blocks.  Accepted shapes are
+    # not called here (that would launch); the next multiple of 16 is refused.
+    assert _int4(L, N=112) == mq.EALIGN and b"multiple of 32" in L.moeq_last_error()
+    assert _nvfp4(L, N=112) == mq.EALIGN and b"multiple of 32" in L.moeq_last_error()
+    assert _fp8(L, N=160) == mq.EALIGN and b"multiple of 128" in L.moeq_last_error()
+
+
+def test_binding_checks_combine_out_shape():
+    # a too-small caller-supplied out would let the kernel write [T][N] past
+    # its end; the binding refuses it before anything is launched
+    import torch
+    y = torch.zeros(8, 64, dtype=torch.float16)
+    p2s = torch.zeros(8, dtype=torch.int32)
+    tw = torch.zeros(4, 2, dtype=torch.float32)
+    with pytest.raises(ValueError, match=r"out must be \[4\]\[64\]"):
+        mq.moe_scatter_combine(y, p2s, tw, out=torch.zeros(3, 64, dtype=torch.float16))
+    with pytest.raises(ValueError, match=r"out must be \[4\]\[64\]"):
+        mq.moe_scatter_combine(y, p2s, tw, out=torch.zeros(4, 32, dtype=torch.float16))
+    with pytest.raises(ValueError, match="on the GPU"):       # right shape: reaches the device check
+        mq.moe_scatter_combine(y, p2s, tw, out=torch.zeros(4, 64, dtype=torch.float16))
+
+
+def test_binding_checks_sum_pairs_out_shape():
+    import torch
+    y = torch.zeros(8, 64, dtype=torch.bfloat16)
+    p2s = torch.zeros(8, dtype=torch.int32)
+    with pytest.raises(ValueError, match=r"out must be \[4\]\[64\]"):
+        mq.moe_sum_pairs(y, p2s, 4, 2, out=torch.zeros(2, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="on the GPU"):
+        mq.moe_sum_pairs(y, p2s, 4, 2, out=torch.zeros(4, 64, dtype=torch.bfloat16))
+
+
+def test_binding_checks_pair_weights_rows():
+    # with pair_weights, FC2 writes rows at pair ids up to the pair count - 1:
+    # an explicit P below that count is refused
+    import torch
+    E, N, K, pairs = 2, 32, 128, 8
+    x = torch.zeros(pairs, K, dtype=torch.float16)
+    w = torch.zeros(E, N, K // 2, dtype=torch.uint8)
+    sf = torch.zeros(E, N, K // 16, dtype=torch.uint8)
+    g = torch.ones(E, dtype=torch.float32)
+    offs = torch.zeros(E + 1, dtype=torch.int32)
+    srt = torch.zeros(pairs, dtype=torch.int32)
+    pw = torch.ones(pairs, dtype=torch.float32)
+    with pytest.raises(ValueError, match="P must be at least"):
+        mq.grouped_gemm_qnvfp4(x, w, sf, g, offs, srt, 2, a_row="sorted", pair_weights=pw, P=pairs - 1)
+    with pytest.raises(ValueError, match="on the GPU"):
+        mq.grouped_gemm_qnvfp4(x, w, sf, g, offs, srt, 2, a_row="sorted", pair_weights=pw, P=pairs)
 
 
 def _repack(L, **kw):
