@@ -1,18 +1,21 @@
 """Throughput of the quantized MoE grouped-GEMM path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload {0,1,...,8}]
+    python bench.py --peaks      (the chip's sustained HBM read rate and
+                                  MFMA rate per dtype, measured on the box)
 
 One step is one pass of the whole hot path over one batch of seeded
 synthetic input already resident in HBM:
   0  W4A4 INT4, 64 tokens, E=4, top-2, K=N=256: route + INT4 GEMM + combine
   1  FP8 e4m3 1x128 / 128x128 block-scaled dense GEMM M=1024 N=4096
-     K=7168 (default): route (E=1) + FP8 GEMM
+     K=7168: route (E=1) + FP8 GEMM
   2  NVFP4 W4A16 decode, 8 tokens, E=256, top-8, H=7168 I=2048:
      route + FC1 (SiLU-gated) + FC2 + combine; with --act f16 (default) the
      bf16 input is first cast to binary16 and h is binary16
   3  NVFP4 W4A16 prefill, 4096 tokens, Zipf(1.1) routing: as 2
-  4  W4A4 INT4 Mixtral-like, 8192 tokens, E=8, top-2, H=4096 I=14336:
-     route + FC1 (SiLU-gated) + FC2 (int4 rows in sorted order) + combine
+  4  W4A4 INT4 Mixtral-like, 8192 tokens, E=8, top-2, H=4096 I=14336
+     (default, the largest configuration): route + FC1 (SiLU-gated) + FC2
+     (int4 rows in sorted order) + combine
   5  per-row INT4 quantization of 16384 fp16 rows of 14336 (the FC2 input
      of 4 in a full W4A4 chain)
   6  FP8 block-scaled MoE projection, decode: 8 tokens, E=256, top-8,
@@ -21,10 +24,12 @@ synthetic input already resident in HBM:
      x + FC1 (SiLU) + per-row int4 of h + FC2 + combine
   7  one-shot NVFP4 weight repack of 2's gate+up weights (E=256, 4096 rows,
      K=7168) from the up-first, 128x4-swizzled-scale layout of megamoe_rm.cu
-Prints ONE JSON line: whole-path throughput, the dominant kernel's roofline
-fraction (its launches timed with HIP events on the launch stream inside the
-timed region) and the CPU oracle's throughput on the host as a reported
-baseline.
+Prints ONE JSON line: whole-path throughput (and the p10 / p50 / p90 of the
+per-step times), the dominant kernel's roofline fraction (its launches timed
+with HIP events on the launch stream inside the timed region) against the
+published peak and against the peak measured on the box (--peaks, summarized
+in profiles/peaks_mi355x.txt), and the CPU oracle's throughput on the host
+as a reported baseline.
 """
 from __future__ import annotations
 
@@ -78,6 +83,68 @@ def _traffic(kernel_tag, sources):
         return float(kv["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+# ---------------------------------------------------------------- peaks
+# MFMA kinds of the peak probe: (name, K per 32x32 instruction, published
+# dense peak in T(FL)OP/s).
+MFMA_KINDS = {0: ("int8", 32, 5000.0), 1: ("fp8", 64, 5000.0), 2: ("bf16", 16, 2500.0),
+              3: ("fp16", 16, 2500.0), 4: ("fp6", 64, 10100.0), 5: ("fp4", 64, 10100.0)}
+PEAKS_FILE = os.path.join(ROOT, "profiles", "peaks_mi355x.txt")
+
+
+def measure_peaks(reps: int = 10):
+    """The chip's sustained rates: HBM read (4 GiB streamed with 16-byte
+    nontemporal loads) and each MFMA kind on register operands (2 workgroups
+    of 4 waves per CU).  Median of `reps` launches timed with HIP events."""
+    import ctypes as C
+    import torch
+    from quantized_moe_grouped_route_amd import build as b
+    L = C.CDLL(b.PEAKS_LIB)
+    L.moeq_peak_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p]
+    L.moeq_peak_mfma.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    st = torch.cuda.current_stream().cuda_stream
+
+    def timed(launch):
+        ms = []
+        for i in range(reps + 2):
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            assert launch() == 0
+            z.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ms.append(a.elapsed_time(z))
+        return float(np.median(ms))
+
+    res = {}
+    nbytes = 1 << 32
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    grid = cus * 8
+    sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+    ms = timed(lambda: L.moeq_peak_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, st))
+    res["hbm_read"] = dict(value=nbytes / (ms * 1e-3) / 1e9, unit="GB/s", spec=PEAK["hbm_GBps"], ms=ms)
+    del buf
+    grid = cus * 2
+    sinkf = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    for kind, (name, K, spec) in MFMA_KINDS.items():
+        iters = 20000 if K == 16 else 10000
+        ms = timed(lambda: L.moeq_peak_mfma(kind, grid, iters, sinkf.data_ptr(), st))
+        ops = grid * 4 * iters * 4 * 2.0 * 32 * 32 * K
+        res[name] = dict(value=ops / (ms * 1e-3) / 1e12, unit="TFLOP/s" if name != "int8" else "TOP/s",
+                         spec=spec, ms=ms)
+    return res
+
+
+def measured_peak(key):
+    """The committed on-box measurement of one peak, or None."""
+    if not os.path.exists(PEAKS_FILE):
+        return None
+    for line in open(PEAKS_FILE):
+        if line.startswith(key + ":"):
+            return float(line.split(":", 1)[1].split()[0])
+    return None
 
 
 # ---------------------------------------------------------------- workloads
@@ -623,7 +690,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=1, choices=sorted(__import__("synth").WORKLOADS))
+    ap.add_argument("--workload", type=int, default=4, choices=sorted(__import__("synth").WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--act", choices=("bf16", "f16"), default="f16",
                     help="NVFP4 workloads: GEMMs on the bf16 activations, or on binary16 activations "
@@ -638,6 +705,9 @@ def main():
                     help="NVFP4 workloads: FC2 writes sorted rows and the combine applies the top-k "
                          "weights (sorted), or FC2's epilogue applies them and writes pair-ordered "
                          "rows that a pair sum adds (pair)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure the sustained HBM read rate and each MFMA kind's rate on this "
+                         "GPU, print them as the lines of profiles/peaks_mi355x.txt, and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device 5 times (a kernel of known traffic "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -661,6 +731,15 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.peaks:
+        res = measure_peaks()
+        print(f"# Sustained peaks of one {torch.cuda.get_device_name(0)} "
+              f"({torch.cuda.get_device_properties(0).multi_processor_count} CUs), median of 10 launches")
+        print("# command (from the repository root): python3 bench.py --peaks")
+        for k, v in res.items():
+            print(f"{k}: {v['value']:.1f} {v['unit']} (published {v['spec']:.0f}, "
+                  f"{v['value'] / v['spec']:.3f} of it; {v['ms']:.3f} ms per launch)")
+        return
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -692,18 +771,19 @@ def main():
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    # step boundaries: step i runs from marks[i] to marks[i + 1]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     torch.cuda._sleep(int(min(spin_ms, 2000.0) * cycles_per_ms))
     wall = time.perf_counter()
-    t0.record()
+    marks[0].record()
     for i in range(args.steps):
         wl.step(evs[i])
-    t1.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall
-    ms = t0.elapsed_time(t1) / args.steps
+    ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     cfg = wl.cfg
@@ -720,6 +800,12 @@ def main():
     roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": runit,
             "frac": round(achieved / peak, 4), "traffic": _traffic(f"{tag}_{cfg['name']}", srcs),
             "kernel": tag, "kernel_ms": round(dom_ms, 5)}
+    mkey = {"hbm": "hbm_read"}.get(bound) or {"int4_via_int8_mfma": "int8", "fp8_e4m3": "fp8",
+                                              "f16_x_nvfp4": "fp16", "bf16_x_nvfp4": "bf16"}.get(wl.dtype)
+    mpeak = measured_peak(mkey) if mkey else None
+    if mpeak:
+        roof["peak_measured"] = round(mpeak, 1)
+        roof["frac_of_measured"] = round(achieved / mpeak, 4)
     config = {"workload": cfg["name"]}
     config.update({k: v for k, v in cfg.items() if k not in ("name", "kind")})
     if cfg["kind"] == "nvfp4":
@@ -732,6 +818,7 @@ def main():
         config["weight_bytes"] = wl.weight_bytes
     rec = {"metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "ms_per_step_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
            "data": "synthetic (seeded generators, shapes of the workload)", "config": config,
            "roofline": roof}

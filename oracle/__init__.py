@@ -33,9 +33,9 @@ from .formats import (unpack_nibbles, int4_value, e2m1_value, e4m3fn_value, ue4m
                       bf16_to_f16_bits)
 from .route import route_prep
 from .gemm import (grouped_gemm_qint4, grouped_gemm_qfp8_block, grouped_gemm_qnvfp4, silu_mul,
-                   gemm_rows)
+                   gemm_rows, weight_rows)
 from .combine import scatter_combine, pair_rows, sum_pairs
-from .layer import int4_layer, nvfp4_layer, fp8_dense
+from .layer import int4_layer, int4_ffn_layer, nvfp4_layer, fp8_dense, token_rows, combine_tokens
 from .quant import quantize_int4_rows
 from .layouts import (scale_swizzle_offset, unswizzle_scales, swizzle_scales, repack_nvfp4,
                       quads_from_rows, rows_from_quads, tiles_from_rows, rows_from_tiles)

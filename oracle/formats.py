@@ -22,23 +22,63 @@ def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+# Each decoder below is a pure function of its code.  The closed form is
+# evaluated once over the format's whole code alphabet and each code then
+# looks its value up: the same values as evaluating it per element, without
+# a large array's worth of temporaries (a code outside the alphabet raises
+# IndexError).
+
+
+def _int4_closed_form(c: np.ndarray) -> np.ndarray:
+    c = c.astype(np.int64)
+    return c - 16 * (c >= 8)
+
+
+def _e2m1_closed_form(c: np.ndarray) -> np.ndarray:
+    c = c.astype(np.int64)
+    s = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, (e - 1).astype(np.int32)))
+    return np.where(s == 1, -mag, mag)
+
+
+def _e4m3fn_closed_form(b: np.ndarray) -> np.ndarray:
+    b = b.astype(np.int64)
+    s = (b >> 7) & 1
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6),
+                   np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int32)))
+    mag = np.where((e == 15) & (b & 7 == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+_INT4 = _int4_closed_form(np.arange(16))
+_E2M1 = _e2m1_closed_form(np.arange(16))
+_E4M3FN = _e4m3fn_closed_form(np.arange(256))
+
+
+def _codes(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes)
+    if c.dtype.kind not in "iu":
+        raise TypeError("codes must be integers")
+    if c.size and c.min() < 0:
+        raise IndexError("negative code")
+    return c
+
+
 def int4_value(codes: np.ndarray) -> np.ndarray:
     """Two's-complement 4-bit integer: code c in [0,15] -> c - 16*[c >= 8],
-    range [-8, 7] (W4A4 INT4 of CUTLASS discussion #2855)."""
-    c = np.asarray(codes).astype(np.int64)
-    return c - 16 * (c >= 8)
+    range [-8, 7] (W4A4 INT4 of CUTLASS discussion #2855).  int64."""
+    return _INT4[_codes(codes)]
 
 
 def e2m1_value(codes: np.ndarray) -> np.ndarray:
     """FP4 E2M1: sign bit 3, exponent bits 2:1 (bias 1), mantissa bit 0.
     exponent 0 is subnormal: m/2; otherwise 2^(e-1) * (1 + m/2).
     (The NVFP4 element format of tilelang_kernels.py and megamoe_rm.cu.)"""
-    c = np.asarray(codes).astype(np.int64)
-    s = (c >> 3) & 1
-    e = (c >> 1) & 3
-    m = (c & 1).astype(np.float64)
-    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, (e - 1).astype(np.int32)))
-    return np.where(s == 1, -mag, mag)
+    return _E2M1[_codes(codes)]
 
 
 def e4m3fn_value(codes: np.ndarray) -> np.ndarray:
@@ -47,14 +87,7 @@ def e4m3fn_value(codes: np.ndarray) -> np.ndarray:
     (no infinities); otherwise 2^(e-7) * (1 + m/8).  Largest finite 448.
     (cutlass::float_e4m3_t of CUTLASS issue #2087; float8_e4m3fn of
     tilelang_kernels.py.)"""
-    b = np.asarray(codes).astype(np.int64)
-    s = (b >> 7) & 1
-    e = (b >> 3) & 15
-    m = (b & 7).astype(np.float64)
-    mag = np.where(e == 0, np.ldexp(m / 8.0, -6),
-                   np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int32)))
-    mag = np.where((e == 15) & (b & 7 == 7), np.nan, mag)
-    return np.where(s == 1, -mag, mag)
+    return _E4M3FN[_codes(codes)]
 
 
 def ue4m3_value(codes: np.ndarray) -> np.ndarray:

@@ -16,6 +16,10 @@ product of integer values (every partial sum is an integer below 2^53, so
 exact), the floating contractions are float64 products of exactly decoded
 values.  `rows` restricts the computation to a subset of sorted positions
 (for sampled checks of large problems); the result then has len(rows) rows.
+`cols` likewise restricts it to a subset of output columns: the weight rows
+those columns need are selected before the contraction (with act 'silu_mul',
+output column j takes weight rows j and I + j), and the result has
+len(cols) columns.  Neither changes any arithmetic.
 """
 from __future__ import annotations
 
@@ -44,6 +48,20 @@ def gemm_rows(offsets, sorted_pair_ids, topk: int, a_row: str, rows=None):
     return s, e, r
 
 
+def weight_rows(N: int, act: str, cols):
+    """Weight rows (output channels of the GEMM) that the output columns
+    `cols` depend on, in the order the contraction returns them: all N when
+    cols is None; cols itself for act 'none'; for 'silu_mul' the gate rows
+    cols followed by the up rows I + cols, so that silu_mul's halves line up."""
+    if cols is None:
+        return np.arange(N)
+    c = np.asarray(cols, np.int64)
+    lim = N // 2 if act == "silu_mul" else N
+    if c.size and (c.min() < 0 or c.max() >= lim):
+        raise ValueError("column outside the output")
+    return np.concatenate([c, N // 2 + c]) if act == "silu_mul" else c
+
+
 def silu_mul(y: np.ndarray, limit=None) -> np.ndarray:
     """SiLU-gated product over the two halves of y [n][2I]: columns [0, I) are
     the gate g, columns [I, 2I) the up projection u; h = g / (1 + exp(-g)) * u.
@@ -63,7 +81,7 @@ def silu_mul(y: np.ndarray, limit=None) -> np.ndarray:
 
 
 def grouped_gemm_qint4(a, a_scale, a_row, w, w_scale, offsets, sorted_pair_ids, topk,
-                       act="none", rows=None):
+                       act="none", rows=None, cols=None):
     """W4A4 INT4 grouped GEMM with the per-token x per-channel epilogue.
 
     CUTLASS discussion #2855 (problem statement): activations quantized per
@@ -73,18 +91,19 @@ def grouped_gemm_qint4(a, a_scale, a_row, w, w_scale, offsets, sorted_pair_ids, 
       y[s, n]   = a_scale[r] * w_scale[e, n] * acc[s, n]
     a [rows_a][K/2] bytes, a_scale [rows_a] f32, w [E][N][K/2] bytes,
     w_scale [E][N] f32.  act 'silu_mul' returns silu_mul(y).
-    Returns dict(acc=int64 [n][N], y=float64 [n][N or N/2])."""
+    Returns dict(acc=int64 [n][N], y=float64 [n][N or N/2]) (with cols:
+    acc over the selected weight rows, see weight_rows)."""
     s, e, r = gemm_rows(offsets, sorted_pair_ids, topk, a_row, rows)
-    N = w.shape[1]
+    wr = weight_rows(w.shape[1], act, cols)
     A = int4_value(unpack_nibbles(np.asarray(a)[r])).astype(np.float64)
-    acc = np.zeros((s.size, N), np.float64)
+    acc = np.zeros((s.size, wr.size), np.float64)
     for ex in np.unique(e):
         m = e == ex
-        W = int4_value(unpack_nibbles(np.asarray(w)[ex])).astype(np.float64)
+        W = int4_value(unpack_nibbles(np.asarray(w)[ex][wr])).astype(np.float64)
         acc[m] = A[m] @ W.T
     assert np.all(np.abs(acc) < 2.0 ** 31), "int32 accumulator would overflow"
     sa = np.asarray(a_scale, np.float64)[r]
-    sw = np.asarray(w_scale, np.float64)[e]
+    sw = np.asarray(w_scale, np.float64)[e][:, wr]
     y = sa[:, None] * sw * acc
     if act == "silu_mul":
         y = silu_mul(y)
@@ -92,7 +111,7 @@ def grouped_gemm_qint4(a, a_scale, a_row, w, w_scale, offsets, sorted_pair_ids, 
 
 
 def grouped_gemm_qfp8_block(a, a_scale, a_row, w, w_scale, offsets, sorted_pair_ids, topk,
-                            rows=None):
+                            rows=None, cols=None):
     """FP8 e4m3 block-scaled grouped GEMM (CUTLASS issue #2087).
 
     A is quantized per token per 128 columns of K: a_scale [K/128][rows_a]
@@ -104,21 +123,21 @@ def grouped_gemm_qfp8_block(a, a_scale, a_row, w, w_scale, offsets, sorted_pair_
                     * (w_scale[e, n//128, k//128] * e4m3(W[e, n, k]))
     Returns dict(y=float64 [n][N])."""
     s, e, r = gemm_rows(offsets, sorted_pair_ids, topk, a_row, rows)
-    N, K = w.shape[1], w.shape[2]
+    wr = weight_rows(w.shape[1], "none", cols)
     sa = np.asarray(a_scale, np.float64)[:, r].T              # [n][K/128]
     Ad = e4m3fn_value(np.asarray(a)[r]) * np.repeat(sa, 128, axis=1)
-    y = np.zeros((s.size, N), np.float64)
+    y = np.zeros((s.size, wr.size), np.float64)
     for ex in np.unique(e):
         m = e == ex
-        sb = np.asarray(w_scale, np.float64)[ex]              # [N/128][K/128]
-        Wd = e4m3fn_value(np.asarray(w)[ex]) * np.repeat(np.repeat(sb, 128, axis=0), 128, axis=1)
+        sb = np.asarray(w_scale, np.float64)[ex][wr // 128]   # [n_cols][K/128]: block row of each column
+        Wd = e4m3fn_value(np.asarray(w)[ex][wr]) * np.repeat(sb, 128, axis=1)
         y[m] = Ad[m] @ Wd.T
     return dict(y=y)
 
 
 def grouped_gemm_qnvfp4(x, a_row, w, w_sf, w_gscale, offsets, sorted_pair_ids, topk,
                         act="none", rows=None, limit=None, x_dtype="bf16", sf_layout="rows",
-                        w_layout="rows"):
+                        w_layout="rows", cols=None):
     """NVFP4 W4A16 grouped GEMM (tilelang_kernels.py grouped_gemm_fp4, with the
     per-expert global scale of megamoe_rm.cu).
 
@@ -145,13 +164,14 @@ def grouped_gemm_qnvfp4(x, a_row, w, w_sf, w_gscale, offsets, sorted_pair_ids, t
         w = rows_from_tiles(np.asarray(w))
     elif w_layout != "rows":
         raise ValueError(w_layout)
-    N = w.shape[1]
+    wr = weight_rows(w.shape[1], act, cols)
     X = (bf16_value if x_dtype == "bf16" else f16_value)(np.asarray(x)[r])
-    y = np.zeros((s.size, N), np.float64)
+    y = np.zeros((s.size, wr.size), np.float64)
     for ex in np.unique(e):
         m = e == ex
-        Wd = e2m1_value(unpack_nibbles(np.asarray(w)[ex])) * np.repeat(
-            ue4m3_value(np.asarray(w_sf)[ex]), 16, axis=1)
+        codes = e2m1_value(unpack_nibbles(np.asarray(w)[ex][wr]))         # [n_w][K]
+        sc = ue4m3_value(np.asarray(w_sf)[ex][wr])                          # [n_w][K/16]
+        Wd = (codes.reshape(sc.shape + (16,)) * sc[:, :, None]).reshape(codes.shape)
         y[m] = float(np.asarray(w_gscale)[ex]) * (X[m] @ Wd.T)
     if act == "silu_mul":
         y = silu_mul(y, limit)

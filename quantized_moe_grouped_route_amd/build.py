@@ -3,8 +3,10 @@
     python -m quantized_moe_grouped_route_amd.build
 
 Compiles every source under csrc/ with hipcc for gfx950 and links the
-shared library next to this file.  Packed-FP32 VALU instructions are
-disabled for all device code.
+shared library next to this file; also builds libmoeq_peaks.so from
+probes/ (the on-box peak measurements bench.py --peaks runs; the library
+itself never uses it).  Packed-FP32 VALU instructions are disabled for all
+device code.
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoeq.so")
+PROBES = os.path.join(HERE, "probes")
+PEAKS_LIB = os.path.join(HERE, "libmoeq_peaks.so")
 ARCH = "gfx950"
 
 COMMON = [
@@ -64,7 +68,17 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")
+    _build_peaks()
     return LIB
+
+
+def _build_peaks():
+    tmp = PEAKS_LIB + ".tmp"
+    cmd = [hipcc(), *COMMON, "-shared", "-o", tmp, os.path.join(PROBES, "peaks.hip")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PEAKS_LIB)
 
 
 if __name__ == "__main__":

@@ -655,3 +655,97 @@ def test_nvfp4_f16_layer_with_gpu_cast(sched):
     ref_y = oracle.grouped_gemm_qnvfp4(hb, "sorted", d["w2"], d["s2"], d["g2"], host(offs), host(srt), k,
                                        x_dtype="f16")["y"]
     assert_rows_close(host(y)[:n], ref_y, what=f"f16 FC2 {sched}")
+
+
+# ------------------------------------------------------------------ N % 32 shapes
+def _guarded(P, ncols, dtype, fill):
+    """out [P][ncols] as the head of a longer buffer whose tail holds `fill`,
+    so a write past column ncols of the last row, or past row P, shows."""
+    buf = torch.full((P * ncols + 4096,), fill, dtype=dtype, device="cuda")
+    return buf, buf[: P * ncols].view(P, ncols)
+
+
+@pytest.mark.parametrize("N,act", [(160, "none"), (96, "none"), (96, "silu_mul"), (288, "silu_mul")])
+@pytest.mark.parametrize("sched", ["decode", "prefill", "auto"])
+@pytest.mark.parametrize("xdt,sfl,wl", [("bf16", "rows", "rows"), ("f16", "quads", "tiled")])
+def test_nvfp4_n_multiple_of_32(N, act, sched, xdt, sfl, wl):
+    # N % 32 == 0 but not a multiple of 128 (SILU_MUL: I = 48, 144, a
+    # multiple of 16): PREFILL falls back to the streaming schedule; every
+    # column is computed and nothing past the output is written.
+    T, E, k, H = 90, 5, 2, 256
+    d = synth.nvfp4_moe(49, T, E, k, H, N // 2, routing="repeat")
+    xg, xb = _xin(d["x"], xdt)
+    sg, sa = _sf(d["s1"], sfl)
+    wg, wa = _w(d["w1"], wl)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    P = T * k
+    ncols = N // 2 if act == "silu_mul" else N
+    buf, out = _guarded(P, ncols, torch.float32, 3.0)
+    mq.grouped_gemm_qnvfp4(xg, wg, sg, dev(d["g1"]), offs, srt, k, act=act, out_dtype=torch.float32,
+                           sched=sched, out=out)
+    ref = oracle.grouped_gemm_qnvfp4(xb, "token", wa, sa, d["g1"], host(offs), host(srt), k, act=act,
+                                     x_dtype=xdt, sf_layout=sfl, w_layout=wl)["y"]
+    n = ref.shape[0]
+    assert_rows_close(host(out)[:n], ref, what=f"nvfp4 N={N} {act} {sched}")
+    assert torch.all(buf[n * ncols:] == 3.0), "written past the routed rows or the last column"
+
+
+@pytest.mark.parametrize("N,act", [(160, "none"), (96, "none"), (96, "silu_mul"), (288, "silu_mul")])
+@pytest.mark.parametrize("odt", [torch.int32, torch.float16])
+def test_int4_n_multiple_of_32(N, act, odt):
+    # a partial last column tile: masked columns of the int8-MFMA tile are
+    # neither stored nor allowed to read past the weights
+    if odt == torch.int32 and act == "silu_mul":
+        pytest.skip("raw accumulators need act none")
+    T, E, k, K = 300, 5, 2, 384
+    d = synth.int4_moe(25, T, E, k, N, K, routing="repeat")
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    P = T * k
+    ncols = N // 2 if act == "silu_mul" else N
+    fill = 777 if odt == torch.int32 else 3.0
+    buf, out = _guarded(P, ncols, odt, fill)
+    mq.grouped_gemm_qint4(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]), offs, srt, k,
+                          act=act, out_dtype=odt, out=out)
+    ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], host(offs),
+                                    host(srt), k, act=act)
+    n = ref["y"].shape[0]
+    if odt == torch.int32:
+        assert np.array_equal(host(out)[:n], ref["acc"])
+    else:
+        assert_rows_close(host(out)[:n], ref["y"], what=f"int4 N={N} {act}")
+    assert torch.all(buf[n * ncols:] == fill), "written past the routed rows or the last column"
+
+
+# ------------------------------------------------------------------ no routed pair at all
+def test_every_id_minus_one_gemms_write_nothing_and_combine_writes_zeros():
+    # CUTLASS discussion #2855 returns early with no problem to run; here the
+    # route table is empty, every GEMM (both schedules) leaves its output
+    # untouched and the combine writes zero rows.
+    T, k, E = 37, 2, 4
+    ids = -np.ones((T, k), np.int32)
+    offs, srt, p2s, ninv = mq.moe_route_prep(dev(ids), E)
+    assert host(offs).tolist() == [0] * (E + 1) and int(host(ninv)[0]) == 0
+    assert np.all(host(srt) == -1) and np.all(host(p2s) == -1)
+    P = T * k
+    i4 = synth.int4_moe(26, T, E, k, 256, 256)
+    f8 = synth.fp8_block(36, 0, 256, 256, E=E, T=T, k=k)
+    nv = synth.nvfp4_moe(50, T, E, k, 256, 128)
+    for sched in ("auto", "decode", "prefill"):
+        out = torch.full((P, 256), 5, dtype=torch.int32, device="cuda")
+        mq.grouped_gemm_qint4(dev(i4["a"]), dev(i4["a_scale"]), dev(i4["w"]), dev(i4["w_scale"]), offs, srt, k,
+                              out_dtype=torch.int32, out=out, sched=sched)
+        assert torch.all(out == 5)
+        out = torch.full((P, 256), 5.0, dtype=torch.bfloat16, device="cuda")
+        mq.grouped_gemm_qfp8_block(dev(f8["a"]), dev(f8["a_scale"]), dev(f8["w"]), dev(f8["w_scale"]), offs, srt,
+                                   k, out=out, sched=sched)
+        assert torch.all(out == 5.0)
+        for act in ("none", "silu_mul"):
+            out = torch.full((P, 256 if act == "none" else 128), 5.0, dtype=torch.bfloat16, device="cuda")
+            mq.grouped_gemm_qnvfp4(dev(nv["x"]), dev(nv["w1"]), dev(nv["s1"]), dev(nv["g1"]), offs, srt, k,
+                                   act=act, out=out, sched=sched)
+            assert torch.all(out == 5.0)
+    y = torch.full((P, 256), 9.0, dtype=torch.float16, device="cuda")
+    comb = mq.moe_scatter_combine(y, p2s, dev(synth.softmax_weights(np.random.default_rng(0), T, k)))
+    pairs = mq.moe_sum_pairs(y, p2s, T, k)
+    torch.cuda.synchronize()
+    assert torch.all(comb == 0) and torch.all(pairs == 0)

@@ -1,8 +1,16 @@
 """Parity at the workloads' full sizes, in the launch configuration the
-benchmark times (bench.Workload issues the calls).  Route tables must be
-equal; expert outputs are checked on sampled rows that the oracle computes
-one by one; the combine is checked in full against the oracle applied to the
-GPU's own expert rows."""
+benchmark times (bench.Workload issues the calls).
+
+Coverage: route tables equal; every sorted row of every GEMM is compared,
+in full where the oracle is cheap and otherwise on a column sample with one
+column in every 16 (NVFP4) or 32 (INT4) consecutive output columns, so that
+every (expert, m-tile, n-tile) work item of every schedule and every wave's
+column slice is checked.  End to end, the oracle's own chain (route -> FC1 ->
+rounded h -> FC2 -> rounded y -> combine) is compared with the GPU's output
+on every token (decode) or on a token sample that includes the tokens of the
+largest and the smallest expert."""
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -19,8 +27,11 @@ def _gpu():
         pytest.skip("no GPU")
 
 
+@functools.lru_cache(maxsize=3)
 def _run(idx, fc2="sorted", act="f16", sfl="quads", wlay="tiled"):
+    """One bench step of workload idx (cached: each test reads its outputs)."""
     import bench
+    print(f"[workload {idx} fc2={fc2} act={act} sf={sfl} w={wlay}]", flush=True)
     wl = bench.Workload(idx, fc2, act, sfl, wlay)
     wl.step()
     torch.cuda.synchronize()
@@ -35,174 +46,234 @@ def _check_route(wl):
     return ref
 
 
-def _sample_rows(offs, n_per=2, max_experts=6, seed=0):
-    """A few sorted rows from the largest, the smallest and random non-empty experts."""
+def _stratified_cols(n_out, block, seed):
+    """One random column in each run of `block` consecutive output columns."""
     rng = np.random.default_rng(seed)
-    sizes = np.diff(offs)
+    starts = np.arange(0, n_out, block)
+    return starts + rng.integers(0, np.minimum(block, n_out - starts))
+
+
+def _token_sample(off, srt, k, T, n_rand, seed):
+    """Tokens of the largest and the smallest non-empty expert, the first
+    and last token, and n_rand random ones."""
+    rng = np.random.default_rng(seed)
+    sizes = np.diff(off)
     ne = np.nonzero(sizes)[0]
-    order = ne[np.argsort(sizes[ne])]
-    pick = list(dict.fromkeys([order[-1], order[0]] + list(rng.permutation(ne)[: max_experts - 2])))
-    rows = []
-    for e in pick[:max_experts]:
-        lo, hi = offs[e], offs[e + 1]
-        rows += list(rng.choice(np.arange(lo, hi), size=min(n_per, hi - lo), replace=False))
-        rows.append(hi - 1)
-    return np.unique(np.array(rows, np.int64))
+    big, small = ne[np.argmax(sizes[ne])], ne[np.argmin(sizes[ne])]
+    pick = [srt[off[big]] // k, srt[off[big + 1] - 1] // k, srt[off[small]] // k, 0, T - 1]
+    pick += list(rng.choice(T, n_rand, replace=False))
+    return np.array(list(dict.fromkeys(int(t) for t in pick)))
 
 
+# ------------------------------------------------------------------ config 0
 def test_workload0_w4a4_tiny_end_to_end():
     wl = _run(0)
     off, srt, p2s, _ = _check_route(wl)
     d = wl.d
     ref = oracle.int4_layer(d)
-    assert_rows_close(host(wl.y), ref["y"], what="y")
-    assert_rows_close(host(wl.out), oracle.scatter_combine(host(wl.y), p2s, d["topk_weights"]),
-                      what="combine (GPU y)")
+    assert_rows_close(host(wl.y)[: ref["y"].shape[0]], ref["y"], what="y")
     assert_rows_close(host(wl.out), ref["out"], what="layer")
     acc = wl.mq.grouped_gemm_qint4(wl.a, wl.sa, wl.w, wl.sw, wl.route_out[0], wl.route_out[1], wl.k,
                                    out_dtype=torch.int32)
     assert np.array_equal(host(acc), ref["acc"])
 
 
-def test_workload1_fp8_dense_sampled_rows():
+# ------------------------------------------------------------------ config 1
+def test_workload1_fp8_dense_every_output():
     wl = _run(1)
-    _check_route(wl)
+    off, srt, _, _ = _check_route(wl)
     d = wl.d
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 511, 1023],
-                                     np.random.default_rng(1).choice(1024, 40, replace=False)]))
-    ref = oracle.grouped_gemm_qfp8_block(d["a"], d["a_scale"], "token", d["w"], d["w_scale"],
-                                         host(wl.route_out[0]), host(wl.route_out[1]), 1, rows=rows)["y"]
-    assert_rows_close(host(wl.y)[rows], ref, what="fp8 full size")
+    ref = oracle.grouped_gemm_qfp8_block(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], off, srt, 1)["y"]
+    assert_rows_close(host(wl.y), ref, what="fp8 1024x4096x7168")
 
 
-def _nvfp4_checks(wl, n_per):
-    off, srt, p2s, _ = _check_route(wl)
+# ------------------------------------------------------------------ NVFP4 (configs 2, 3)
+def _nvfp4_rows_layout(wl):
+    """The workload's weights in the oracle's row-major layouts (one
+    conversion per test instead of one per oracle call)."""
+    w1 = oracle.rows_from_tiles(wl.w1_host) if wl.wl == "tiled" else wl.w1_host
+    w2 = oracle.rows_from_tiles(wl.w2_host) if wl.wl == "tiled" else wl.w2_host
+    s1 = oracle.rows_from_quads(wl.s1_host) if wl.sfl == "quads" else wl.s1_host
+    s2 = oracle.rows_from_quads(wl.s2_host) if wl.sfl == "quads" else wl.s2_host
+    return w1, s1, w2, s2
+
+
+def _x_bits(wl):
     d = wl.d
-    rows = _sample_rows(off, n_per=n_per)
-    xdt = wl.act
-    if xdt == "f16":
+    if wl.act == "f16":
         xb = oracle.bf16_to_f16_bits(d["x"])
         assert np.array_equal(host(wl.xh.view(torch.int16)).view(np.uint16), xb)
-    else:
-        xb = d["x"]
-    h_ref = oracle.grouped_gemm_qnvfp4(xb, "token", wl.w1_host, wl.s1_host, d["g1"], off, srt, d["k"],
-                                       act="silu_mul", rows=rows, x_dtype=xdt, sf_layout=wl.sfl,
-                                       w_layout=wl.wl)["y"]
-    assert_rows_close(host(wl.h)[rows], h_ref, what="FC1 h")
-    # FC2 consumes the GPU's h (per-call parity)
-    hb = host(wl.h.view(torch.int16)).view(np.uint16) if xdt == "f16" else bf16_bits(wl.h)
-    y_ref = oracle.grouped_gemm_qnvfp4(hb, "sorted", wl.w2_host, wl.s2_host, d["g2"], off, srt, d["k"],
-                                       rows=rows, x_dtype=xdt, sf_layout=wl.sfl, w_layout=wl.wl)["y"]
-    assert_rows_close(host(wl.y)[rows], y_ref, what="FC2 y")
-    out_ref = oracle.scatter_combine(host(wl.y), p2s, d["topk_weights"])
-    assert_rows_close(host(wl.out), out_ref, what="combine")
+        return xb
+    return d["x"]
 
 
-def test_workload2_nvfp4_decode():
-    _nvfp4_checks(_run(2), n_per=1)
+def _h_bits(wl):
+    return host(wl.h.view(torch.int16)).view(np.uint16) if wl.act == "f16" else bf16_bits(wl.h)
 
 
-def test_workload3_nvfp4_prefill_zipf():
+def _nvfp4_per_call(wl, block_h, block_y):
+    """FC1 and FC2 on every sorted row (FC2 on the GPU's own h), on a
+    stratified column sample when block_* > 1; the combine on every token
+    against the oracle applied to the GPU's own y."""
+    off, srt, p2s, _ = _check_route(wl)
+    d = wl.d
+    w1, s1, w2, s2 = _nvfp4_rows_layout(wl)
+    n = int(off[-1])
+    ch = None if block_h == 1 else _stratified_cols(d["I"], block_h, 31)
+    h_ref = oracle.grouped_gemm_qnvfp4(_x_bits(wl), "token", w1, s1, d["g1"], off, srt, d["k"],
+                                       act="silu_mul", x_dtype=wl.act, cols=ch)["y"]
+    hg = host(wl.h)[:n]
+    assert_rows_close(hg if ch is None else hg[:, ch], h_ref, what="FC1 h")
+    cy = None if block_y == 1 else _stratified_cols(d["H"], block_y, 32)
+    y_ref = oracle.grouped_gemm_qnvfp4(_h_bits(wl), "sorted", w2, s2, d["g2"], off, srt, d["k"],
+                                       x_dtype=wl.act, cols=cy)["y"]
+    yg = host(wl.y)[:n]
+    assert_rows_close(yg if cy is None else yg[:, cy], y_ref, what="FC2 y")
+    assert_rows_close(host(wl.out), oracle.scatter_combine(host(wl.y), p2s, d["topk_weights"]),
+                      what="combine (GPU y)")
+
+
+def _nvfp4_end_to_end(wl, tokens):
+    w1, s1, w2, s2 = _nvfp4_rows_layout(wl)
+    d = dict(wl.d, w1=w1, s1=s1, w2=w2, s2=s2)
+    ref = oracle.nvfp4_layer(d, rows_dtype="bf16", tokens=tokens, x_dtype=wl.act)
+    assert_rows_close(host(wl.out)[tokens], ref["out"], what="layer (oracle chain)")
+
+
+def test_workload2_nvfp4_decode_every_row():
+    _nvfp4_per_call(_run(2), block_h=1, block_y=1)
+
+
+def test_workload2_nvfp4_decode_end_to_end_every_token():
+    wl = _run(2)
+    _nvfp4_end_to_end(wl, np.arange(wl.T))
+
+
+def test_workload3_nvfp4_prefill_zipf_every_row():
     wl = _run(3)
     sizes = np.diff(host(wl.route_out[0]))
     assert sizes.min() == 0 and sizes.max() > 1000      # skewed, with empty experts
-    _nvfp4_checks(wl, n_per=2)
+    _nvfp4_per_call(wl, block_h=16, block_y=16)
+
+
+def test_workload3_nvfp4_prefill_end_to_end_token_sample():
+    wl = _run(3)
+    off, srt, _, _ = _check_route(wl)
+    _nvfp4_end_to_end(wl, _token_sample(off, srt, wl.k, wl.T, 3, 33))
 
 
 @pytest.mark.parametrize("idx", [2, 3])
 def test_nvfp4_workloads_with_bf16_activations_rows_scales(idx):
     wl = _run(idx, act="bf16", sfl="rows", wlay="rows")
-    _nvfp4_checks(wl, n_per=1 if idx == 2 else 2)
+    _nvfp4_per_call(wl, block_h=1 if idx == 2 else 16, block_y=1 if idx == 2 else 16)
 
 
 @pytest.mark.parametrize("idx", [2, 3])
 def test_nvfp4_workloads_with_fc2_pair_epilogue(idx):
-    # the step with the top-k weight in FC2's epilogue: pair rows of sampled
-    # sorted rows, then the whole pair sum against the oracle on the GPU's rows
+    # the step with the top-k weight in FC2's epilogue: every pair row (on
+    # the column sample at prefill size), then the whole pair sum against
+    # the oracle on the GPU's rows
     wl = _run(idx, fc2="pair")
     off, srt, p2s, _ = _check_route(wl)
     d = wl.d
-    rows = _sample_rows(off, n_per=1 if idx == 2 else 2)
-    hb = host(wl.h.view(torch.int16)).view(np.uint16)
-    y_ref = oracle.grouped_gemm_qnvfp4(hb, "sorted", wl.w2_host, wl.s2_host, d["g2"], off, srt, d["k"], rows=rows,
-                                       x_dtype="f16", sf_layout="quads", w_layout="tiled")["y"]
-    pairs = srt[rows]
+    _, _, w2, s2 = _nvfp4_rows_layout(wl)
+    n = int(off[-1])
+    cy = None if idx == 2 else _stratified_cols(d["H"], 16, 34)
+    y_ref = oracle.grouped_gemm_qnvfp4(_h_bits(wl), "sorted", w2, s2, d["g2"], off, srt, d["k"],
+                                       x_dtype="f16", cols=cy)["y"]
+    pairs = srt[:n]
     w = d["topk_weights"].reshape(-1)[pairs]
-    assert_rows_close(host(wl.y)[pairs], w[:, None] * y_ref, what="FC2 pair rows")
     yp = host(wl.y)
+    got = yp[pairs] if cy is None else yp[pairs][:, cy]
+    assert_rows_close(got, w[:, None] * y_ref, what="FC2 pair rows")
     yp[p2s < 0] = 0
     assert_rows_close(host(wl.out), oracle.sum_pairs(yp, p2s, wl.T, wl.k), what="pair sum")
 
 
-def test_workload4_w4a4_mixtral():
+# ------------------------------------------------------------------ config 4
+def test_workload4_w4a4_mixtral_every_row():
     wl = _run(4)
     off, srt, p2s, _ = _check_route(wl)
     d = wl.d
-    rows = _sample_rows(off, n_per=2, max_experts=3)
+    n = int(off[-1])
+    ch = _stratified_cols(d["N"] // 2, 32, 41)
     h_ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], off, srt,
-                                      d["k"], act="silu_mul", rows=rows)["y"]
-    assert_rows_close(host(wl.h)[rows], h_ref, what="FC1 h")
-    # FC2 raw accumulators at full size, bit-exact on the sampled rows
+                                      d["k"], act="silu_mul", cols=ch)["y"]
+    assert_rows_close(host(wl.h)[:n][:, ch], h_ref, what="FC1 h")
+    # FC2 raw accumulators at full size, bit-exact on every row
     acc = wl.mq.grouped_gemm_qint4(wl.a2, wl.sa2, wl.w2, wl.sw2, wl.route_out[0], wl.route_out[1],
                                    wl.k, a_row="sorted", out_dtype=torch.int32)
+    cy = _stratified_cols(d["N2"], 32, 42)
     ref2 = oracle.grouped_gemm_qint4(d["a2"], d["a2_scale"], "sorted", d["w2"], d["w2_scale"], off,
-                                     srt, d["k"], rows=rows)
-    assert np.array_equal(host(acc)[rows], ref2["acc"])
-    assert_rows_close(host(wl.y)[rows], ref2["y"], what="FC2 y")
+                                     srt, d["k"], cols=cy)
+    assert np.array_equal(host(acc)[:n][:, cy], ref2["acc"])
+    assert_rows_close(host(wl.y)[:n][:, cy], ref2["y"], what="FC2 y")
     assert_rows_close(host(wl.out), oracle.scatter_combine(host(wl.y), p2s, d["topk_weights"]),
-                      what="combine")
+                      what="combine (GPU y)")
 
 
-def test_workload5_int4_quantizer_sampled_rows():
+def test_workload4_w4a4_mixtral_end_to_end_token_sample():
+    wl = _run(4)
+    off, srt, _, _ = _check_route(wl)
+    tok = _token_sample(off, srt, wl.k, wl.T, 3, 43)
+    d = dict(wl.d, H=wl.d["K"], I=wl.d["N"] // 2)
+    ref = oracle.int4_ffn_layer(d, tok)
+    assert_rows_close(host(wl.h)[ref["rows"]], ref["h"], what="FC1 h (oracle chain)")
+    assert_rows_close(host(wl.out)[tok], ref["out"], what="layer (oracle chain)")
+
+
+# ------------------------------------------------------------------ next-row workloads
+def test_workload5_int4_quantizer_every_row():
     wl = _run(5)
-    x = wl.d["x"]
-    rows = np.unique(np.concatenate([[0, x.shape[0] - 1],
-                                     np.random.default_rng(5).integers(0, x.shape[0], 62)]))
-    ref_q, ref_s = oracle.quantize_int4_rows(x[rows])
-    assert np.array_equal(host(wl.qs)[rows], ref_s)
-    assert np.array_equal(host(wl.q)[rows], ref_q)
+    ref_q, ref_s = oracle.quantize_int4_rows(wl.d["x"])
+    assert np.array_equal(host(wl.qs), ref_s)
+    assert np.array_equal(host(wl.q), ref_q)
 
 
-def test_workload6_fp8_moe_decode_sampled_rows():
+def test_workload6_fp8_moe_decode_every_row():
     # the FP8 block-scaled kernel under routing, weight-streaming schedule
     wl = _run(6)
     off, srt, p2s, _ = _check_route(wl)
     d = wl.d
-    rows = _sample_rows(off, n_per=2, max_experts=6)
     ref = oracle.grouped_gemm_qfp8_block(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], off, srt,
-                                         d["k"], rows=rows)["y"]
-    assert_rows_close(host(wl.y)[rows], ref, what="fp8 decode full size")
+                                         d["k"])["y"]
+    assert_rows_close(host(wl.y)[: ref.shape[0]], ref, what="fp8 decode full size")
 
 
-def test_workload7_nvfp4_repack_sampled_experts():
+def test_workload7_nvfp4_repack_every_expert():
     wl = _run(7)
     d = wl.d
-    experts = np.unique(np.concatenate([[0, 1, d["E"] - 1],
-                                        np.random.default_rng(7).integers(0, d["E"], 3)]))
-    for e in experts:
-        rw, rs = oracle.repack_nvfp4(d["w"][e:e + 1], d["sf"][e:e + 1], bool(wl.cfg["swap"]))
-        assert np.array_equal(host(wl.w_out[int(e)]), rw[0]), e
-        assert np.array_equal(host(wl.sf_out[int(e)]), rs[0]), e
+    rw, rs = oracle.repack_nvfp4(d["w"], d["sf"], bool(wl.cfg["swap"]))
+    assert np.array_equal(host(wl.w_out), rw)
+    assert np.array_equal(host(wl.sf_out).reshape(rs.shape), rs)
 
 
-def test_workload8_w4a4_chain_from_fp16():
+def test_workload8_w4a4_chain_from_fp16_every_row():
     # every step of the chain against the oracle applied to the GPU's own
-    # input of that step; both quantizations bit-exact on sampled rows
+    # input of that step; both quantizations bit-exact on every row
     wl = _run(8)
     off, srt, p2s, _ = _check_route(wl)
     d = wl.d
-    rows = _sample_rows(off, n_per=2, max_experts=3)
-    toks = np.unique(np.concatenate([[0, wl.T - 1], srt[rows] // wl.k]))
-    ref_q, ref_s = oracle.quantize_int4_rows(d["x"][toks])
-    assert np.array_equal(host(wl.qx)[toks], ref_q) and np.array_equal(host(wl.sx)[toks], ref_s)
-    qx, sx = host(wl.qx), host(wl.sx)
-    h_ref = oracle.grouped_gemm_qint4(qx, sx, "token", d["w"], d["w_scale"], off, srt, d["k"],
-                                      act="silu_mul", rows=rows)["y"]
-    assert_rows_close(host(wl.h)[rows], h_ref, what="FC1 h")
-    hq_ref, hs_ref = oracle.quantize_int4_rows(host(wl.h)[rows].astype(np.float16))
-    assert np.array_equal(host(wl.qh)[rows], hq_ref) and np.array_equal(host(wl.sh)[rows], hs_ref)
+    n = int(off[-1])
+    ref_q, ref_s = oracle.quantize_int4_rows(d["x"])
+    assert np.array_equal(host(wl.qx), ref_q) and np.array_equal(host(wl.sx), ref_s)
+    ch = _stratified_cols(d["I"], 32, 81)
+    h_ref = oracle.grouped_gemm_qint4(host(wl.qx), host(wl.sx), "token", d["w"], d["w_scale"], off, srt,
+                                      d["k"], act="silu_mul", cols=ch)["y"]
+    assert_rows_close(host(wl.h)[:n][:, ch], h_ref, what="FC1 h")
+    hq_ref, hs_ref = oracle.quantize_int4_rows(host(wl.h)[:n].astype(np.float16))
+    assert np.array_equal(host(wl.qh)[:n], hq_ref) and np.array_equal(host(wl.sh)[:n], hs_ref)
+    cy = _stratified_cols(d["H"], 32, 82)
     y_ref = oracle.grouped_gemm_qint4(host(wl.qh), host(wl.sh), "sorted", d["w2"], d["w2_scale"], off, srt,
-                                      d["k"], rows=rows)["y"]
-    assert_rows_close(host(wl.y)[rows], y_ref, what="FC2 y")
+                                      d["k"], cols=cy)["y"]
+    assert_rows_close(host(wl.y)[:n][:, cy], y_ref, what="FC2 y")
     assert_rows_close(host(wl.out), oracle.scatter_combine(host(wl.y), p2s, d["topk_weights"]),
-                      what="combine")
+                      what="combine (GPU y)")
+
+
+def test_workload8_w4a4_chain_end_to_end_token_sample():
+    wl = _run(8)
+    off, srt, _, _ = _check_route(wl)
+    tok = _token_sample(off, srt, wl.k, wl.T, 3, 83)
+    ref = oracle.int4_ffn_layer(wl.d, tok, chain=True)
+    assert_rows_close(host(wl.out)[tok], ref["out"], what="W4A4 layer (oracle chain)")

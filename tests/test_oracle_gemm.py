@@ -273,3 +273,48 @@ def test_nvfp4_f16_activations_equal_bf16_when_exact():
     assert xh[0, 0] == 0
     with pytest.raises(ValueError):
         oracle.grouped_gemm_qnvfp4(xh, "token", d["w1"], d["s1"], d["g1"], off, srt, 1, x_dtype="f32")
+
+
+# ------------------------------------------------------------------ column selection
+def test_column_selection_is_the_same_contraction():
+    # `cols` picks the weight rows of the selected outputs before the matmul:
+    # integers bit-exact, floats equal up to fp64 summation order (the BLAS
+    # may block a narrower product differently)
+    d = synth.int4_moe(13, T=30, E=3, k=2, N=96, K=256, routing="repeat")
+    off, srt, inv, _ = oracle.route_prep(d["topk_ids"], 3)
+    full = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], off, srt, 2)
+    cols = np.array([0, 5, 31, 32, 95])
+    part = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], off, srt, 2,
+                                     cols=cols)
+    assert np.array_equal(part["acc"], full["acc"][:, cols])
+    assert np.array_equal(part["y"], full["y"][:, cols])
+    fs = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], off, srt, 2,
+                                   act="silu_mul")["y"]
+    hc = np.array([0, 7, 47])
+    ps = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], off, srt, 2,
+                                   act="silu_mul", cols=hc)
+    assert np.array_equal(ps["y"], fs[:, hc])
+    # the gate rows come first, then the matching up rows
+    assert np.array_equal(oracle.weight_rows(96, "silu_mul", hc), np.array([0, 7, 47, 48, 55, 95]))
+    with pytest.raises(ValueError):
+        oracle.weight_rows(96, "silu_mul", [48])
+
+    f = synth.fp8_block(14, 0, 384, 256, E=2, T=20, k=2)
+    off, srt, inv, _ = oracle.route_prep(f["topk_ids"], 2)
+    full = oracle.grouped_gemm_qfp8_block(f["a"], f["a_scale"], "token", f["w"], f["w_scale"], off, srt, 2)["y"]
+    c = np.array([1, 127, 128, 300, 383])      # three 128-column scale blocks
+    part = oracle.grouped_gemm_qfp8_block(f["a"], f["a_scale"], "token", f["w"], f["w_scale"], off, srt, 2,
+                                          cols=c)["y"]
+    np.testing.assert_allclose(part, full[:, c], rtol=1e-12, atol=0)
+
+    n = synth.nvfp4_moe(15, 24, 3, 2, 128, 64, routing="repeat")
+    off, srt, inv, _ = oracle.route_prep(n["topk_ids"], 3)
+    for sfl, wl in (("rows", "rows"), ("quads", "tiled")):
+        w = n["w1"] if wl == "rows" else oracle.tiles_from_rows(n["w1"])
+        s = n["s1"] if sfl == "rows" else oracle.quads_from_rows(n["s1"])
+        full = oracle.grouped_gemm_qnvfp4(n["x"], "token", w, s, n["g1"], off, srt, 2, act="silu_mul",
+                                          sf_layout=sfl, w_layout=wl)["y"]
+        hc = np.array([0, 15, 16, 63])
+        part = oracle.grouped_gemm_qnvfp4(n["x"], "token", w, s, n["g1"], off, srt, 2, act="silu_mul",
+                                          sf_layout=sfl, w_layout=wl, cols=hc)["y"]
+        np.testing.assert_allclose(part, full[:, hc], rtol=1e-12, atol=0)
