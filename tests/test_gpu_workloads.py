@@ -53,6 +53,26 @@ def _stratified_cols(n_out, block, seed):
     return starts + rng.integers(0, np.minimum(block, n_out - starts))
 
 
+def _assert_cols_close(gpu_rows, cols, ref_cols, full_ref, what):
+    """The per-row tolerance on a column sample.  The bound is 2e-3 times the
+    L2 norm of the whole oracle row, which is at least the norm over the
+    sampled columns; rows that pass against the sampled norm pass, and any
+    other row is recomputed by the oracle over all its columns
+    (full_ref(row_indices) -> rows) and judged against its full norm."""
+    gpu_rows = np.asarray(gpu_rows)
+    sel = gpu_rows if cols is None else gpu_rows[:, cols]
+    ref_cols = np.asarray(ref_cols, np.float64)
+    assert np.all(np.isfinite(sel)), f"{what}: non-finite output"
+    err = np.abs(sel - ref_cols).max(axis=1)
+    norm = np.linalg.norm(ref_cols, axis=1)
+    unsure = np.nonzero(err > 2e-3 * norm)[0]
+    if cols is None or unsure.size == 0:
+        assert_rows_close(sel, ref_cols, what=what)
+        return
+    assert unsure.size <= 0.05 * sel.shape[0], f"{what}: {unsure.size} rows exceed the sampled-norm bound"
+    assert_rows_close(gpu_rows[unsure], full_ref(unsure), what=what + " (whole rows)")
+
+
 def _token_sample(off, srt, k, T, n_rand, seed):
     """Tokens of the largest and the smallest non-empty expert, the first
     and last token, and n_rand random ones."""
@@ -119,16 +139,15 @@ def _nvfp4_per_call(wl, block_h, block_y):
     d = wl.d
     w1, s1, w2, s2 = _nvfp4_rows_layout(wl)
     n = int(off[-1])
+    xb, hb = _x_bits(wl), _h_bits(wl)
+    fc1 = lambda cols=None, rows=None: oracle.grouped_gemm_qnvfp4(
+        xb, "token", w1, s1, d["g1"], off, srt, d["k"], act="silu_mul", x_dtype=wl.act, cols=cols, rows=rows)["y"]
+    fc2 = lambda cols=None, rows=None: oracle.grouped_gemm_qnvfp4(
+        hb, "sorted", w2, s2, d["g2"], off, srt, d["k"], x_dtype=wl.act, cols=cols, rows=rows)["y"]
     ch = None if block_h == 1 else _stratified_cols(d["I"], block_h, 31)
-    h_ref = oracle.grouped_gemm_qnvfp4(_x_bits(wl), "token", w1, s1, d["g1"], off, srt, d["k"],
-                                       act="silu_mul", x_dtype=wl.act, cols=ch)["y"]
-    hg = host(wl.h)[:n]
-    assert_rows_close(hg if ch is None else hg[:, ch], h_ref, what="FC1 h")
+    _assert_cols_close(host(wl.h)[:n], ch, fc1(cols=ch), lambda r: fc1(rows=r), "FC1 h")
     cy = None if block_y == 1 else _stratified_cols(d["H"], block_y, 32)
-    y_ref = oracle.grouped_gemm_qnvfp4(_h_bits(wl), "sorted", w2, s2, d["g2"], off, srt, d["k"],
-                                       x_dtype=wl.act, cols=cy)["y"]
-    yg = host(wl.y)[:n]
-    assert_rows_close(yg if cy is None else yg[:, cy], y_ref, what="FC2 y")
+    _assert_cols_close(host(wl.y)[:n], cy, fc2(cols=cy), lambda r: fc2(rows=r), "FC2 y")
     assert_rows_close(host(wl.out), oracle.scatter_combine(host(wl.y), p2s, d["topk_weights"]),
                       what="combine (GPU y)")
 
@@ -179,13 +198,14 @@ def test_nvfp4_workloads_with_fc2_pair_epilogue(idx):
     _, _, w2, s2 = _nvfp4_rows_layout(wl)
     n = int(off[-1])
     cy = None if idx == 2 else _stratified_cols(d["H"], 16, 34)
-    y_ref = oracle.grouped_gemm_qnvfp4(_h_bits(wl), "sorted", w2, s2, d["g2"], off, srt, d["k"],
-                                       x_dtype="f16", cols=cy)["y"]
+    hb = _h_bits(wl)
+    fc2 = lambda cols=None, rows=None: oracle.grouped_gemm_qnvfp4(
+        hb, "sorted", w2, s2, d["g2"], off, srt, d["k"], x_dtype="f16", cols=cols, rows=rows)["y"]
     pairs = srt[:n]
     w = d["topk_weights"].reshape(-1)[pairs]
     yp = host(wl.y)
-    got = yp[pairs] if cy is None else yp[pairs][:, cy]
-    assert_rows_close(got, w[:, None] * y_ref, what="FC2 pair rows")
+    _assert_cols_close(yp[pairs], cy, w[:, None] * fc2(cols=cy), lambda r: w[r, None] * fc2(rows=r),
+                       "FC2 pair rows")
     yp[p2s < 0] = 0
     assert_rows_close(host(wl.out), oracle.sum_pairs(yp, p2s, wl.T, wl.k), what="pair sum")
 
@@ -197,17 +217,19 @@ def test_workload4_w4a4_mixtral_every_row():
     d = wl.d
     n = int(off[-1])
     ch = _stratified_cols(d["N"] // 2, 32, 41)
-    h_ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], off, srt,
-                                      d["k"], act="silu_mul", cols=ch)["y"]
-    assert_rows_close(host(wl.h)[:n][:, ch], h_ref, what="FC1 h")
+    fc1 = lambda cols=None, rows=None: oracle.grouped_gemm_qint4(
+        d["a"], d["a_scale"], "token", d["w"], d["w_scale"], off, srt, d["k"], act="silu_mul", cols=cols,
+        rows=rows)["y"]
+    _assert_cols_close(host(wl.h)[:n], ch, fc1(cols=ch), lambda r: fc1(rows=r), "FC1 h")
     # FC2 raw accumulators at full size, bit-exact on every row
     acc = wl.mq.grouped_gemm_qint4(wl.a2, wl.sa2, wl.w2, wl.sw2, wl.route_out[0], wl.route_out[1],
                                    wl.k, a_row="sorted", out_dtype=torch.int32)
     cy = _stratified_cols(d["N2"], 32, 42)
-    ref2 = oracle.grouped_gemm_qint4(d["a2"], d["a2_scale"], "sorted", d["w2"], d["w2_scale"], off,
-                                     srt, d["k"], cols=cy)
+    fc2 = lambda cols=None, rows=None: oracle.grouped_gemm_qint4(
+        d["a2"], d["a2_scale"], "sorted", d["w2"], d["w2_scale"], off, srt, d["k"], cols=cols, rows=rows)
+    ref2 = fc2(cols=cy)
     assert np.array_equal(host(acc)[:n][:, cy], ref2["acc"])
-    assert_rows_close(host(wl.y)[:n][:, cy], ref2["y"], what="FC2 y")
+    _assert_cols_close(host(wl.y)[:n], cy, ref2["y"], lambda r: fc2(rows=r)["y"], "FC2 y")
     assert_rows_close(host(wl.out), oracle.scatter_combine(host(wl.y), p2s, d["topk_weights"]),
                       what="combine (GPU y)")
 
@@ -258,15 +280,17 @@ def test_workload8_w4a4_chain_from_fp16_every_row():
     ref_q, ref_s = oracle.quantize_int4_rows(d["x"])
     assert np.array_equal(host(wl.qx), ref_q) and np.array_equal(host(wl.sx), ref_s)
     ch = _stratified_cols(d["I"], 32, 81)
-    h_ref = oracle.grouped_gemm_qint4(host(wl.qx), host(wl.sx), "token", d["w"], d["w_scale"], off, srt,
-                                      d["k"], act="silu_mul", cols=ch)["y"]
-    assert_rows_close(host(wl.h)[:n][:, ch], h_ref, what="FC1 h")
+    qx, sx = host(wl.qx), host(wl.sx)
+    fc1 = lambda cols=None, rows=None: oracle.grouped_gemm_qint4(
+        qx, sx, "token", d["w"], d["w_scale"], off, srt, d["k"], act="silu_mul", cols=cols, rows=rows)["y"]
+    _assert_cols_close(host(wl.h)[:n], ch, fc1(cols=ch), lambda r: fc1(rows=r), "FC1 h")
     hq_ref, hs_ref = oracle.quantize_int4_rows(host(wl.h)[:n].astype(np.float16))
     assert np.array_equal(host(wl.qh)[:n], hq_ref) and np.array_equal(host(wl.sh)[:n], hs_ref)
     cy = _stratified_cols(d["H"], 32, 82)
-    y_ref = oracle.grouped_gemm_qint4(host(wl.qh), host(wl.sh), "sorted", d["w2"], d["w2_scale"], off, srt,
-                                      d["k"], cols=cy)["y"]
-    assert_rows_close(host(wl.y)[:n][:, cy], y_ref, what="FC2 y")
+    qh, sh = host(wl.qh), host(wl.sh)
+    fc2 = lambda cols=None, rows=None: oracle.grouped_gemm_qint4(
+        qh, sh, "sorted", d["w2"], d["w2_scale"], off, srt, d["k"], cols=cols, rows=rows)["y"]
+    _assert_cols_close(host(wl.y)[:n], cy, fc2(cols=cy), lambda r: fc2(rows=r), "FC2 y")
     assert_rows_close(host(wl.out), oracle.scatter_combine(host(wl.y), p2s, d["topk_weights"]),
                       what="combine (GPU y)")
 
