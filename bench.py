@@ -102,7 +102,7 @@ def measure_peaks(reps: int = 10):
     from quantized_moe_grouped_route_amd import build as b
     L = C.CDLL(b.PEAKS_LIB)
     L.moeq_peak_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_void_p]
-    L.moeq_peak_mfma.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    L.moeq_peak_mfma.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     st = torch.cuda.current_stream().cuda_stream
 
@@ -128,13 +128,33 @@ def measure_peaks(reps: int = 10):
     del buf
     grid = cus * 2
     sinkf = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    rng = np.random.default_rng(0)
     for kind, (name, K, spec) in MFMA_KINDS.items():
         iters = 20000 if K == 16 else 10000
-        ms = timed(lambda: L.moeq_peak_mfma(kind, grid, iters, sinkf.data_ptr(), st))
+        src = torch.from_numpy(peak_operands(rng, name, grid * 256 * 64)).cuda()
+        ms = timed(lambda: L.moeq_peak_mfma(kind, grid, iters, src.data_ptr(), sinkf.data_ptr(), st))
         ops = grid * 4 * iters * 4 * 2.0 * 32 * 32 * K
         res[name] = dict(value=ops / (ms * 1e-3) / 1e12, unit="TFLOP/s" if name != "int8" else "TOP/s",
                          spec=spec, ms=ms)
     return res
+
+
+def peak_operands(rng, name, nbytes):
+    """Operand bytes for the MFMA probe: finite values of the format, as the
+    grouped GEMMs feed it (int8: nibbles times 16, as the INT4 GEMM splits
+    them; fp8: e4m3 codes of N(0,1) values; bf16 / fp16: N(0,1); fp6 / fp4:
+    uniform codes, all of which are finite)."""
+    import torch
+    n = nbytes
+    if name == "int8":
+        return ((rng.integers(-8, 8, n) * 16) & 0xFF).astype(np.uint8)
+    if name == "fp8":
+        x = torch.from_numpy(rng.standard_normal(n).astype(np.float32))
+        return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    if name in ("bf16", "fp16"):
+        x = torch.from_numpy(rng.standard_normal(n // 2).astype(np.float32))
+        return x.to(torch.bfloat16 if name == "bf16" else torch.float16).view(torch.uint8).numpy()
+    return rng.integers(0, 256, n).astype(np.uint8)
 
 
 def measured_peak(key):

@@ -39,11 +39,13 @@ __global__ __launch_bounds__(256) void read_stream(const u32x4* __restrict__ src
 
 // Kinds: 0 int8 32x32x32, 1 fp8 e4m3 32x32x64, 2 bf16 32x32x16,
 // 3 fp16 32x32x16, 4 fp6 e3m2 32x32x64, 5 fp4 e2m1 32x32x64.
-// Four independent accumulators per wave; operands depend on the lane so
-// nothing folds; the accumulators are stored at the end.
+// Four independent accumulators per wave.  The operands are read once from
+// `src` (64 bytes per thread, finite values of the kind's format drawn by
+// the caller: the switching activity, and so the power and the clock, then
+// resembles real data); the accumulators are stored at the end.
 template <int KIND>
-__global__ __launch_bounds__(256) void mfma_loop(int iters, float* __restrict__ sink) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void mfma_loop(int iters, const v8i* __restrict__ src, float* __restrict__ sink) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   v16f f[4];
   v16i n[4];
 #pragma unroll
@@ -51,11 +53,9 @@ __global__ __launch_bounds__(256) void mfma_loop(int iters, float* __restrict__ 
     f[j] = v16f{};
     n[j] = v16i{};
   }
-  const int s = lane * 0x01010101 + (int)blockIdx.x;
-  v8i a8 = {s, s + 1, s + 2, s + 3, s + 4, s + 5, s + 6, s + 7};
-  v8i b8 = a8 ^ 0x5a5a5a5a;
-  v4i a4 = {s, s + 1, s + 2, s + 3};
-  v4i b4 = a4 ^ 0x5a5a5a5a;
+  const v8i a8 = src[2 * t], b8 = src[2 * t + 1];
+  const v4i a4 = {a8[0], a8[1], a8[2], a8[3]};
+  const v4i b4 = {b8[0], b8[1], b8[2], b8[3]};
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -85,8 +85,8 @@ __global__ __launch_bounds__(256) void mfma_loop(int iters, float* __restrict__ 
 }
 
 template <int KIND>
-hipError_t go(int grid, int iters, float* sink, hipStream_t st) {
-  hipLaunchKernelGGL(mfma_loop<KIND>, dim3(grid), dim3(256), 0, st, iters, sink);
+hipError_t go(int grid, int iters, const v8i* src, float* sink, hipStream_t st) {
+  hipLaunchKernelGGL(mfma_loop<KIND>, dim3(grid), dim3(256), 0, st, iters, src, sink);
   return hipGetLastError();
 }
 
@@ -103,20 +103,22 @@ int moeq_peak_read(const void* src, int64_t bytes, void* sink, int grid, void* s
 }
 
 // grid workgroups of 4 waves, each wave `iters` x 4 MFMAs of `kind`;
-// sink: grid * 256 floats.  Flops (ops) per MFMA: 2 * 32 * 32 * K with
-// K = 32 (int8), 64 (fp8, fp6, fp4), 16 (bf16, fp16).
-int moeq_peak_mfma(int kind, int grid, int iters, void* sink, void* stream) {
-  if (!sink || grid <= 0 || iters <= 0) return 1;
+// src: grid * 256 * 64 bytes of operands (A then B, 32 bytes each per
+// thread); sink: grid * 256 floats.  Flops (ops) per MFMA: 2 * 32 * 32 * K
+// with K = 32 (int8), 64 (fp8, fp6, fp4), 16 (bf16, fp16).
+int moeq_peak_mfma(int kind, int grid, int iters, const void* src, void* sink, void* stream) {
+  if (!src || !sink || grid <= 0 || iters <= 0) return 1;
+  const v8i* o = static_cast<const v8i*>(src);
   float* s = static_cast<float*>(sink);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   switch (kind) {
-    case 0: e = go<0>(grid, iters, s, st); break;
-    case 1: e = go<1>(grid, iters, s, st); break;
-    case 2: e = go<2>(grid, iters, s, st); break;
-    case 3: e = go<3>(grid, iters, s, st); break;
-    case 4: e = go<4>(grid, iters, s, st); break;
-    case 5: e = go<5>(grid, iters, s, st); break;
+    case 0: e = go<0>(grid, iters, o, s, st); break;
+    case 1: e = go<1>(grid, iters, o, s, st); break;
+    case 2: e = go<2>(grid, iters, o, s, st); break;
+    case 3: e = go<3>(grid, iters, o, s, st); break;
+    case 4: e = go<4>(grid, iters, o, s, st); break;
+    case 5: e = go<5>(grid, iters, o, s, st); break;
     default: return 1;
   }
   return e == hipSuccess ? 0 : 4;
