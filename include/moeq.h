@@ -141,6 +141,31 @@ moeq_status moe_route_prep(const int32_t* topk_ids, int64_t T, int32_t topk, int
                            size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_route_prep_noalloc - moe_route_prep for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same tables, with the per-chunk
+ * counts kept in a fixed device array of the library instead of a
+ * caller's workspace.
+ *
+ * Arguments, outputs and checks as moe_route_prep, without the workspace.
+ * The array holds MOEQ_ROUTE_NOALLOC_SCRATCH_BYTES per GPU, so the call
+ * serves T*topk pairs while moe_route_prep_workspace_bytes(T, topk, E) is
+ * at most that (e.g. E = 256: about 10^6 pairs); larger sizes give
+ * MOEQ_EINVAL.  Each GPU holds its own array from the first call made with
+ * that device current (which looks up its address) until the process
+ * ends.  Every call on one GPU uses the same array: calls that overlap in
+ * time on one GPU (different streams, or different host threads) race and
+ * give undefined tables; calls ordered on one stream do not.  The array
+ * needs no clearing (each call writes every count it later reads).  The
+ * call allocates nothing and never synchronizes.
+ * ---------------------------------------------------------------------- */
+#define MOEQ_ROUTE_NOALLOC_SCRATCH_BYTES ((size_t)1 << 20)
+
+moeq_status moe_route_prep_noalloc(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
+                                   int32_t* expert_offsets, int32_t* sorted_pair_ids,
+                                   int32_t* pair_to_sorted, int32_t* n_invalid, void* stream);
+
+/* ------------------------------------------------------------------------
  * grouped_gemm_qint4 - W4A4 INT4 grouped GEMM with the dequantization fused
  * into the epilogue.  [W4A4] problem statement: activations quantized per
  * token, weights per output channel, int32 accumulation,

@@ -34,7 +34,10 @@ _DTYPE_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32, tor
 EXPORTS = ("moeq_last_error", "moeq_abi_version", "moe_route_prep_workspace_bytes",
            "moe_route_prep", "grouped_gemm_qint4", "grouped_gemm_qfp8_block",
            "grouped_gemm_qnvfp4", "moe_scatter_combine", "moe_quantize_int4",
-           "moe_nvfp4_repack", "moe_sum_pairs", "moe_cast_bf16_to_f16")
+           "moe_nvfp4_repack", "moe_sum_pairs", "moe_cast_bf16_to_f16", "moe_route_prep_noalloc")
+
+# Fixed device scratch of moe_route_prep_noalloc per GPU (include/moeq.h).
+ROUTE_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 
 class MoeqError(RuntimeError):
@@ -60,6 +63,7 @@ def lib():
         "moeq_abi_version": (i32, []),
         "moe_route_prep_workspace_bytes": (sz, [i64, i32, i32]),
         "moe_route_prep": (i32, [vp, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "moe_route_prep_noalloc": (i32, [vp, i64, i32, i32, vp, vp, vp, vp, vp]),
         "grouped_gemm_qint4": (i32, [vp, vp, i64, i32, vp, vp, vp, vp, i64, i32, i32, i64, i64,
                                      i32, i32, vp, i32, vp]),
         "grouped_gemm_qfp8_block": (i32, [vp, vp, i64, i32, vp, vp, vp, vp, i64, i32, i32, i64,
@@ -147,6 +151,28 @@ def moe_route_prep(topk_ids, E: int, *, out=None, workspace=None):
     st = lib().moe_route_prep(_ptr(topk_ids), T, k, E, _ptr(offs), _ptr(srt), _ptr(p2s),
                               _ptr(ninv), _ptr(workspace), wsb, _stream())
     _check("moe_route_prep", st)
+    return offs, srt, p2s, ninv
+
+
+def moe_route_prep_noalloc(topk_ids, E: int, *, out):
+    """moe_route_prep without a workspace: the library keeps the per-chunk
+    counts in its fixed per-GPU device array (ROUTE_NOALLOC_SCRATCH_BYTES),
+    so the call allocates nothing.  `out` supplies the four int32 output
+    tensors (expert_offsets [E+1], sorted_pair_ids [P], pair_to_sorted [P],
+    n_invalid [1]).  Calls that overlap in time on one GPU race."""
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    T, k = topk_ids.shape
+    P = T * k
+    offs, srt, p2s, ninv = out
+    for t, n, sz in ((offs, "expert_offsets", E + 1), (srt, "sorted_pair_ids", P),
+                     (p2s, "pair_to_sorted", P), (ninv, "n_invalid", 1)):
+        _need(t, n, torch.int32)
+        if t.numel() < sz:
+            raise ValueError(f"{n} needs {sz} elements")
+    _gpu(topk_ids=topk_ids, expert_offsets=offs, sorted_pair_ids=srt, pair_to_sorted=p2s, n_invalid=ninv)
+    st = lib().moe_route_prep_noalloc(_ptr(topk_ids), T, k, E, _ptr(offs), _ptr(srt), _ptr(p2s), _ptr(ninv),
+                                      _stream())
+    _check("moe_route_prep_noalloc", st)
     return offs, srt, p2s, ninv
 
 

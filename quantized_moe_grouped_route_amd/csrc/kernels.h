@@ -12,6 +12,11 @@ namespace moeq {
 size_t route_workspace_bytes(int64_t P, int E);
 hipError_t launch_route(const int* ids, int P, int E, int* offsets, int* sorted_ids,
                         int* pair_to_sorted, int* n_invalid, void* ws, hipStream_t stream);
+// Route prep with its per-chunk counts in the library's fixed device array
+// (kRouteNoallocScratchBytes per device) instead of a caller's workspace.
+constexpr size_t kRouteNoallocScratchBytes = size_t(1) << 20;
+hipError_t launch_route_noalloc(const int* ids, int P, int E, int* offsets, int* sorted_ids,
+                                int* pair_to_sorted, int* n_invalid, hipStream_t stream);
 
 // Combine.  y_kind / out_kind are OutKind values.  tw == null: y holds
 // pre-weighted rows in pair order (row t*topk + j), summed unweighted.

@@ -138,6 +138,30 @@ moeq_status moe_route_prep(const int32_t* topk_ids, int64_t T, int32_t topk, int
                     fn);
 }
 
+moeq_status moe_route_prep_noalloc(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
+                                   int32_t* expert_offsets, int32_t* sorted_pair_ids,
+                                   int32_t* pair_to_sorted, int32_t* n_invalid, void* stream) {
+  const char* fn = "moe_route_prep_noalloc";
+  static_assert(moeq::kRouteNoallocScratchBytes == MOEQ_ROUTE_NOALLOC_SCRATCH_BYTES, "header and library agree");
+  if (T < 0) return fail(MOEQ_EINVAL, "%s: T=%lld < 0", fn, (long long)T);
+  if (topk < 1 || topk > kMaxTopk) return fail(MOEQ_EINVAL, "%s: topk=%d outside [1, %d]", fn, topk, kMaxTopk);
+  if (E < 1 || E > kMaxE) return fail(MOEQ_EINVAL, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  const int64_t P = T * (int64_t)topk;
+  if (P >= (int64_t(1) << 31)) return fail(MOEQ_EINVAL, "%s: T*topk too large", fn);
+  if (!expert_offsets || !n_invalid || (P > 0 && (!topk_ids || !sorted_pair_ids || !pair_to_sorted)))
+    return fail(MOEQ_EINVAL, "%s: null pointer", fn);
+  if (!aligned(topk_ids, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_pair_ids, 4) ||
+      !aligned(pair_to_sorted, 4) || !aligned(n_invalid, 4))
+    return fail(MOEQ_EALIGN, "%s: int32 arrays must be 4-byte aligned", fn);
+  const size_t need = moeq::route_workspace_bytes(P, E);
+  if (need > moeq::kRouteNoallocScratchBytes)
+    return fail(MOEQ_EINVAL, "%s: T*topk=%lld with E=%d needs %zu bytes of scratch, above the fixed %zu", fn,
+                (long long)P, E, need, moeq::kRouteNoallocScratchBytes);
+  return hip_status(moeq::launch_route_noalloc(topk_ids, (int)P, E, expert_offsets, sorted_pair_ids,
+                                               pair_to_sorted, n_invalid, (hipStream_t)stream),
+                    fn);
+}
+
 moeq_status grouped_gemm_qint4(const uint8_t* a, const float* a_scale, int64_t rows_a,
                                moeq_arow a_row, const uint8_t* w, const float* w_scale,
                                const int32_t* expert_offsets, const int32_t* sorted_pair_ids,

@@ -16,10 +16,21 @@
 //   * otherwise:   route_count writes per-chunk counts to the workspace and
 //                  route_scatter (one workgroup per chunk) derives every
 //                  prefix it needs from them.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace moeq {
+
+// Device memory of moe_route_prep_noalloc: the per-chunk counts that
+// route_count writes and route_scatter reads, in a fixed array instead of a
+// caller's workspace.  Every GPU the library runs on holds its own copy
+// until the process ends.  Host code must not pass `scratch` itself to a
+// kernel (in host code it names a host-side stand-in); it uses the device
+// address that static_scratch() looks up once per device.
+static __device__ __align__(256) unsigned char scratch[kRouteNoallocScratchBytes];
+
 namespace {
 
 constexpr int kChunk = 1024;
@@ -223,6 +234,36 @@ size_t route_workspace_bytes(int64_t P, int E) {
 // dynamic LDS of route_scatter with nw waves
 static size_t route_lds_bytes(int E, int nw) {
   return sizeof(int) * (size_t)(2 * (E + 1) + E + 2 * nw + 1) + (size_t)nw * E;
+}
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept per device.
+static hipError_t static_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_route_noalloc(const int* ids, int P, int E, int* offsets, int* sorted_ids,
+                                int* pair_to_sorted, int* n_invalid, hipStream_t stream) {
+  if (route_workspace_bytes(P, E) > kRouteNoallocScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  hipError_t e = static_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_route(ids, P, E, offsets, sorted_ids, pair_to_sorted, n_invalid, ws, stream);
 }
 
 hipError_t launch_route(const int* ids, int P, int E, int* offsets, int* sorted_ids,

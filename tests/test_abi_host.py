@@ -275,3 +275,15 @@ def test_cast_rejects(L, kw, status):
     a = dict(x=A16, n=64, y=0x20000)
     a.update(kw)
     assert L.moe_cast_bf16_to_f16(a["x"], a["n"], a["y"], None) == status
+
+
+def test_noalloc_route_rejects_before_any_device_call(L):
+    # argument checks and the fixed-array limit come before the device
+    # address lookup, so they run without a GPU
+    f = L.moe_route_prep_noalloc
+    assert f(A16, -1, 2, 4, A16, A16, A16, A16, None) == mq.EINVAL
+    assert f(A16, 4, 0, 4, A16, A16, A16, A16, None) == mq.EINVAL
+    assert f(A16, 4, 2, 4, A16, ODD, A16, A16, None) == mq.EALIGN
+    chunks = mq.ROUTE_NOALLOC_SCRATCH_BYTES // ((256 + 1) * 4)
+    assert f(A16, chunks * 1024 + 1, 1, 256, A16, A16, A16, A16, None) == mq.EINVAL
+    assert b"fixed" in L.moeq_last_error()
