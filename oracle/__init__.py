@@ -37,7 +37,6 @@ from .gemm import (grouped_gemm_qint4, grouped_gemm_qfp8_block, grouped_gemm_qnv
 from .combine import scatter_combine, pair_rows, sum_pairs
 from .layer import int4_layer, int4_ffn_layer, nvfp4_layer, fp8_dense, token_rows, combine_tokens
 from .quant import quantize_int4_rows
-from .int4_e3m2 import e3m2_value, e3m2_code_of_int, int4_to_e3m2_rows, e3m2_rows_values
 from .layouts import (scale_swizzle_offset, unswizzle_scales, swizzle_scales, repack_nvfp4,
                       quads_from_rows, rows_from_quads, tiles_from_rows, rows_from_tiles)
 

@@ -81,7 +81,7 @@ def silu_mul(y: np.ndarray, limit=None) -> np.ndarray:
 
 
 def grouped_gemm_qint4(a, a_scale, a_row, w, w_scale, offsets, sorted_pair_ids, topk,
-                       act="none", rows=None, cols=None, layout="packed"):
+                       act="none", rows=None, cols=None):
     """W4A4 INT4 grouped GEMM with the per-token x per-channel epilogue.
 
     CUTLASS discussion #2855 (problem statement): activations quantized per
@@ -91,24 +91,15 @@ def grouped_gemm_qint4(a, a_scale, a_row, w, w_scale, offsets, sorted_pair_ids, 
       y[s, n]   = a_scale[r] * w_scale[e, n] * acc[s, n]
     a [rows_a][K/2] bytes, a_scale [rows_a] f32, w [E][N][K/2] bytes,
     w_scale [E][N] f32.  act 'silu_mul' returns silu_mul(y).
-    layout 'e3m2': a [rows_a][3K/4] and w [E][N][3K/4] hold the same int4
-    values as FP6 E3M2 codes (oracle.int4_e3m2).
     Returns dict(acc=int64 [n][N], y=float64 [n][N or N/2]) (with cols:
     acc over the selected weight rows, see weight_rows)."""
     s, e, r = gemm_rows(offsets, sorted_pair_ids, topk, a_row, rows)
     wr = weight_rows(w.shape[1], act, cols)
-    if layout == "packed":
-        values = lambda x: int4_value(unpack_nibbles(x)).astype(np.float64)
-    elif layout == "e3m2":
-        from .int4_e3m2 import e3m2_rows_values
-        values = e3m2_rows_values
-    else:
-        raise ValueError(layout)
-    A = values(np.asarray(a)[r])
+    A = int4_value(unpack_nibbles(np.asarray(a)[r])).astype(np.float64)
     acc = np.zeros((s.size, wr.size), np.float64)
     for ex in np.unique(e):
         m = e == ex
-        W = values(np.asarray(w)[ex][wr])
+        W = int4_value(unpack_nibbles(np.asarray(w)[ex][wr])).astype(np.float64)
         acc[m] = A[m] @ W.T
     assert np.all(np.abs(acc) < 2.0 ** 31), "int32 accumulator would overflow"
     sa = np.asarray(a_scale, np.float64)[r]
