@@ -691,11 +691,17 @@ def summarize_profiles(idx: int, pdir: str, steps: int = 50, warmup: int = 10):
              f"mfma_busy_fraction_at_{NOMINAL_GHZ}ghz: {busy / (trace_s * NOMINAL_GHZ * 1e9):.3f} "
              f"(busy cycles per SIMD / (kernel-trace duration x nominal clock))",
              "GRBM_GUI_ACTIVE counts the whole counter window; the next two figures hold only where the "
-             "launch is much longer than the counter run's dispatch overhead:",
-             f"shader_clock_ghz: {gui / dur_s / 1e9:.3f} (GRBM_GUI_ACTIVE / XCDs / counter-run duration)",
-             f"mfma_busy_fraction_of_active_cycles: {busy / gui:.3f} "
-             f"(SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / GRBM_GUI_ACTIVE per XCD)",
-             f"wave_time_waiting_fraction: {avg('SQ_WAIT_INST_ANY') / avg('SQ_WAVE_CYCLES'):.3f} "
+             "launch is much longer than the counter run's dispatch overhead:"]
+    if dur_s > 1.1 * trace_s or gui / dur_s / 1e9 > NOMINAL_GHZ:
+        # the counter window of a short launch takes in the dispatch around it
+        why = (f"invalid for this launch (counter-run duration {dur_s * 1e6:.1f} us against "
+               f"{trace_s * 1e6:.1f} us traced)")
+        ctxt += [f"shader_clock_ghz: {why}", f"mfma_busy_fraction_of_active_cycles: {why}"]
+    else:
+        ctxt += [f"shader_clock_ghz: {gui / dur_s / 1e9:.3f} (GRBM_GUI_ACTIVE / XCDs / counter-run duration)",
+                 f"mfma_busy_fraction_of_active_cycles: {busy / gui:.3f} "
+                 f"(SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / GRBM_GUI_ACTIVE per XCD)"]
+    ctxt += [f"wave_time_waiting_fraction: {avg('SQ_WAIT_INST_ANY') / avg('SQ_WAVE_CYCLES'):.3f} "
              f"(SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)",
              f"wave_time_valu_fraction: {avg('SQ_ACTIVE_INST_VALU') / avg('SQ_WAVE_CYCLES'):.3f}",
              f"wave_time_lds_fraction: {avg('SQ_ACTIVE_INST_LDS') / avg('SQ_WAVE_CYCLES'):.3f}",

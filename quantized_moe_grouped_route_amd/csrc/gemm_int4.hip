@@ -343,6 +343,11 @@ __global__ __launch_bounds__(kThreads4, 1) void int4_prefill(
     const Tile4 t = tile_of(tile_start, offsets, E, P, n_tiles, ep_item);
     epilogue<OUT, SILU>(t, reinterpret_cast<const float*>(sbuf + ep_sbuf * kScaleBytes4), wm, wn, lane, N, acc,
                         out);
+    // Let the tile's stores (and the copies in flight) complete before the
+    // next stage: measured 1-3 % faster on the SiLU GEMM of the Mixtral
+    // layer, no change on the other.  A wait for more than the stage needs
+    // only makes the later stage waits conservative.
+    wait_vmcnt<0>();
 #pragma unroll
     for (int wo = 0; wo < 2; ++wo)
 #pragma unroll
