@@ -692,7 +692,7 @@ def summarize_profiles(idx: int, pdir: str, steps: int = 50, warmup: int = 10):
              f"(busy cycles per SIMD / (kernel-trace duration x nominal clock))",
              "GRBM_GUI_ACTIVE counts the whole counter window; the next two figures hold only where the "
              "launch is much longer than the counter run's dispatch overhead:"]
-    if dur_s > 1.1 * trace_s or gui / dur_s / 1e9 > NOMINAL_GHZ:
+    if gui / dur_s / 1e9 > NOMINAL_GHZ or (trace_s < 200e-6 and dur_s > 1.1 * trace_s):
         # the counter window of a short launch takes in the dispatch around it
         why = (f"invalid for this launch (counter-run duration {dur_s * 1e6:.1f} us against "
                f"{trace_s * 1e6:.1f} us traced)")
