@@ -216,6 +216,10 @@ class Workload:
             self.weight_bytes = None
             self.dtype = "int4_via_int8_mfma"
             self.dom = ("int4_prefill", ["gemm_int4.hip", "common.h", "tile.h"], "mfma", PEAK["int8"])
+            if self.int4_streaming():  # weight GB/s against HBM
+                self.active, self.fc1_bytes, self.weight_bytes = self.int4_stream_bytes()
+                self.dom = ("int4_decode", ["gemm_int4.hip", "common.h", "tile.h", "pipeline.h"], "hbm",
+                            PEAK["hbm_GBps"])
         elif kind == "fp8":
             self.a, self.sa = _dev(d["a"]), _dev(d["a_scale"])
             self.w, self.sw = _dev(d["w"]), _dev(d["w_scale"])
@@ -375,6 +379,21 @@ class Workload:
         """(launches of the dominant kernel per step, index of the timed one)."""
         return (1, 0) if self.cfg["kind"] in ("fp8", "quant", "repack") or self.idx == 0 else (2, 0)
 
+    def int4_streaming(self):
+        """The W4A4 layer at decode size: few rows per expert, so the INT4
+        GEMMs take the weight-streaming schedule."""
+        return self.cfg["kind"] == "int4chain" and self.T * self.k < 16 * self.E
+
+    def int4_stream_bytes(self):
+        """(active experts, FC1 weight + scale bytes, FC1 + FC2 bytes) of the
+        experts the step routes to."""
+        d = self.d
+        H, I, E = d["H"], d["I"], self.E
+        ids = d["topk_ids"].reshape(-1)
+        active = int(np.unique(ids[(ids >= 0) & (ids < E)]).size)
+        fc1 = float(active * 2 * I * (H // 2 + 4))
+        return active, fc1, fc1 + float(active * H * (I // 2 + 4))
+
     def dominant_bytes(self):
         """Fewest HBM bytes one launch of the dominant kernel can move: every
         operand read once, every output written once."""
@@ -385,6 +404,8 @@ class Workload:
         if kind == "fp8":
             N, K = d["N"], d["K"]
             return float(P * K + self.weight_bytes + d["a_scale"].size * 4 + P * N * 2)
+        if self.int4_streaming():
+            return float(self.int4_stream_bytes()[1] + P * (d["H"] // 2 + 4) + P * d["I"] * 2)
         if kind in ("int4", "int4chain"):
             N, K = d["N"], d["K"]
             out = N * 2 if self.idx == 0 else N  # f16 y, or f16 h = N/2 columns
@@ -403,6 +424,8 @@ class Workload:
             return self.weight_bytes, "byte"
         if kind == "fp8":
             return 2.0 * self.T * self.k * d["N"] * d["K"], "flop"
+        if self.int4_streaming():
+            return self.int4_stream_bytes()[1], "byte"
         if kind in ("int4", "int4chain"):
             return 2.0 * self.T * self.k * d["N"] * d["K"], "flop"
         if self.idx == 2:
@@ -427,7 +450,7 @@ def cpu_baseline(idx: int, d, budget_s: float = 10.0):
     except Exception:
         cores = os.cpu_count()
     kind = {0: "int4", 1: "fp8", 2: "nvfp4", 3: "nvfp4", 4: "int4", 5: "quant", 6: "fp8",
-            7: "repack", 8: "int4"}[idx]
+            7: "repack", 8: "int4", 9: "int4"}[idx]
     times = []
     if kind == "repack":
         ne = 64
@@ -473,6 +496,20 @@ def cpu_baseline(idx: int, d, budget_s: float = 10.0):
             times.append(time.perf_counter() - t)
         return dict(value=work / float(np.median(times)) / 1e12, unit="TFLOP/s", cores=cores,
                     kind="oracle", sample=sample + f", median of {len(times)} runs")
+    if kind == "int4" and idx == 9:
+        # the FC1 rows of 2 active experts, on the oracle's own codes of x;
+        # weight GB/s over those experts' bytes
+        a, sa = oracle.quantize_int4_rows(d["x"])
+        experts = [e for e in range(d["E"]) if off[e + 1] > off[e]][:2]
+        rows = np.concatenate([np.arange(off[e], off[e + 1]) for e in experts])
+        nbytes = len(experts) * d["N"] * (d["K"] // 2 + 4)
+        while sum(times) < budget_s and len(times) < 3:
+            t = time.perf_counter()
+            oracle.grouped_gemm_qint4(a, sa, "token", d["w"], d["w_scale"], off, srt, d["k"], act="silu_mul",
+                                      rows=rows)
+            times.append(time.perf_counter() - t)
+        return dict(value=nbytes / float(np.median(times)) / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                    sample=f"{rows.size} rows of {len(experts)} active experts of FC1, median of {len(times)} runs")
     if kind == "int4":
         rows = np.arange(n) if idx == 0 else np.arange(0, n, max(1, n // 64))
         sample = "the whole workload" if idx == 0 else f"{rows.size} sorted rows of FC1 (gate+up, K={d['K']})"
@@ -560,13 +597,14 @@ def summarize_profiles(idx: int, pdir: str, steps: int = 50, warmup: int = 10):
         wl.d = synth.workload(idx)
         wl.T, wl.k, wl.E = wl.d["T"], wl.d["k"], wl.d["E"]
     d = wl.d
-    tag = ("fp8_decode" if idx == 6 else None) or \
+    tag = ("fp8_decode" if idx == 6 else None) or ("int4_decode" if idx == 9 else None) or \
         {"fp8": "fp8_prefill", "int4": "int4_prefill", "int4chain": "int4_prefill", "quant": "quant_int4_rows_reg",
          "repack": "repack_nvfp4"}.get(cfg["kind"]) or \
         ("nvfp4_decode" if idx == 2 else "nvfp4_prefill")
     srcs = {"fp8_prefill": ["gemm_fp8.hip", "common.h", "tile.h", "pipeline.h"],
             "fp8_decode": ["gemm_fp8.hip", "common.h", "tile.h", "pipeline.h"],
             "int4_prefill": ["gemm_int4.hip", "common.h", "tile.h"],
+            "int4_decode": ["gemm_int4.hip", "common.h", "tile.h", "pipeline.h"],
             "quant_int4_rows_reg": ["quant.hip", "common.h"],
             "repack_nvfp4": ["repack.hip", "kernels.h", "common.h"]}.get(
         tag, ["gemm_nvfp4.hip", "nvfp4.h", "common.h", "tile.h", "pipeline.h"])
@@ -813,7 +851,7 @@ def main():
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     cfg = wl.cfg
-    if args.workload in (2, 5, 6, 7):
+    if args.workload in (2, 5, 6, 7, 9):
         value, unit = wl.weight_bytes / (ms * 1e-3) / 1e9, "GB/s"
     else:
         value, unit = wl.flops / (ms * 1e-3) / 1e12, "TFLOP/s"
@@ -839,7 +877,7 @@ def main():
         config["activations"] = args.act
         config["scale_layout"] = args.sf_layout
         config["code_layout"] = args.w_layout
-    if args.workload in (2, 6):
+    if args.workload in (2, 6, 9):
         config["active_experts"] = wl.active
         config["weight_bytes"] = wl.weight_bytes
     rec = {"metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,

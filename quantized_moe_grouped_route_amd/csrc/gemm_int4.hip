@@ -397,6 +397,212 @@ __global__ __launch_bounds__(kThreads4, 1) void int4_prefill(
   }
 }
 
+// ------------------------------------------------------------------ decode
+// Few routed rows per expert (decode): the weight stream is the whole cost,
+// so the wave is the unit of work and every operand arrives through a
+// per-wave direct-to-LDS ring, as in the FP8 and NVFP4 streaming schedules.
+// The arithmetic is the tiled schedule's: nibble planes scaled by 16, int8
+// MFMA, acc >> 8, and the same fp32 epilogue expression, so both schedules
+// give identical outputs.
+//
+// Item = (at most 4 routed rows of one expert) x (32 weight rows): with
+// SILU_MUL the 16 gate rows and the 16 up rows of 16 output columns, else
+// 32 consecutive rows.  Per K group of 256 values (128 packed bytes of a
+// row, one cache line) a ring slot holds the 32 weight rows as four whole-
+// line copies of 8 rows (16-byte piece p of row r at position
+// p ^ ((r >> 1) & 7)) and the item's activation rows (one copy; lanes
+// 32..63 repeat rows 0..3).  The item's scales ride in group 0's slot: one
+// 4-byte-per-lane copy, lanes 0..3 the rows' activation scales and lanes
+// 4..35 the 32 weight scales, read into registers at group 0.
+//
+// v_mfma_i32_16x16x64_i8 takes the weights as the 16-row operand and the
+// routed rows as the 16 columns (columns past the item's rows are
+// discarded).  Lane l supplies row l % 16 and 16 bytes of its K quarter
+// l / 16: it reads pieces 2q and 2q + 1 of its weight row and of its routed
+// row, and each piece gives a low- and a high-nibble plane, so a group is 4
+// MFMAs per 16-row block.  Value i of lane l is weight row 4(l/16) + i of
+// the block and routed row l % 16.
+namespace dd {
+constexpr int kM = 4;                                  // routed rows per item
+constexpr int kRowsW = 32;                             // weight rows per item
+constexpr int kWaves = 4;                              // waves per workgroup, independent
+constexpr int kDepth = 3;                              // K groups in flight per wave
+constexpr int kW = 0, kX = 4096, kS = 5120;            // slot regions
+constexpr int kSlot = 5376;
+constexpr int kCopies = 5;                             // per K group: 4 weight, 1 activation
+constexpr int kGroupK = 256;
+}  // namespace dd
+
+// vmcnt(n * dd::kCopies) for n in [0, kDepth - 1]
+__device__ __forceinline__ void wait_groups4(int n) {
+  static_assert(dd::kDepth == 3, "wait table");
+  if (n <= 0) wait_vmcnt<0>();
+  else if (n == 1) wait_vmcnt<dd::kCopies>();
+  else wait_vmcnt<2 * dd::kCopies>();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ v4i mfma_i8_16x16x64(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+template <int OUT, bool SILU>
+__global__ __launch_bounds__(64 * dd::kWaves) void int4_decode(
+    const uint8_t* __restrict__ a, const float* __restrict__ a_scale, int64_t rows_a, int a_sorted,
+    const uint8_t* __restrict__ w, const float* __restrict__ w_scale,
+    const int* __restrict__ offsets, const int* __restrict__ sorted_ids, int topk, int E, int P, int N,
+    int K, void* __restrict__ out) {
+  __shared__ int tile_start[kMaxExperts + 1];
+  __shared__ int sched_scratch[2 * kMaxWaves];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[dd::kWaves][dd::kDepth][dd::kSlot];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_blocks = N / dd::kRowsW;
+  sched_build(tile_start, sched_scratch, offsets, E, P, dd::kM, n_blocks);
+  const int total = __builtin_amdgcn_readfirstlane(tile_start[E]);
+  // Items go to the fewest waves that still need the same number of rounds.
+  const int waves = gridDim.x * dd::kWaves;
+  const int rounds = (total + waves - 1) / waves;
+  const int active = rounds ? (total + rounds - 1) / rounds : 0;
+  const int wid = blockIdx.x * dd::kWaves + wv;
+  if (wid >= active) return;
+  const int G = K / dd::kGroupK;
+  const int64_t rowb = K / 2;
+  const int I = N / 2;
+  uint8_t* myring = &ring[wv][0][0];
+  const uint32_t lb = lds_addr(myring);
+  const int l16 = lane & 15, quarter = lane >> 4;
+  // weight copy c (0..3): block c / 2, block row 8 (c % 2) + lane / 8, piece
+  // fetched (lane % 8) ^ ((row >> 1) & 7) so that LDS position lane % 8
+  // holds it
+  const int crow = lane >> 3;  // + 8 (c % 2)
+  const int cp0 = ((lane & 7) ^ ((crow >> 1) & 7)) << 4;
+  const int cp1 = ((lane & 7) ^(((crow + 8) >> 1) & 7)) << 4;
+  // fragment reads: block row l16, pieces 2 quarter and 2 quarter + 1
+  const int wkey = (l16 >> 1) & 7;
+  const int wf0 = dd::kW + l16 * 128 + (((2 * quarter) ^ wkey) << 4);
+  const int wf1 = dd::kW + l16 * 128 + (((2 * quarter + 1) ^ wkey) << 4);
+  const int xslot = l16 < dd::kM ? l16 : 0;
+  const int xf0 = dd::kX + xslot * 128 + ((2 * quarter) << 4);
+  const int xf1 = xf0 + 16;
+
+  for (int item = wid; item < total; item += active) {
+    // Tile of the item, every field wave-uniform (m-tile major, then blocks).
+    int bl = 0, bh = E - 1;
+    while (bl < bh) {
+      const int mid = (bl + bh + 1) >> 1;
+      if (__builtin_amdgcn_readfirstlane(tile_start[mid]) <= item) bl = mid; else bh = mid - 1;
+    }
+    const int e = __builtin_amdgcn_readfirstlane(bl);
+    const int local = item - __builtin_amdgcn_readfirstlane(tile_start[e]);
+    const int lo = min(max(ld_uniform_i32(offsets, e), 0), P);
+    const int hi = min(max(ld_uniform_i32(offsets, e + 1), lo), P);
+    const int mt = local / n_blocks;
+    const int nb = local - mt * n_blocks;
+    const int row0 = lo + mt * dd::kM;
+    const int rows = min(dd::kM, hi - row0);
+    int arow[dd::kM];
+#pragma unroll
+    for (int j = 0; j < dd::kM; ++j) {
+      const int sp = row0 + min(j, rows - 1);
+      const int r = (a_sorted || sorted_ids == nullptr) ? sp : ld_uniform_i32(sorted_ids, sp) / topk;
+      arow[j] = (r < 0 || r >= rows_a) ? 0 : r;
+    }
+    // expert-local weight row of item row rb (block rb / 16)
+    auto wrow = [&](int rb) __attribute__((always_inline)) {
+      if (SILU) return (rb < 16 ? 0 : I) + nb * 16 + (rb & 15);
+      return nb * dd::kRowsW + rb;
+    };
+    const uint8_t* wbase = w + (int64_t)e * N * rowb;
+    const uint8_t* sw[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      sw[c] = wbase + (int64_t)wrow(16 * (c >> 1) + 8 * (c & 1) + crow) * rowb + ((c & 1) ? cp1 : cp0);
+    const int xr = (lane >> 3) & 3;
+    const int xrow = xr == 0 ? arow[0] : xr == 1 ? arow[1] : xr == 2 ? arow[2] : arow[3];
+    const uint8_t* sx = a + (int64_t)xrow * rowb + ((lane & 7) << 4);
+    const float* ss;
+    if (lane < dd::kM) ss = a_scale + (lane == 0 ? arow[0] : lane == 1 ? arow[1] : lane == 2 ? arow[2] : arow[3]);
+    else if (lane < dd::kM + dd::kRowsW) ss = w_scale + (int64_t)e * N + wrow(lane - dd::kM);
+    else ss = a_scale + arow[0];
+    auto issue = [&](int g) __attribute__((always_inline)) {
+      const uint32_t sl = lb + (uint32_t)((g % dd::kDepth) * dd::kSlot);
+      const int64_t ko = (int64_t)g * (dd::kGroupK / 2);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dma16(sw[c] + ko, sl + dd::kW + c * 1024);
+      dma16(sx + ko, sl + dd::kX);
+      if (g == 0) dma4(ss, sl + dd::kS);
+    };
+    const int npre = G < dd::kDepth ? G : dd::kDepth;
+    for (int g = 0; g < npre; ++g) issue(g);
+    v4i acc[2] = {v4i{}, v4i{}};
+    float sa = 0.f;
+    v4f sw0 = v4f{}, sw1 = v4f{};
+    for (int g = 0; g < G; ++g) {
+      const int after = G - 1 - g;
+      wait_groups4(after < dd::kDepth - 1 ? after : dd::kDepth - 1);
+      const uint8_t* sp = myring + (g % dd::kDepth) * dd::kSlot;
+      const u32x4 w00 = ld16(sp + wf0), w01 = ld16(sp + wf1);
+      const u32x4 w10 = ld16(sp + 2048 + wf0), w11 = ld16(sp + 2048 + wf1);
+      const u32x4 x0 = ld16(sp + xf0), x1 = ld16(sp + xf1);
+      if (g == 0) {
+        const float* s = reinterpret_cast<const float*>(sp + dd::kS);
+        sa = s[xslot];
+        sw0 = *reinterpret_cast<const v4f*>(s + dd::kM + 4 * quarter);
+        sw1 = *reinterpret_cast<const v4f*>(s + dd::kM + 16 + 4 * quarter);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot is read; it may be refilled
+      if (g + dd::kDepth < G) issue(g + dd::kDepth);
+      const v4i xl0 = lo_nibbles(x0), xh0 = hi_nibbles(x0), xl1 = lo_nibbles(x1), xh1 = hi_nibbles(x1);
+      acc[0] = mfma_i8_16x16x64(lo_nibbles(w00), xl0, acc[0]);
+      acc[1] = mfma_i8_16x16x64(lo_nibbles(w10), xl0, acc[1]);
+      acc[0] = mfma_i8_16x16x64(hi_nibbles(w00), xh0, acc[0]);
+      acc[1] = mfma_i8_16x16x64(hi_nibbles(w10), xh0, acc[1]);
+      acc[0] = mfma_i8_16x16x64(lo_nibbles(w01), xl1, acc[0]);
+      acc[1] = mfma_i8_16x16x64(lo_nibbles(w11), xl1, acc[1]);
+      acc[0] = mfma_i8_16x16x64(hi_nibbles(w01), xh1, acc[0]);
+      acc[1] = mfma_i8_16x16x64(hi_nibbles(w11), xh1, acc[1]);
+    }
+    if (l16 < rows) {
+      const int64_t orow = row0 + l16;
+      if constexpr (SILU) {
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float gt = sa * sw0[i] * (float)(acc[0][i] >> 8);
+          const float up = sa * sw1[i] * (float)(acc[1][i] >> 8);
+          o[i] = silu(gt) * up;
+        }
+        store4<OUT>(out, orow * I + nb * 16 + 4 * quarter, o);
+      } else {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int64_t idx = orow * N + nb * dd::kRowsW + 16 * b + 4 * quarter;
+          if constexpr (OUT == OUT_I32) {
+            *reinterpret_cast<v4i*>(static_cast<int*>(out) + idx) =
+                v4i{acc[b][0] >> 8, acc[b][1] >> 8, acc[b][2] >> 8, acc[b][3] >> 8};
+          } else {
+            const v4f s = b ? sw1 : sw0;
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = sa * s[i] * (float)(acc[b][i] >> 8);
+            store4<OUT>(out, idx, o);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int OUT, bool SILU>
+hipError_t go_decode(const GroupedArgs& g, const uint8_t* a, const float* a_scale, const uint8_t* w,
+                     const float* w_scale, hipStream_t stream) {
+  hipLaunchKernelGGL((int4_decode<OUT, SILU>), dim3(g.num_cus * 2), dim3(64 * dd::kWaves), 0, stream, a,
+                     a_scale, g.rows_a, g.a_sorted, w, w_scale, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P,
+                     g.N, g.K, g.out);
+  return hipGetLastError();
+}
+
 template <int OUT, bool SILU>
 hipError_t go(const GroupedArgs& g, int grid, const uint8_t* a, const float* a_scale,
               const uint8_t* w, const float* w_scale, hipStream_t stream) {
@@ -410,6 +616,25 @@ hipError_t go(const GroupedArgs& g, int grid, const uint8_t* a, const float* a_s
 
 hipError_t launch_gemm_int4(const GroupedArgs& g, const uint8_t* a, const float* a_scale,
                             const uint8_t* w, const float* w_scale, hipStream_t stream) {
+  // AUTO takes the streaming schedule when experts hold few rows on average
+  // and K fills whole 256-value groups (the host rejects DECODE otherwise).
+  const bool decode = g.sched == 1 || (g.sched == 0 && g.P < (int64_t)16 * g.E && g.K % dd::kGroupK == 0);
+  if (decode) {
+    if (g.P == 0) return hipSuccess;
+    if (g.silu_mul) {
+      switch (g.out_kind) {
+        case OUT_F16: return go_decode<OUT_F16, true>(g, a, a_scale, w, w_scale, stream);
+        case OUT_BF16: return go_decode<OUT_BF16, true>(g, a, a_scale, w, w_scale, stream);
+        default: return go_decode<OUT_F32, true>(g, a, a_scale, w, w_scale, stream);
+      }
+    }
+    switch (g.out_kind) {
+      case OUT_F16: return go_decode<OUT_F16, false>(g, a, a_scale, w, w_scale, stream);
+      case OUT_BF16: return go_decode<OUT_BF16, false>(g, a, a_scale, w, w_scale, stream);
+      case OUT_I32: return go_decode<OUT_I32, false>(g, a, a_scale, w, w_scale, stream);
+      default: return go_decode<OUT_F32, false>(g, a, a_scale, w, w_scale, stream);
+    }
+  }
   // Upper bound on tiles: every expert adds at most one partial m-tile.
   const int64_t mt_ub = (g.P + kBM - 1) / kBM + std::min<int64_t>(g.E, g.P);
   const int64_t n_tiles = g.silu_mul ? (g.N / 2 + 127) / 128 : (g.N + kBN - 1) / kBN;

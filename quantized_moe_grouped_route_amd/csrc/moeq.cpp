@@ -185,6 +185,8 @@ moeq_status grouped_gemm_qint4(const uint8_t* a, const float* a_scale, int64_t r
   if (a_row == MOEQ_AROW_TOKEN && !sorted_pair_ids && rows_a < P)
     return fail(MOEQ_EINVAL, "%s: identity rows need rows_a >= P", fn);
   if (sched < MOEQ_SCHED_AUTO || sched > MOEQ_SCHED_PREFILL) return fail(MOEQ_EINVAL, "%s: sched %d", fn, sched);
+  if (sched == MOEQ_SCHED_DECODE && K % 256 != 0)
+    return fail(MOEQ_EALIGN, "%s: the streaming schedule needs K %% 256 == 0 (K=%lld)", fn, (long long)K);
   moeq::GroupedArgs g = make_args(expert_offsets, sorted_pair_ids, rows_a, a_row, P, topk, E, N, K,
                                   act == MOEQ_ACT_SILU_MUL, out_dtype, out, sched);
   return hip_status(moeq::launch_gemm_int4(g, a, a_scale, w, w_scale, (hipStream_t)stream), fn);

@@ -285,6 +285,9 @@ WORKLOADS = {
     # the complete W4A4 layer at config 4's sizes from fp16 activations:
     # per-token int4 of x, FC1 (SiLU), per-row int4 of h, FC2, combine
     8: dict(name="w4a4_int4_chain_mixtral_T8192", kind="int4chain", T=8192, E=8, k=2, H=4096, I=14336),
+    # the same layer for one 8-token decode step: 16 routed rows over the 8
+    # experts, so the GEMMs stream the weights (HBM-bound)
+    9: dict(name="w4a4_int4_chain_mixtral_decode_T8", kind="int4chain", T=8, E=8, k=2, H=4096, I=14336),
 }
 
 
@@ -312,6 +315,6 @@ def workload(idx: int):
         return fp8_moe(seed, c["T"], c["E"], c["k"], c["N"], c["K"])
     if idx == 7:
         return nvfp4_stored_weights(seed, c["E"], c["N"], c["K"])
-    if idx == 8:
+    if idx in (8, 9):
         return int4_chain(seed, c["T"], c["E"], c["k"], c["H"], c["I"])
     raise KeyError(idx)

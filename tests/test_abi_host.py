@@ -89,6 +89,8 @@ def _int4(L, **kw):
     # K = 2^17 with every code -8 would sum 2^17 products of 2^14 to 2^31 in
     # the int32 accumulator; the largest accepted K is 2^17 - 128
     (dict(K=1 << 17), mq.EINVAL),
+    # the streaming schedule reads whole 256-value K groups
+    (dict(K=384, sched=1), mq.EALIGN),
 ])
 def test_int4_rejects(L, kw, status):
     assert _int4(L, **kw) == status

@@ -168,6 +168,108 @@ def test_int4_extreme_codes():
     assert torch.all(acc == 64 * K)
 
 
+# INT4 weight-streaming schedule (few rows per expert).  AUTO takes it for
+# P < 16 E with K % 256 == 0; its arithmetic is the tiled schedule's, so the
+# two schedules must give identical outputs as well as meet the oracle.
+INT4_DECODE_CASES = [
+    (8, 8, 2, 256, 512),      # Mixtral-like decode routing, tiny shapes
+    (5, 16, 4, 96, 256),      # N not a multiple of 64, one K group
+    (33, 4, 1, 160, 768),     # several 4-row tiles per expert, ragged last tile
+    (1, 3, 1, 32, 256),       # one row, one 32-row weight block
+    (60, 8, 2, 4096, 4096),   # more items than waves: two rounds per wave
+]
+
+
+@pytest.mark.parametrize("sched", ["decode", "auto"])
+@pytest.mark.parametrize("T,E,k,N,K", INT4_DECODE_CASES)
+def test_int4_decode_raw_accumulator_bit_exact(sched, T, E, k, N, K):
+    d, offs, srt, p2s = _int4_case(31, T, E, k, N, K, routing="repeat")
+    assert T * k < 16 * E  # AUTO must pick the streaming schedule here
+    acc = mq.grouped_gemm_qint4(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]),
+                                offs, srt, k, out_dtype=torch.int32, sched=sched)
+    ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"],
+                                    host(offs), host(srt), k)
+    n = int(host(offs)[-1])
+    assert np.array_equal(host(acc)[:n], ref["acc"])
+
+
+@pytest.mark.parametrize("act", ["none", "silu_mul"])
+@pytest.mark.parametrize("T,E,k,N,K", [INT4_DECODE_CASES[0], INT4_DECODE_CASES[2], INT4_DECODE_CASES[4]])
+def test_int4_decode_scaled_matches_oracle_and_tiled_schedule(act, T, E, k, N, K):
+    d, offs, srt, p2s = _int4_case(32, T, E, k, N, K)
+    args = (dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]), offs, srt, k)
+    ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"],
+                                    host(offs), host(srt), k, act=act)
+    n = ref["y"].shape[0]
+    y32 = mq.grouped_gemm_qint4(*args, act=act, out_dtype=torch.float32, sched="decode")
+    assert_rows_close(host(y32)[:n], ref["y"], what=f"int4 decode {act}")
+    for odt in (torch.float32, torch.float16, torch.bfloat16):
+        y_dec = mq.grouped_gemm_qint4(*args, act=act, out_dtype=odt, sched="decode")
+        y_til = mq.grouped_gemm_qint4(*args, act=act, out_dtype=odt, sched="prefill")
+        assert torch.equal(y_dec[:n], y_til[:n]), odt
+        if odt == torch.float16:
+            # the last multiply may be fused with the conversion (one rounding
+            # of the exact product straight to binary16), so a binary16 output
+            # is the f32 output rounded, or its neighbour where rounding twice
+            # would differ: within one binary16 ulp
+            h = host(y_dec)[:n].astype(np.float32)
+            f = host(y32)[:n]
+            assert np.all(np.abs(h - f) <= np.spacing(np.abs(h).astype(np.float16)).astype(np.float32)), odt
+            assert np.mean(h == f.astype(np.float16).astype(np.float32)) > 0.999
+        else:
+            assert torch.equal(y_dec[:n], y32[:n].to(odt)), odt
+
+
+def test_int4_decode_sorted_rows_invalid_ids_and_untouched_rows():
+    T, E, k, N, K = 40, 12, 2, 320, 1024
+    d = synth.int4_moe(33, T, E, k, N, K, routing="repeat")
+    ids = d["topk_ids"].copy()
+    ids[ids >= 9] = -1                               # experts 9..11 empty, some pairs skipped
+    ids[::7, 0] = 99                                 # out-of-range ids are skipped too
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(ids), E)
+    n = int(host(offs)[-1])
+    # TOKEN rows, I32, rows past the routed ones untouched
+    out = torch.full((T * k, N), 12345, dtype=torch.int32, device="cuda")
+    mq.grouped_gemm_qint4(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]),
+                          offs, srt, k, out_dtype=torch.int32, out=out, sched="decode")
+    assert torch.all(out[n:] == 12345)
+    ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"],
+                                    host(offs), host(srt), k)
+    assert np.array_equal(host(out)[:n], ref["acc"])
+    # SORTED rows with SiLU: A holds one row per routed pair
+    rng = np.random.default_rng(34)
+    a2 = synth.uniform_bytes(rng, (T * k, K // 2))
+    s2 = synth.uniform_f32(rng, (T * k,), 0.005, 0.05)
+    h = torch.full((T * k, N // 2), -7.0, dtype=torch.float32, device="cuda")
+    mq.grouped_gemm_qint4(dev(a2), dev(s2), dev(d["w"]), dev(d["w_scale"]), offs, srt, k, a_row="sorted",
+                          act="silu_mul", out_dtype=torch.float32, out=h, sched="decode")
+    ref2 = oracle.grouped_gemm_qint4(a2, s2, "sorted", d["w"], d["w_scale"], host(offs), host(srt), k,
+                                     act="silu_mul")
+    assert_rows_close(host(h)[:n], ref2["y"], what="int4 decode sorted silu")
+    assert torch.all(h[n:] == -7.0)
+
+
+def test_int4_decode_extreme_codes_and_no_rows():
+    # all codes -8 at the largest K the streaming schedule is given here
+    T, E, N, K = 6, 2, 64, 8192
+    ids = np.zeros((T, 1), np.int32)
+    ids[::2] = 1
+    a = np.full((T, K // 2), 0x88, np.uint8)
+    w = np.full((E, N, K // 2), 0x88, np.uint8)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(ids), E)
+    acc = mq.grouped_gemm_qint4(dev(a), dev(np.ones(T, np.float32)), dev(w),
+                                dev(np.ones((E, N), np.float32)), offs, srt, 1,
+                                out_dtype=torch.int32, sched="decode")
+    assert torch.all(acc == 64 * K)
+    # every id -1: no routed rows, the output is left as it was
+    ids = -np.ones((T, 1), np.int32)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(ids), E)
+    out = torch.full((T, N), 77, dtype=torch.int32, device="cuda")
+    mq.grouped_gemm_qint4(dev(a), dev(np.ones(T, np.float32)), dev(w), dev(np.ones((E, N), np.float32)),
+                          offs, srt, 1, out_dtype=torch.int32, out=out, sched="decode")
+    assert torch.all(out == 77)
+
+
 # ------------------------------------------------------------------ FP8
 @pytest.mark.parametrize("M,N,K", [(300, 256, 512), (128, 128, 128), (1, 384, 256)])
 def test_fp8_dense(M, N, K):

@@ -301,3 +301,26 @@ def test_workload8_w4a4_chain_end_to_end_token_sample():
     tok = _token_sample(off, srt, wl.k, wl.T, 3, 83)
     ref = oracle.int4_ffn_layer(wl.d, tok, chain=True)
     assert_rows_close(host(wl.out)[tok], ref["out"], what="W4A4 layer (oracle chain)")
+
+
+def test_workload9_w4a4_chain_decode_every_row_and_token():
+    # the layer at one 8-token decode step: both GEMMs on the weight-streaming
+    # schedule; every element of every step against the oracle, both
+    # quantizations bit-exact, and the oracle's own chain on every token
+    wl = _run(9)
+    off, srt, p2s, _ = _check_route(wl)
+    d = wl.d
+    n = int(off[-1])
+    assert n == wl.T * wl.k < 16 * wl.E
+    ref_q, ref_s = oracle.quantize_int4_rows(d["x"])
+    assert np.array_equal(host(wl.qx), ref_q) and np.array_equal(host(wl.sx), ref_s)
+    h_ref = oracle.grouped_gemm_qint4(host(wl.qx), host(wl.sx), "token", d["w"], d["w_scale"], off, srt,
+                                      d["k"], act="silu_mul")["y"]
+    assert_rows_close(host(wl.h)[:n], h_ref, what="FC1 h")
+    hq_ref, hs_ref = oracle.quantize_int4_rows(host(wl.h)[:n].astype(np.float16))
+    assert np.array_equal(host(wl.qh)[:n], hq_ref) and np.array_equal(host(wl.sh)[:n], hs_ref)
+    y_ref = oracle.grouped_gemm_qint4(host(wl.qh), host(wl.sh), "sorted", d["w2"], d["w2_scale"], off, srt,
+                                      d["k"])["y"]
+    assert_rows_close(host(wl.y)[:n], y_ref, what="FC2 y")
+    ref = oracle.int4_ffn_layer(d, np.arange(wl.T), chain=True)
+    assert_rows_close(host(wl.out), ref["out"], what="W4A4 decode layer (oracle chain)")
