@@ -98,6 +98,27 @@ def test_round_to_bf16_matches_torch_from_f32():
     assert np.array_equal(got, ref)
 
 
+def test_round_to_bf16_rounds_once_from_f64():
+    # values off the fp32 grid, where rounding to fp32 first (to a tie) and
+    # then to bf16 would land on the other neighbour; expected values from
+    # the definition of nearest-even on the bf16 grid (8 significant bits)
+    cases = [
+        (1 + 2.0 ** -8 + 2.0 ** -30, 1 + 2.0 ** -7),   # above the midpoint: up
+        (1 + 2.0 ** -8 - 2.0 ** -30, 1.0),              # below it: down
+        (1 + 2.0 ** -8, 1.0),                           # the tie: even (1.0)
+        (1 + 3 * 2.0 ** -8, 1 + 2.0 ** -6),             # tie between odd and even: even
+        (-(3 + 2.0 ** -7 + 2.0 ** -40), -(3 + 2.0 ** -6)),
+        (2.0 ** -134 * (1 + 2.0 ** -40), 2.0 ** -133),  # subnormal grid, just above half
+        (2.0 ** -134, 0.0),                             # subnormal tie: even (zero)
+        # the largest bf16, (2 - 2^-7) 2^127, has spacing 2^120 above it
+        ((2 - 2.0 ** -7) * 2.0 ** 127 + 2.0 ** 119 - 2.0 ** 90, (2 - 2.0 ** -7) * 2.0 ** 127),
+        ((2 - 2.0 ** -7) * 2.0 ** 127 + 2.0 ** 119, np.inf),   # tie at the top: even is 2^128
+    ]
+    x = np.array([c[0] for c in cases])
+    want = np.array([c[1] for c in cases])
+    assert np.array_equal(oracle.round_to_bf16(x), want)
+
+
 def test_round_to_f16_matches_torch_from_f32():
     x = _ties_and_randoms(np.random.default_rng(2))
     x = x[np.isfinite(x)]

@@ -77,3 +77,65 @@ def test_input_dtype_is_read_exactly(dtype):
     qa, sa = oracle.quantize_int4_rows(x)
     qb, sb = oracle.quantize_int4_rows(x.astype(np.float64))
     assert np.array_equal(qa, qb) and np.array_equal(sa, sb)
+
+
+# Rows on which the two readings of the rule differ: codes from the
+# reciprocal, rne(fl32(x * fl32(7 / amax))) (the reading taken), against the
+# quotient, rne(fl32(x / fl32(amax / 7))).  Each row is [amax, x] as fp32
+# bits; the last two fields are the code of x under each reading.
+SEPARATING = [
+    (0x4012A5E6, 0x3F92A5E6, 3, 4),    # x = amax / 2: exactly 3.5 in the reals
+    (0x3F809561, 0x3F6ECC47, 7, 6),
+    (0x401B1BE7, 0xBF04F358, -2, -1),
+    (0x3F18B166, 0x3EEFF232, 5, 6),
+    (0x3FD3B845, 0xBDF1F72B, 0, -1),
+    (0x3F9B25E0, 0x3DB14FDC, 0, 1),
+]
+
+
+def _fp32_from_bits(b):
+    return struct.unpack("<f", struct.pack("<I", b))[0]
+
+
+def _nearest_fp32(q):
+    """Correctly rounded fp32 value (ties to even) of a nonzero rational q in
+    the normal range, from the definition: q / 2^(e-23) rounded to an
+    integer, e = floor(log2 |q|)."""
+    from fractions import Fraction
+    s, q = (-1, -q) if q < 0 else (1, q)
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    if Fraction(2) ** e > q:
+        e -= 1
+    quantum = Fraction(2) ** (e - 23)
+    n = q / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return s * fl * quantum
+
+
+def _rne_int(q):
+    from fractions import Fraction
+    fl = q.numerator // q.denominator
+    rem = q - fl
+    return fl + 1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1) else fl
+
+
+@pytest.mark.parametrize("amax_bits,x_bits,code_recip,code_quot", SEPARATING)
+def test_reading_separates_reciprocal_from_quotient(amax_bits, x_bits, code_recip, code_quot):
+    from fractions import Fraction
+    amax, x = Fraction(_fp32_from_bits(amax_bits)), Fraction(_fp32_from_bits(x_bits))
+    # both readings in exact rational arithmetic with explicit fp32 roundings
+    recip = _nearest_fp32(Fraction(7) / amax)
+    t_recip = _nearest_fp32(x * recip) if x else Fraction(0)
+    s = _nearest_fp32(amax / 7)
+    t_quot = _nearest_fp32(x / s) if x else Fraction(0)
+    assert _rne_int(t_recip) == code_recip and _rne_int(t_quot) == code_quot
+    assert code_recip != code_quot
+    # the oracle follows the reciprocal reading, and its scale is fl32(amax/7)
+    row = np.array([[_fp32_from_bits(amax_bits), _fp32_from_bits(x_bits)]], np.float32)
+    q, sc = oracle.quantize_int4_rows(row)
+    codes = oracle.int4_value(oracle.unpack_nibbles(q))[0]
+    assert codes[0] == 7 and codes[1] == code_recip
+    assert Fraction(float(sc[0])) == s
