@@ -252,7 +252,10 @@ class Workload:
                 self.out = torch.empty(T, d["N2"], dtype=torch.float16, device="cuda")
                 self.flops = 2.0 * P * (d["N"] * d["K"] + d["N2"] * d["K2"])
             self.weight_bytes = None
-            self.dom = ("int4_prefill", ["gemm_int4.hip", "common.h", "tile.h"], "mfma", PEAK["int8"])
+            # the 64-token problem runs on the streaming schedule (its 256x256
+            # tiles would occupy a handful of compute units)
+            self.dom = (("int4_decode", ["gemm_int4.hip", "common.h", "tile.h", "pipeline.h"]) if idx == 0 else
+                        ("int4_prefill", ["gemm_int4.hip", "common.h", "tile.h"])) + ("mfma", PEAK["int8"])
         else:  # nvfp4
             H, I = d["H"], d["I"]
             self.x = _dev(d["x"])
@@ -597,7 +600,7 @@ def summarize_profiles(idx: int, pdir: str, steps: int = 50, warmup: int = 10):
         wl.d = synth.workload(idx)
         wl.T, wl.k, wl.E = wl.d["T"], wl.d["k"], wl.d["E"]
     d = wl.d
-    tag = ("fp8_decode" if idx == 6 else None) or ("int4_decode" if idx == 9 else None) or \
+    tag = ("fp8_decode" if idx == 6 else None) or ("int4_decode" if idx in (0, 9) else None) or \
         {"fp8": "fp8_prefill", "int4": "int4_prefill", "int4chain": "int4_prefill", "quant": "quant_int4_rows_reg",
          "repack": "repack_nvfp4"}.get(cfg["kind"]) or \
         ("nvfp4_decode" if idx == 2 else "nvfp4_prefill")

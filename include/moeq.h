@@ -187,6 +187,11 @@ moeq_status moe_route_prep_noalloc(const int32_t* topk_ids, int64_t T, int32_t t
  * a multiple of 16), K < 131072 so that the int32 accumulator cannot wrap
  * (else MOEQ_EINVAL), all pointers 16-byte aligned, 1 <= E <= 1024,
  * 1 <= topk <= 64.
+ * Two schedules give identical outputs: 256x256 MFMA tiles (PREFILL), and
+ * waves streaming 32 weight rows x at most 8 routed rows of one expert
+ * (DECODE), which needs K % 256 == 0 (else MOEQ_EALIGN).  AUTO streams when
+ * K % 256 == 0 and either P < 16 * E or the tiles would be fewer than half
+ * the compute units.
  * ---------------------------------------------------------------------- */
 moeq_status grouped_gemm_qint4(const uint8_t* a, const float* a_scale, int64_t rows_a,
                                moeq_arow a_row, const uint8_t* w, const float* w_scale,

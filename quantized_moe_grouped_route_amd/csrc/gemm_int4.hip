@@ -622,9 +622,15 @@ hipError_t go(const GroupedArgs& g, int grid, const uint8_t* a, const float* a_s
 
 hipError_t launch_gemm_int4(const GroupedArgs& g, const uint8_t* a, const float* a_scale,
                             const uint8_t* w, const float* w_scale, hipStream_t stream) {
-  // AUTO takes the streaming schedule when experts hold few rows on average
-  // and K fills whole 256-value groups (the host rejects DECODE otherwise).
-  const bool decode = g.sched == 1 || (g.sched == 0 && g.P < (int64_t)16 * g.E && g.K % dd::kGroupK == 0);
+  // Upper bound on tiles: every expert adds at most one partial m-tile.
+  const int64_t mt_ub = (g.P + kBM - 1) / kBM + std::min<int64_t>(g.E, g.P);
+  const int64_t n_tiles = g.silu_mul ? (g.N / 2 + 127) / 128 : (g.N + kBN - 1) / kBN;
+  const int64_t items_ub = mt_ub * n_tiles;
+  // AUTO takes the streaming schedule when experts hold few rows on average,
+  // or when the tiles would leave most compute units idle, and K fills whole
+  // 256-value groups (the host rejects DECODE otherwise).
+  const bool decode = g.sched == 1 || (g.sched == 0 && g.K % dd::kGroupK == 0 &&
+                                       (g.P < (int64_t)16 * g.E || 2 * items_ub < g.num_cus));
   if (decode) {
     if (g.P == 0) return hipSuccess;
     if (g.silu_mul) {
@@ -641,10 +647,6 @@ hipError_t launch_gemm_int4(const GroupedArgs& g, const uint8_t* a, const float*
       default: return go_decode<OUT_F32, false>(g, a, a_scale, w, w_scale, stream);
     }
   }
-  // Upper bound on tiles: every expert adds at most one partial m-tile.
-  const int64_t mt_ub = (g.P + kBM - 1) / kBM + std::min<int64_t>(g.E, g.P);
-  const int64_t n_tiles = g.silu_mul ? (g.N / 2 + 127) / 128 : (g.N + kBN - 1) / kBN;
-  const int64_t items_ub = mt_ub * n_tiles;
   if (items_ub == 0) return hipSuccess;
   const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus);
   if (g.silu_mul) {

@@ -97,32 +97,35 @@ def _int4_case(seed, T, E, k, N, K, routing="distinct"):
     return d, offs, srt, p2s
 
 
+@pytest.mark.parametrize("sched", ["prefill", "auto"])
 @pytest.mark.parametrize("T,E,k,N,K", [(300, 5, 2, 384, 512), (64, 4, 2, 256, 256),
                                        (37, 3, 3, 128, 128), (5, 8, 2, 256, 384)])
-def test_int4_raw_accumulator_bit_exact(T, E, k, N, K):
+def test_int4_raw_accumulator_bit_exact(sched, T, E, k, N, K):
     d, offs, srt, p2s = _int4_case(21, T, E, k, N, K, routing="repeat")
     acc = mq.grouped_gemm_qint4(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]),
-                                offs, srt, k, out_dtype=torch.int32)
+                                offs, srt, k, out_dtype=torch.int32, sched=sched)
     ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"],
                                     host(offs), host(srt), k)
     n = int(host(offs)[-1])
     assert np.array_equal(host(acc)[:n], ref["acc"])
 
 
+@pytest.mark.parametrize("sched", ["prefill", "auto"])
 @pytest.mark.parametrize("odt", [torch.float16, torch.bfloat16, torch.float32])
-def test_int4_scaled(odt):
+def test_int4_scaled(sched, odt):
     d, offs, srt, p2s = _int4_case(22, 300, 5, 2, 384, 512)
     y = mq.grouped_gemm_qint4(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]),
-                              offs, srt, 2, out_dtype=odt)
+                              offs, srt, 2, out_dtype=odt, sched=sched)
     ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"],
                                     host(offs), host(srt), 2)
     assert_rows_close(host(y)[: ref["y"].shape[0]], ref["y"], what="int4")
 
 
-def test_int4_silu_mul_and_sorted_rows():
+@pytest.mark.parametrize("sched", ["prefill", "auto"])
+def test_int4_silu_mul_and_sorted_rows(sched):
     d, offs, srt, p2s = _int4_case(23, 200, 4, 2, 512, 256)
     h = mq.grouped_gemm_qint4(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]),
-                              offs, srt, 2, act="silu_mul", out_dtype=torch.float16)
+                              offs, srt, 2, act="silu_mul", out_dtype=torch.float16, sched=sched)
     ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"],
                                     host(offs), host(srt), 2, act="silu_mul")
     assert_rows_close(host(h)[: ref["y"].shape[0]], ref["y"], what="int4 silu")
@@ -133,13 +136,14 @@ def test_int4_silu_mul_and_sorted_rows():
     s2 = synth.uniform_f32(rng, (P,), 0.005, 0.05)
     y2 = mq.grouped_gemm_qint4(dev(a2), dev(s2), dev(d["w"][:, :, :128].copy()),
                                dev(d["w_scale"]), offs, srt, 2, a_row="sorted",
-                               out_dtype=torch.int32)
+                               out_dtype=torch.int32, sched=sched)
     ref2 = oracle.grouped_gemm_qint4(a2, s2, "sorted", d["w"][:, :, :128], d["w_scale"],
                                      host(offs), host(srt), 2)
     assert np.array_equal(host(y2)[: ref2["acc"].shape[0]], ref2["acc"])
 
 
-def test_int4_rows_past_offsets_untouched_and_empty_experts():
+@pytest.mark.parametrize("sched", ["prefill", "auto"])
+def test_int4_rows_past_offsets_untouched_and_empty_experts(sched):
     T, E, k, N, K = 50, 6, 2, 256, 256
     d = synth.int4_moe(24, T, E, k, N, K)
     d["topk_ids"][d["topk_ids"] >= 3] = -1          # experts 3..5 empty, some pairs skipped
@@ -147,14 +151,15 @@ def test_int4_rows_past_offsets_untouched_and_empty_experts():
     n = int(host(offs)[-1])
     out = torch.full((T * k, N), 12345, dtype=torch.int32, device="cuda")
     mq.grouped_gemm_qint4(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]),
-                          offs, srt, k, out_dtype=torch.int32, out=out)
+                          offs, srt, k, out_dtype=torch.int32, out=out, sched=sched)
     assert torch.all(out[n:] == 12345)
     ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"],
                                     host(offs), host(srt), k)
     assert np.array_equal(host(out)[:n], ref["acc"])
 
 
-def test_int4_extreme_codes():
+@pytest.mark.parametrize("sched", ["prefill", "auto"])
+def test_int4_extreme_codes(sched):
     # all codes -8: acc = 64*K per element, the largest magnitude
     T, E, N, K = 40, 2, 128, 4096
     ids = np.zeros((T, 1), np.int32)
@@ -164,7 +169,7 @@ def test_int4_extreme_codes():
     offs, srt, p2s, _ = mq.moe_route_prep(dev(ids), E)
     acc = mq.grouped_gemm_qint4(dev(a), dev(np.ones(T, np.float32)), dev(w),
                                 dev(np.ones((E, N), np.float32)), offs, srt, 1,
-                                out_dtype=torch.int32)
+                                out_dtype=torch.int32, sched=sched)
     assert torch.all(acc == 64 * K)
 
 
