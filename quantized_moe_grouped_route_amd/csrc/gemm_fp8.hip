@@ -311,12 +311,11 @@ __global__ __launch_bounds__(64 * fd::kWaves) void fp8_decode(
   const int n_blocks = N / 16;
   sched_build(tile_start, sched_scratch, offsets, E, P, fd::kM, n_blocks);
   const int total = __builtin_amdgcn_readfirstlane(tile_start[E]);
-  // Items go to the fewest waves that still need the same number of rounds.
-  const int waves = gridDim.x * fd::kWaves;
-  const int rounds = (total + waves - 1) / waves;
-  const int active = rounds ? (total + rounds - 1) / rounds : 0;
+  // Items are dealt round robin over all waves (as in the INT4 and NVFP4
+  // streaming schedules; equal to dealing them to the fewest waves here).
+  const int active = gridDim.x * fd::kWaves;
   const int wid = blockIdx.x * fd::kWaves + wv;
-  if (wid >= active) return;
+  if (wid >= total) return;
   const int G = K / 128;
   uint8_t* myring = &ring[wv][0][0];
   const uint32_t lb = lds_addr(myring);
