@@ -277,6 +277,7 @@ class Workload:
             self.h = torch.empty(P, I, dtype=hdt, device="cuda")
             self.y = torch.empty(P, H, dtype=torch.bfloat16, device="cuda")
             self.tw_flat = self.tw.reshape(-1)
+            self.wq = mq.work_queue()  # tile balancing of the tiled schedule (one per stream)
             self.out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
             ids = d["topk_ids"].reshape(-1)
             valid = ids[(ids >= 0) & (ids < E)]
@@ -366,16 +367,17 @@ class Workload:
                 x = mq.cast_bf16_to_f16(self.x, out=self.xh)
             if ev: ev[0].record()
             mq.grouped_gemm_qnvfp4(x, self.w1, self.s1, self.g1, offs, srt, self.k, act="silu_mul",
-                                   out=self.h, out_dtype=self.h.dtype)
+                                   out=self.h, out_dtype=self.h.dtype, work_queue=self.wq)
             if ev: ev[1].record()
             if self.fc2 == "pair":
                 # top-k weight in FC2's epilogue, rows in pair order, then the pair sum
                 mq.grouped_gemm_qnvfp4(self.h, self.w2, self.s2, self.g2, offs, srt, self.k,
-                                       a_row="sorted", pair_weights=self.tw_flat, out=self.y)
+                                       a_row="sorted", pair_weights=self.tw_flat, out=self.y,
+                                       work_queue=self.wq)
                 mq.moe_sum_pairs(self.y, p2s, self.T, self.k, out=self.out)
             else:
                 mq.grouped_gemm_qnvfp4(self.h, self.w2, self.s2, self.g2, offs, srt, self.k,
-                                       a_row="sorted", out=self.y)
+                                       a_row="sorted", out=self.y, work_queue=self.wq)
                 mq.moe_scatter_combine(self.y, p2s, self.tw, out=self.out)
 
     def dominant_launches(self):

@@ -110,6 +110,9 @@ typedef enum { MOEQ_SCHED_AUTO = 0, MOEQ_SCHED_DECODE = 1, MOEQ_SCHED_PREFILL = 
  * (host, thread-local, owned by the library; valid until the next call). */
 const char* moeq_last_error(void);
 
+/* int32 counters of grouped_gemm_qnvfp4's optional work queue. */
+#define MOEQ_WORK_QUEUE_INTS 16
+
 /* Library ABI version (host). */
 int32_t moeq_abi_version(void);
 
@@ -259,6 +262,16 @@ moeq_status grouped_gemm_qfp8_block(const uint8_t* a, const float* a_scale, int6
  *             MOEQ_EINVAL); every pair id must be < P, as moe_route_prep's
  *             are.  moe_sum_pairs then sums each token's rows.
  *   out       [P][N] (NONE) or [P][N/2] (SILU_MUL*), BF16 | F16 | F32
+ *   work_queue  NULL, or MOEQ_WORK_QUEUE_INTS int32 of device memory, 4-byte
+ *             aligned (else MOEQ_EALIGN), that are zero when the call starts
+ *             running (zero them once: every call leaves them zero).  The
+ *             tiled schedule then hands its tiles out through atomic
+ *             counters in them (one per XCD), so a workgroup takes the next
+ *             tile when it finishes one, which balances tiles of unequal
+ *             cost (the partial last m-tiles of skewed routing); without it
+ *             each workgroup takes every gridDim-th tile.  The outputs are
+ *             the same either way.  Calls that may overlap in time on one
+ *             GPU need separate queues.  The streaming schedule ignores it.
  *   y[s][n] = w_gscale[e] * sum_k x[r][k] * e2m1(w[e][n][k])
  *                                  * ue4m3(w_sf[e][n][k/16])
  * Requires K % 128 == 0 and N % 32 == 0 (else MOEQ_EALIGN; SILU_MUL then
@@ -273,7 +286,8 @@ moeq_status grouped_gemm_qnvfp4(const void* x, moeq_dtype x_dtype, int64_t rows_
                                 const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
                                 int64_t P, int32_t topk, int32_t E, int64_t N, int64_t K,
                                 moeq_act act, float act_limit, const float* pair_weights,
-                                moeq_dtype out_dtype, void* out, moeq_sched sched, void* stream);
+                                moeq_dtype out_dtype, void* out, int32_t* work_queue, moeq_sched sched,
+                                void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_cast_bf16_to_f16 - bf16 -> IEEE binary16 conversion of activations,

@@ -38,6 +38,14 @@ EXPORTS = ("moeq_last_error", "moeq_abi_version", "moe_route_prep_workspace_byte
 
 # Fixed device scratch of moe_route_prep_noalloc per GPU (include/moeq.h).
 ROUTE_NOALLOC_SCRATCH_BYTES = 1 << 20
+# int32 counters of grouped_gemm_qnvfp4's optional work queue (include/moeq.h).
+WORK_QUEUE_INTS = 16
+
+
+def work_queue(device="cuda"):
+    """A zeroed work queue for grouped_gemm_qnvfp4 (each call leaves it zero;
+    calls that may overlap in time need their own)."""
+    return torch.zeros(WORK_QUEUE_INTS, dtype=torch.int32, device=device)
 
 
 class MoeqError(RuntimeError):
@@ -69,7 +77,7 @@ def lib():
         "grouped_gemm_qfp8_block": (i32, [vp, vp, i64, i32, vp, vp, vp, vp, i64, i32, i32, i64,
                                           i64, i32, vp, i32, vp]),
         "grouped_gemm_qnvfp4": (i32, [vp, i32, i64, i32, vp, i32, vp, i32, vp, vp, vp, i64, i32, i32, i64, i64,
-                                      i32, C.c_float, vp, i32, vp, i32, vp]),
+                                      i32, C.c_float, vp, i32, vp, vp, i32, vp]),
         "moe_scatter_combine": (i32, [vp, i32, vp, vp, i64, i32, i64, i32, vp, vp]),
         "moe_quantize_int4": (i32, [vp, i32, i64, i64, vp, vp, vp]),
         "moe_nvfp4_repack": (i32, [vp, vp, i64, i64, i64, i32, i32, i32, vp, vp, vp]),
@@ -250,7 +258,7 @@ def grouped_gemm_qfp8_block(a, a_scale, w, w_scale, expert_offsets, sorted_pair_
 
 def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, topk: int, *,
                         a_row="token", act="none", limit=None, pair_weights=None,
-                        out_dtype=torch.bfloat16, out=None, P=None, sched="auto"):
+                        out_dtype=torch.bfloat16, out=None, P=None, sched="auto", work_queue=None):
     """NVFP4 W4A16 grouped GEMM: x bf16 or f16 [rows_a][K] (f16: dequant and
     MFMA in binary16, megamoe_rm.cu's fp16 activations), w uint8 [E][N][K/2]
     (row-major) or [E][N/16][K/64][16][32] (tiled)
@@ -260,7 +268,9 @@ def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, t
     f32 [E].  Returns out [P][N] (act 'none') or [P][N/2] ('silu_mul';
     with `limit`, the clamped SwiGLU of megamoe_rm.cu's fc1_rm).
     pair_weights (f32, T*topk values, e.g. topk_weights): megamoe_rm.cu's
-    fc2_rm epilogue, out row p = w[p] * y of pair p, in pair order."""
+    fc2_rm epilogue, out row p = w[p] * y of pair p, in pair order.
+    work_queue (int32, WORK_QUEUE_INTS zeros, see work_queue()): the tiled
+    schedule then balances its tiles through atomic counters in it."""
     _need(x, "x", (torch.bfloat16, torch.float16), 2)
     _need(w, "w", torch.uint8)
     if w.dim() == 5 and tuple(w.shape[3:]) == (16, 32):
@@ -291,15 +301,19 @@ def grouped_gemm_qnvfp4(x, w, w_sf, w_gscale, expert_offsets, sorted_pair_ids, t
         if P < sorted_pair_ids.numel():
             # rows are written at pair ids, which run up to sorted_pair_ids.numel() - 1
             raise ValueError("with pair_weights, P must be at least the number of pairs")
+    if work_queue is not None:
+        _need(work_queue, "work_queue", torch.int32, 1)
+        if work_queue.numel() < WORK_QUEUE_INTS:
+            raise ValueError(f"work_queue needs {WORK_QUEUE_INTS} int32")
     out = _out(out, P, N // 2 if act == "silu_mul" else N, out_dtype, x.device)
     _gpu(x=x, w=w, w_sf=w_sf, w_gscale=w_gscale, expert_offsets=expert_offsets,
-         sorted_pair_ids=sorted_pair_ids, pair_weights=pair_weights, out=out)
+         sorted_pair_ids=sorted_pair_ids, pair_weights=pair_weights, work_queue=work_queue, out=out)
     st = lib().grouped_gemm_qnvfp4(_ptr(x), _DTYPE_CODE[x.dtype], x.shape[0], arow, _ptr(w),
                                    W_LAYOUT["tiled" if w_tiled else "rows"], _ptr(w_sf),
                                    SF_LAYOUT["quads" if quads else "rows"], _ptr(w_gscale),
                                    _ptr(expert_offsets), _ptr(sorted_pair_ids), P, topk, E, N, K,
                                    act_code, 0.0 if limit is None else float(limit), _ptr(pair_weights),
-                                   _DTYPE_CODE[out_dtype], _ptr(out), SCHED[sched], _stream())
+                                   _DTYPE_CODE[out_dtype], _ptr(out), _ptr(work_queue), SCHED[sched], _stream())
     _check("grouped_gemm_qnvfp4", st)
     return out
 

@@ -83,7 +83,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void nvfp4_prefill(
     const uint16_t* __restrict__ x, int64_t rows_a, int a_sorted, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ w_sf, const float* __restrict__ w_gscale,
     const int* __restrict__ offsets, const int* __restrict__ sorted_ids, int topk, int E, int P, int N,
-    int K, void* __restrict__ out, float limit, const float* __restrict__ pair_w, int sf_quads, int w_tiled) {
+    int K, void* __restrict__ out, float limit, const float* __restrict__ pair_w, int sf_quads, int w_tiled,
+    int* __restrict__ queue) {
   static_assert(!(SILU && PAIR), "pair-ordered output is for act NONE");
   static_assert(NW == 4 || NW == 8, "tile widths");
   using pf::kM;
@@ -118,7 +119,25 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void nvfp4_prefill(
 #pragma unroll
   for (int s = 0; s < 4; ++s) aoff[s] = (((4 * slice + s) ^ key) << 4);
 
-  for (int item = xcd_logical_id(blockIdx.x, gridDim.x); item < total; item += gridDim.x) {
+  // Tile order.  Without a queue, workgroup b takes every gridDim-th tile
+  // from its XCD-first logical id, so an XCD holds a contiguous block of
+  // each round of gridDim tiles.  With a queue, the workgroups of an XCD
+  // claim that same block of each round through the XCD's counter, in
+  // order, each taking the next tile when it finishes one; the last
+  // workgroup to finish zeroes the counters for the next call.
+  const int nxcd = gridDim.x % 8 == 0 ? 8 : 1;
+  const int xq = blockIdx.x % nxcd, per = gridDim.x / nxcd;
+  __shared__ int s_item;
+  auto claim = [&]() __attribute__((always_inline)) {
+    if (threadIdx.x == 0) {
+      const int c = atomicAdd(&queue[xq], 1);
+      s_item = (c / per) * (int)gridDim.x + per * xq + c % per;
+    }
+    __syncthreads();  // also: every thread has read the previous claim
+    return s_item;
+  };
+  for (int item = queue ? claim() : xcd_logical_id(blockIdx.x, gridDim.x); item < total;
+       item = queue ? claim() : item + (int)gridDim.x) {
     // two m-tiles per n-tile sweep: measured 1-3 % faster than four on the
     // Zipf prefill (FC1 and FC2), equal to one within the noise
     const Tile t = sched_tile<2>(tile_start, offsets, E, P, kM, n_tiles, item);
@@ -310,6 +329,11 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void nvfp4_prefill(
         }
       }
     }
+  }
+  if (queue && threadIdx.x == 0 && atomicAdd(&queue[8], 1) == (int)gridDim.x - 1) {
+    // every workgroup has made its last claim
+    for (int x = 0; x < 8; ++x) atomicExch(&queue[x], 0);
+    atomicExch(&queue[8], 0);
   }
 }
 
@@ -716,13 +740,13 @@ hipError_t go(const GroupedArgs& g, bool decode, const uint16_t* x, const uint8_
       const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus);
       hipLaunchKernelGGL((nvfp4_prefill<OUT, SILU, PAIR, H16, 8>), dim3(grid), dim3(pf::Geo<8>::kThreads), 0, stream,
                          x, g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P,
-                         g.N, g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads, g.w_tiled);
+                         g.N, g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads, g.w_tiled, g.queue);
     } else {
       const int64_t items_ub = mt_ub * (g.N / pf::Geo<4>::kN);
       const int grid = (int)std::min<int64_t>(items_ub, (int64_t)g.num_cus * 2);
       hipLaunchKernelGGL((nvfp4_prefill<OUT, SILU, PAIR, H16, 4>), dim3(grid), dim3(pf::Geo<4>::kThreads), 0, stream,
                          x, g.rows_a, g.a_sorted, w, sf, gsc, g.offsets, g.sorted_ids, g.topk, g.E, (int)g.P,
-                         g.N, g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads, g.w_tiled);
+                         g.N, g.K, g.out, g.act_limit, g.pair_weights, g.sf_quads, g.w_tiled, g.queue);
     }
   }
   return hipGetLastError();

@@ -15,6 +15,9 @@ hipError_t launch_route(const int* ids, int P, int E, int* offsets, int* sorted_
 // Route prep with its per-chunk counts in the library's fixed device array
 // (kRouteNoallocScratchBytes per device) instead of a caller's workspace.
 constexpr size_t kRouteNoallocScratchBytes = size_t(1) << 20;
+// Counters of the NVFP4 tiled schedule's work queue: one claim counter per
+// XCD (8) and one count of finished workgroups.
+constexpr int kWorkQueueInts = 16;
 hipError_t launch_route_noalloc(const int* ids, int P, int E, int* offsets, int* sorted_ids,
                                 int* pair_to_sorted, int* n_invalid, hipStream_t stream);
 
@@ -47,6 +50,7 @@ struct GroupedArgs {
   int out_kind;             // OutKind
   void* out;
   int sched;                // 0 auto, 1 decode, 2 prefill
+  int* queue;               // NVFP4 tiled schedule: [kWorkQueueInts] zeroed counters, or null
   int num_cus;              // compute units of the current device
 };
 

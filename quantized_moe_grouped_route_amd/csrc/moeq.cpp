@@ -98,6 +98,7 @@ moeq::GroupedArgs make_args(const int32_t* offsets, const int32_t* sorted, int64
   g.out_kind = (int)od;
   g.out = out;
   g.sched = (int)sched;
+  g.queue = nullptr;
   g.num_cus = device_cus();
   return g;
 }
@@ -108,7 +109,7 @@ extern "C" {
 
 const char* moeq_last_error(void) { return g_err.c_str(); }
 
-int32_t moeq_abi_version(void) { return 2; }
+int32_t moeq_abi_version(void) { return 3; }
 
 size_t moe_route_prep_workspace_bytes(int64_t T, int32_t topk, int32_t E) {
   if (T < 0 || topk < 1 || E < 1) return 0;
@@ -219,7 +220,8 @@ moeq_status grouped_gemm_qnvfp4(const void* x, moeq_dtype x_dtype, int64_t rows_
                                 const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
                                 int64_t P, int32_t topk, int32_t E, int64_t N, int64_t K,
                                 moeq_act act, float act_limit, const float* pair_weights,
-                                moeq_dtype out_dtype, void* out, moeq_sched sched, void* stream) {
+                                moeq_dtype out_dtype, void* out, int32_t* work_queue, moeq_sched sched,
+                                void* stream) {
   const char* fn = "grouped_gemm_qnvfp4";
   moeq_status st = check_grouped(fn, x, rows_a, a_row, w, expert_offsets, P, topk, E, N, K, out, 32);
   if (st != MOEQ_OK) return st;
@@ -243,8 +245,11 @@ moeq_status grouped_gemm_qnvfp4(const void* x, moeq_dtype x_dtype, int64_t rows_
   if (a_row == MOEQ_AROW_TOKEN && !sorted_pair_ids && rows_a < P)
     return fail(MOEQ_EINVAL, "%s: identity rows need rows_a >= P", fn);
   if (sched < MOEQ_SCHED_AUTO || sched > MOEQ_SCHED_PREFILL) return fail(MOEQ_EINVAL, "%s: sched %d", fn, sched);
+  static_assert(moeq::kWorkQueueInts == MOEQ_WORK_QUEUE_INTS, "header and library agree");
+  if (work_queue && !aligned(work_queue, 4)) return fail(MOEQ_EALIGN, "%s: work_queue misaligned", fn);
   moeq::GroupedArgs g = make_args(expert_offsets, sorted_pair_ids, rows_a, a_row, P, topk, E, N, K,
                                   act != MOEQ_ACT_NONE, out_dtype, out, sched);
+  g.queue = work_queue;
   if (act == MOEQ_ACT_SILU_MUL_LIMIT) g.act_limit = act_limit;
   g.pair_weights = pair_weights;
   g.x_f16 = x_dtype == MOEQ_F16 ? 1 : 0;

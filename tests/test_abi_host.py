@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(L):
     raw = C.CDLL(mq.LIB_PATH)
     for f in declared_functions():
         assert hasattr(raw, f), f
-    assert L.moeq_abi_version() == 2
+    assert L.moeq_abi_version() == 3
 
 
 def test_workspace_bytes(L):
@@ -115,12 +115,12 @@ def test_fp8_rejects(L, kw, status):
 
 def _nvfp4(L, **kw):
     a = dict(x=A16, xd=mq.BF16, rows=16, arow=0, w=A16, wl=0, sf=A16, sfl=0, gs=A16, off=A16, srt=A16, P=16,
-             topk=2, E=4, N=256, K=256, act=0, lim=0.0, pw=None, od=mq.BF16, out=A16, sched=0)
+             topk=2, E=4, N=256, K=256, act=0, lim=0.0, pw=None, od=mq.BF16, out=A16, wq=None, sched=0)
     a.update(kw)
     return L.grouped_gemm_qnvfp4(a["x"], a["xd"], a["rows"], a["arow"], a["w"], a["wl"], a["sf"], a["sfl"],
                                  a["gs"], a["off"],
                                  a["srt"], a["P"], a["topk"], a["E"], a["N"], a["K"], a["act"],
-                                 a["lim"], a["pw"], a["od"], a["out"], a["sched"], None)
+                                 a["lim"], a["pw"], a["od"], a["out"], a["wq"], a["sched"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -132,6 +132,7 @@ def _nvfp4(L, **kw):
     (dict(pw=A16, act=1), mq.EUNSUPPORTED), (dict(pw=A16, srt=None), mq.EINVAL),
     (dict(pw=ODD), mq.EALIGN), (dict(xd=mq.F32), mq.EUNSUPPORTED), (dict(xd=mq.I32), mq.EUNSUPPORTED),
     (dict(sfl=2), mq.EINVAL), (dict(sfl=-1), mq.EINVAL), (dict(wl=2), mq.EINVAL),
+    (dict(wq=ODD), mq.EALIGN),
 ])
 def test_nvfp4_rejects(L, kw, status):
     assert _nvfp4(L, **kw) == status

@@ -494,6 +494,38 @@ def test_repeat_runs_bitwise_identical():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("I", [512, 384])       # 512-row tiles (8 waves), 256-row tiles (4 waves)
+@pytest.mark.parametrize("pair", [False, True])
+def test_nvfp4_work_queue_same_outputs_and_left_zero(I, pair):
+    # skewed routing: many partial m-tiles of unequal cost, more tiles than
+    # workgroups; the queue only changes which workgroup computes a tile
+    T, E, k, H = 600, 40, 4, 1024
+    d = synth.nvfp4_moe(45, T, E, k, H, I, routing="zipf")
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    x = dev(d["x"])
+    wq = mq.work_queue()
+    fc1 = dict(act="silu_mul", out_dtype=torch.bfloat16, sched="prefill")
+    h0 = mq.grouped_gemm_qnvfp4(x, dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k, **fc1)
+    for _ in range(3):  # the queue is left zero by each call, so every call sees all tiles
+        h1 = mq.grouped_gemm_qnvfp4(x, dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k, **fc1,
+                                    work_queue=wq)
+        assert torch.equal(h0, h1)
+        assert torch.all(wq == 0)
+    tw = dev(d["topk_weights"].reshape(-1).astype(np.float32)) if pair else None
+    fc2 = dict(a_row="sorted", out_dtype=torch.float32, sched="prefill", pair_weights=tw, P=T * k)
+    y0 = mq.grouped_gemm_qnvfp4(h0, dev(d["w2"]), dev(d["s2"]), dev(d["g2"]), offs, srt, k, **fc2)
+    y1 = mq.grouped_gemm_qnvfp4(h0, dev(d["w2"]), dev(d["s2"]), dev(d["g2"]), offs, srt, k, **fc2,
+                                work_queue=wq)
+    n = int(host(offs)[-1])
+    rows = host(srt)[:n] if pair else np.arange(n)
+    assert torch.equal(y0[rows], y1[rows]) and torch.all(wq == 0)
+    ref = oracle.grouped_gemm_qnvfp4(bf16_bits(h0), "sorted", d["w2"], d["s2"], d["g2"], host(offs),
+                                     host(srt), k)["y"]
+    if pair:
+        ref = ref * d["topk_weights"].reshape(-1)[host(srt)[:n]][:, None]
+    assert_rows_close(host(y1)[rows], ref, what=f"nvfp4 work queue FC2 pair={pair}")
+
+
 # ------------------------------------------------------------------ INT4 activation quantizer
 def _quant_check(x_np, torch_dtype):
     x = torch.from_numpy(np.ascontiguousarray(x_np)).to(torch_dtype)
