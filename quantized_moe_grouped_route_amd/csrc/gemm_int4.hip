@@ -477,7 +477,7 @@ __global__ __launch_bounds__(64 * dd::kWaves) void int4_decode(
   // holds it
   const int crow = lane >> 3;  // + 8 (c % 2)
   const int cp0 = ((lane & 7) ^ ((crow >> 1) & 7)) << 4;
-  const int cp1 = ((lane & 7) ^(((crow + 8) >> 1) & 7)) << 4;
+  const int cp1 = ((lane & 7) ^ (((crow + 8) >> 1) & 7)) << 4;
   // fragment reads: block row l16, pieces 2 quarter and 2 quarter + 1
   const int wkey = (l16 >> 1) & 7;
   const int wf0 = dd::kW + l16 * 128 + (((2 * quarter) ^ wkey) << 4);

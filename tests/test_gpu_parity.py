@@ -888,3 +888,62 @@ def test_every_id_minus_one_gemms_write_nothing_and_combine_writes_zeros():
     pairs = mq.moe_sum_pairs(y, p2s, T, k)
     torch.cuda.synchronize()
     assert torch.all(comb == 0) and torch.all(pairs == 0)
+
+
+# ------------------------------------------------------------------ the boundary's largest sizes
+@pytest.mark.parametrize("sched", ["decode", "prefill"])
+def test_int4_largest_k_extreme_codes(sched):
+    # K = 2^17 - 256, the largest K both INT4 schedules take, every code -8:
+    # each output is 64 K exactly, the accumulator's largest magnitude
+    T, E, N, K = 6, 2, 32, (1 << 17) - 256
+    ids = np.zeros((T, 1), np.int32)
+    ids[1::2] = 1
+    a = np.full((T, K // 2), 0x88, np.uint8)
+    w = np.full((E, N, K // 2), 0x88, np.uint8)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(ids), E)
+    acc = mq.grouped_gemm_qint4(dev(a), dev(np.ones(T, np.float32)), dev(w), dev(np.ones((E, N), np.float32)),
+                                offs, srt, 1, out_dtype=torch.int32, sched=sched)
+    assert torch.all(acc == 64 * K)
+
+
+@pytest.mark.parametrize("sched", ["decode", "prefill"])
+def test_int4_1024_experts_top64(sched):
+    # E = 1024 and topk = 64, the boundary's limits: 2048 pairs, about two
+    # per expert, some experts empty
+    T, E, k, N, K = 32, 1024, 64, 64, 256
+    d = synth.int4_moe(71, T, E, k, N, K)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    assert (np.diff(host(offs)) == 0).any()
+    acc = mq.grouped_gemm_qint4(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]), offs, srt, k,
+                                out_dtype=torch.int32, sched=sched)
+    ref = oracle.grouped_gemm_qint4(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], host(offs), host(srt), k)
+    assert np.array_equal(host(acc)[: int(host(offs)[-1])], ref["acc"])
+    y = mq.grouped_gemm_qint4(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]), offs, srt, k,
+                              out_dtype=torch.float16, sched=sched)
+    out = mq.moe_scatter_combine(y, p2s, dev(d["topk_weights"]))
+    ref_out = oracle.scatter_combine(oracle.round_to_f16(ref["y"]), host(p2s), d["topk_weights"])
+    assert_rows_close(host(out), ref_out, what=f"int4 E=1024 top-64 {sched} combine")
+
+
+@pytest.mark.parametrize("sched", ["decode", "prefill"])
+def test_nvfp4_1024_experts_top64(sched):
+    T, E, k, H, I = 16, 1024, 64, 256, 256
+    d = synth.nvfp4_moe(72, T, E, k, H, I)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    h = mq.grouped_gemm_qnvfp4(dev(d["x"]), dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k,
+                               act="silu_mul", out_dtype=torch.float32, sched=sched, work_queue=mq.work_queue())
+    ref = oracle.grouped_gemm_qnvfp4(d["x"], "token", d["w1"], d["s1"], d["g1"], host(offs), host(srt), k,
+                                     act="silu_mul")["y"]
+    assert_rows_close(host(h)[: ref.shape[0]], ref, what=f"nvfp4 E=1024 top-64 {sched}")
+
+
+@pytest.mark.parametrize("sched", ["decode", "prefill"])
+def test_fp8_1024_experts_top64(sched):
+    T, E, k, N, K = 16, 1024, 64, 128, 256
+    d = synth.fp8_moe(73, T, E, k, N, K)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    y = mq.grouped_gemm_qfp8_block(dev(d["a"]), dev(d["a_scale"]), dev(d["w"]), dev(d["w_scale"]), offs, srt, k,
+                                   out_dtype=torch.float32, sched=sched)
+    ref = oracle.grouped_gemm_qfp8_block(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], host(offs),
+                                         host(srt), k)["y"]
+    assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"fp8 E=1024 top-64 {sched}")
