@@ -947,3 +947,17 @@ def test_fp8_1024_experts_top64(sched):
     ref = oracle.grouped_gemm_qfp8_block(d["a"], d["a_scale"], "token", d["w"], d["w_scale"], host(offs),
                                          host(srt), k)["y"]
     assert_rows_close(host(y)[: ref.shape[0]], ref, what=f"fp8 E=1024 top-64 {sched}")
+
+
+def test_nvfp4_work_queue_grid_not_a_multiple_of_8():
+    # few tiles: the grid is smaller than the chip and not a multiple of 8,
+    # so one counter hands out every tile
+    T, E, k, H, I = 50, 3, 1, 512, 256
+    d = synth.nvfp4_moe(74, T, E, k, H, I)
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    args = (dev(d["x"]), dev(d["w1"]), dev(d["s1"]), dev(d["g1"]), offs, srt, k)
+    wq = mq.work_queue()
+    h0 = mq.grouped_gemm_qnvfp4(*args, act="silu_mul", out_dtype=torch.float32, sched="prefill")
+    for _ in range(2):
+        h1 = mq.grouped_gemm_qnvfp4(*args, act="silu_mul", out_dtype=torch.float32, sched="prefill", work_queue=wq)
+        assert torch.equal(h0, h1) and torch.all(wq == 0)
