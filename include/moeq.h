@@ -10,15 +10,19 @@
  *   moe_scatter_combine     top-k weighted sum back to token rows
  *   (or: grouped_gemm_qnvfp4 with pair_weights + moe_sum_pairs, the top-k
  *   weight applied in FC2's epilogue)
- * with two helpers around it:
+ * with helpers around it:
  *   moe_quantize_int4       per-row INT4 activation quantization
  *   moe_nvfp4_repack        one-shot NVFP4 weight layout conversion
+ *   moe_cast_bf16_to_f16    activations for the binary16 NVFP4 form
+ *   moe_route_prep_noalloc  route prep for callers that cannot allocate
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer (memory the caller allocated
  *     on the current HIP device) unless marked "host".  The caller owns all
- *     memory, scratch included; the library allocates nothing, keeps no state
- *     between calls and never synchronizes the host with the device.
+ *     memory, scratch included (route prep's workspace, the NVFP4 work
+ *     queue); the library allocates nothing and never synchronizes the host
+ *     with the device.  Its one piece of state is moe_route_prep_noalloc's
+ *     fixed per-device scratch.
  *   - Every call only validates its arguments on the host and enqueues
  *     kernels on `stream` (a hipStream_t; NULL = the null stream).  Results
  *     are visible to later work on that stream.
