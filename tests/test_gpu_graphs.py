@@ -1,7 +1,9 @@
-"""The library's calls under HIP graph capture: a captured layer replays to
-the eager result, bit for bit, on every replay.  The library allocates
-nothing, copies nothing and records no memset, and the NVFP4 work queue
-zeroes itself at the end of each launch, so a replay needs no reset."""
+"""The library's calls under HIP graph capture and on concurrent streams: a
+captured layer (route prep without a workspace included) replays to the
+eager result, bit for bit, on every replay.  The library allocates nothing,
+copies nothing and records no memset, and the NVFP4 work queue zeroes itself
+at the end of each launch, so a replay needs no reset; two launches running
+at once on two streams with separate queues each give the lone result."""
 import numpy as np
 import pytest
 import torch
@@ -67,7 +69,7 @@ def test_int4_decode_layer_replays():
     out = torch.empty(T, H, dtype=torch.float16, device="cuda")
 
     def step():
-        offs, srt, p2s, _ = mq.moe_route_prep(ids, E, out=route)
+        offs, srt, p2s, _ = mq.moe_route_prep_noalloc(ids, E, out=route)  # no caller workspace
         mq.quantize_int4_rows(x, q=qx, scale=sx)
         mq.grouped_gemm_qint4(qx, sx, w, sw, offs, srt, k, act="silu_mul", out=h)
         mq.quantize_int4_rows(h, q=qh, scale=sh)
@@ -114,3 +116,30 @@ def test_nvfp4_prefill_layer_with_work_queue_replays(pair):
     outputs = [h, out] if pair else [h, y, out]
     _capture_and_replay(step, outputs)
     assert torch.all(wq == 0)
+
+
+def test_nvfp4_prefill_on_two_streams_with_separate_queues():
+    # two tiled-schedule GEMMs running at the same time on two streams, each
+    # with its own work queue, give the outputs each gives alone
+    T, E, k, H, I = 600, 40, 4, 1024, 512
+    d = synth.nvfp4_moe(63, T, E, k, H, I, routing="zipf")
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(d["topk_ids"]), E)
+    x, w1, s1, g1 = dev(d["x"]), dev(d["w1"]), dev(d["s1"]), dev(d["g1"])
+    ref = mq.grouped_gemm_qnvfp4(x, w1, s1, g1, offs, srt, k, act="silu_mul", sched="prefill")
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    queues = [mq.work_queue(), mq.work_queue()]
+    outs = [torch.empty_like(ref), torch.empty_like(ref)]
+    for rep in range(3):
+        for o in outs:
+            o.fill_(5)
+        torch.cuda.synchronize()
+        for s, q, o in zip(streams, queues, outs):
+            with torch.cuda.stream(s):
+                mq.grouped_gemm_qnvfp4(x, w1, s1, g1, offs, srt, k, act="silu_mul", sched="prefill", out=o,
+                                       work_queue=q)
+        torch.cuda.synchronize()
+        n = int(offs[-1].item())
+        for o in outs:
+            assert torch.equal(o[:n], ref[:n]), f"repeat {rep}"
+        assert all(torch.all(q == 0) for q in queues)
