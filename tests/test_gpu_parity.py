@@ -961,3 +961,21 @@ def test_nvfp4_work_queue_grid_not_a_multiple_of_8():
     for _ in range(2):
         h1 = mq.grouped_gemm_qnvfp4(*args, act="silu_mul", out_dtype=torch.float32, sched="prefill", work_queue=wq)
         assert torch.equal(h0, h1) and torch.all(wq == 0)
+
+
+@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
+def test_combine_streaming_size(ydt):
+    # y past 256 MB: the combine takes its nontemporal (streaming) path
+    T, k, N = 8192 if ydt == torch.float32 else 16384, 2, 4096
+    rng = np.random.default_rng(75)
+    ids = synth.uniform_ids_with_repeats(rng, T, k, 64)
+    ids[::97, 1] = -1
+    offs, srt, p2s, _ = mq.moe_route_prep(dev(ids), 64)
+    y = torch.randn(T * k, N, device="cuda").to(ydt)
+    assert y.numel() * y.element_size() >= 256 << 20
+    w = synth.softmax_weights(rng, T, k)
+    out = mq.moe_scatter_combine(y, p2s, dev(w), out_dtype=torch.float32)
+    rows = np.r_[0:64, T - 64:T, rng.integers(0, T, 256)]
+    y_h = host(y)
+    ref = oracle.scatter_combine(y_h, host(p2s), w)
+    assert_rows_close(host(out)[rows], ref[rows], what=f"combine streaming {ydt}")
