@@ -365,8 +365,8 @@ __global__ __launch_bounds__(64 * fd::kWaves) void fp8_decode(
     auto issue = [&](int g) __attribute__((always_inline)) {
       const uint32_t sl = lb + (uint32_t)((g % fd::kDepth) * fd::kSlot);
       const int64_t ko = (int64_t)g * 128;
-      dma16(sw0 + ko, sl + fd::kW);
-      dma16(sw1 + ko, sl + fd::kW + 1024);
+      dma16_nt(sw0 + ko, sl + fd::kW);
+      dma16_nt(sw1 + ko, sl + fd::kW + 1024);
       dma16(sx + ko, sl + fd::kX);
       dma4(lane == fd::kM ? ssw + g : ssa + (int64_t)g * rows_a, sl + fd::kS);
     };

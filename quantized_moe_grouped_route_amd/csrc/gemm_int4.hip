@@ -535,7 +535,7 @@ __global__ __launch_bounds__(64 * dd::kWaves) void int4_decode(
       const uint32_t sl = lb + (uint32_t)((g % dd::kDepth) * dd::kSlot);
       const int64_t ko = (int64_t)g * (dd::kGroupK / 2);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) dma16(sw[c] + ko, sl + dd::kW + c * 1024);
+      for (int c = 0; c < 4; ++c) dma16_nt(sw[c] + ko, sl + dd::kW + c * 1024);
       dma16(sx + ko, sl + dd::kX);
       if (g == 0) dma4(ss, sl + dd::kS);
     };

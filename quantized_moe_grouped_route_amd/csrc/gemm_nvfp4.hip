@@ -588,15 +588,15 @@ __global__ __launch_bounds__(dc::kWaves * 64) void nvfp4_decode(
         ++is_sc;
       }
       const int64_t o = (int64_t)is_st * w_adv;
-      dma16(wsrc[0] + o, l);
-      dma16(wsrc[1] + o, l + 1024);
-      dma16(wsrc[2] + o, l + 2048);
-      dma16(wsrc[3] + o, l + 3072);
+      dma16_nt(wsrc[0] + o, l);
+      dma16_nt(wsrc[1] + o, l + 1024);
+      dma16_nt(wsrc[2] + o, l + 2048);
+      dma16_nt(wsrc[3] + o, l + 3072);
     } else {
       ops = 4;
       const int64_t o = (int64_t)is_st * w_adv;
-      dma16(wsrc[0] + o, l);
-      dma16(wsrc[2] + o, l + 1024);
+      dma16_nt(wsrc[0] + o, l);
+      dma16_nt(wsrc[2] + o, l + 1024);
       dma16(sx + (int64_t)is_st * 256, l + 2048);
       dma4(ss + (int64_t)is_st * s_adv, l + 3072);
     }

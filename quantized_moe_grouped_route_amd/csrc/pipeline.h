@@ -39,6 +39,14 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "s"(lds) : "memory", "m0");
 }
+// The same with the nontemporal hint, for bytes read once (the weight
+// streams of the decode schedules): measured 7-15 % faster there than the
+// plain copy (NVFP4 FC1 of 8 tokens 166 -> 141 us, FP8 decode 290 -> 253 us,
+// INT4 FC1 of 8 tokens 85 -> 77 us).
+__device__ __forceinline__ void dma16_nt(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :: "v"(src), "s"(lds) : "memory", "m0");
+}
 // 4 bytes per lane to LDS at byte address `lds` + 4 * lane.
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"

@@ -2,8 +2,12 @@
 // resources the grouped GEMMs are bound by, measured on the box instead of
 // taken from the data sheet.
 //   moeq_peak_read  streams a buffer from HBM with 16-byte nontemporal loads
-//                   (every byte read once), the bound of the weight-streaming
-//                   decode schedules.
+//                   into registers (every byte read once).
+//   moeq_peak_read_lds  streams it with nontemporal direct-to-LDS copies, 16
+//                   in flight per wave, each wave its own contiguous share,
+//                   the way the weight-streaming decode schedules read; the
+//                   faster of the two is the bound (measured 7.0 against
+//                   6.0 TB/s for the register loads).
 //   moeq_peak_mfma  runs back-to-back MFMAs of one kind on register operands
 //                   (no memory traffic), the bound of the tiled schedules.
 // Each call only enqueues one kernel on `stream`; the caller times it.
@@ -35,6 +39,30 @@ __global__ __launch_bounds__(256) void read_stream(const u32x4* __restrict__ src
   }
   for (; i < n16; i += stride) x ^= __builtin_nontemporal_load(src + i);
   sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = x.x ^ x.y ^ x.z ^ x.w;
+}
+
+// Wave w of the W in the grid copies its own contiguous share of the
+// buffer, 1 KB at a time, into a 16-slot LDS ring of its own (W concurrent
+// sequential streams, as the decode schedules' waves each stream their own
+// rows); a slot is reused once the copy 16 before it has landed (vmcnt 15).
+// The LDS bytes are never read.
+__global__ __launch_bounds__(256) void read_lds(const uint8_t* __restrict__ src, int64_t n1k) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[4][16][1024];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t W = (int64_t)gridDim.x * 4, w = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t per = (n1k + W - 1) / W;
+  const int64_t c0 = w * per, c1 = c0 + per < n1k ? c0 + per : n1k;
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&ring[wv][0][0]);
+  int slot = 0, issued = 0;
+  for (int64_t c = c0; c < c1; ++c) {
+    if (issued >= 16) __builtin_amdgcn_s_waitcnt((15 & 15) | (7 << 4) | (15 << 8) | ((15 >> 4) << 14));
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :: "v"(src + c * 1024 + lane * 16), "s"(base + slot * 1024) : "memory", "m0");
+    slot = (slot + 1) & 15;
+    ++issued;
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
 // Kinds: 0 int8 32x32x32, 1 fp8 e4m3 32x32x64, 2 bf16 32x32x16,
@@ -99,6 +127,15 @@ int moeq_peak_read(const void* src, int64_t bytes, void* sink, int grid, void* s
   if (!src || !sink || bytes <= 0 || bytes % 16 || grid <= 0) return 1;
   hipLaunchKernelGGL(read_stream, dim3(grid), dim3(256), 0, (hipStream_t)stream,
                      static_cast<const u32x4*>(src), bytes / 16, static_cast<unsigned*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// Reads `bytes` (a multiple of 1024) from `src` with direct-to-LDS copies;
+// grid workgroups of 4 waves.
+int moeq_peak_read_lds(const void* src, int64_t bytes, int grid, void* stream) {
+  if (!src || bytes <= 0 || bytes % 1024 || grid <= 0) return 1;
+  hipLaunchKernelGGL(read_lds, dim3(grid), dim3(256), 0, (hipStream_t)stream, static_cast<const uint8_t*>(src),
+                     bytes / 1024);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
