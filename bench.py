@@ -1,6 +1,6 @@
 """Throughput of the quantized MoE grouped-GEMM path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload {0,1,...,8}]
+    python bench.py [--steps K] [--warmup W] [--workload {0,1,...,9}] [--cold-steps C]
     python bench.py --peaks      (the chip's sustained HBM read rate and
                                   MFMA rate per dtype, measured on the box)
 
@@ -24,12 +24,16 @@ synthetic input already resident in HBM:
      x + FC1 (SiLU) + per-row int4 of h + FC2 + combine
   7  one-shot NVFP4 weight repack of 2's gate+up weights (E=256, 4096 rows,
      K=7168) from the up-first, 128x4-swizzled-scale layout of megamoe_rm.cu
+  9  the W4A4 layer of 8 at one 8-token decode step (weight-streaming
+     schedule)
 Prints ONE JSON line: whole-path throughput (and the p10 / p50 / p90 of the
 per-step times), the dominant kernel's roofline fraction (its launches timed
 with HIP events on the launch stream inside the timed region) against the
 published peak and against the peak measured on the box (--peaks, summarized
 in profiles/peaks_mi355x.txt), and the CPU oracle's throughput on the host
-as a reported baseline.
+as a reported baseline.  The steps run back to back with their inputs
+resident; `cold_cache` adds C steps timed one by one after the caches were
+evicted.
 """
 from __future__ import annotations
 
@@ -558,7 +562,7 @@ def cpu_baseline(idx: int, d, budget_s: float = 10.0):
 def profile_commands(idx: int, pdir: str):
     """The rocprofv3 runs whose outputs --summarize-profiles reduces."""
     run = f"python3 bench.py --workload {idx}"
-    short = f"{run} --steps 3 --warmup 1 --no-cpu-baseline"
+    short = f"{run} --steps 3 --warmup 1 --cold-steps 0 --no-cpu-baseline"
     copy = "python3 bench.py --copy-calibration"
     pmc = "rocprofv3 --pmc {c} -d {d} -o run --output-format csv -- {r}"
     return {
@@ -770,6 +774,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=4, choices=sorted(__import__("synth").WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="steps timed one by one after evicting the caches (a 1 GiB device read "
+                         "between steps, outside each step's events), reported as cold_cache; "
+                         "0 skips them")
     ap.add_argument("--act", choices=("bf16", "f16"), default="f16",
                     help="NVFP4 workloads: GEMMs on the bf16 activations, or on binary16 activations "
                          "(the bf16 input cast once, h kept in binary16; half the dequant work)")
@@ -839,13 +847,35 @@ def main():
     # bounded spin kernel holds the stream while the host enqueues every
     # timed step, so the events time the device's work, not the gaps of
     # the Python launches.  The spin ends before t0 is recorded.
-    spin_ms = 2.0 + 1.5 * args.steps * 1e3 * float(np.median(host_s) if host_s else 1e-3)
+    host_step_ms = 1e3 * float(np.median(host_s) if host_s else 1e-3)
+    spin_ms = 2.0 + 1.5 * args.steps * host_step_ms
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     c0.record()
     torch.cuda._sleep(1 << 20)
     c1.record()
     torch.cuda.synchronize()
     cycles_per_ms = (1 << 20) / max(c0.elapsed_time(c1), 1e-3)
+
+    # Cold-cache steps, before the timed region so that a trace's last K
+    # launches are still the timed ones.  Each step follows a 1 GiB device
+    # read, which evicts the L2s and the 256 MB Infinity Cache (a read, so no
+    # dirty lines are written back during the step), then a spin that holds
+    # the stream while the host enqueues the step; its events open after both.
+    cold = None
+    if args.cold_steps > 0:
+        flush_src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        flush_dst = torch.empty((), dtype=torch.float32, device="cuda")
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.cold_steps)]
+        for a, z in cev:
+            torch.sum(flush_src, dim=None, out=flush_dst)
+            torch.cuda._sleep(int((0.2 + 2.0 * host_step_ms) * cycles_per_ms))
+            a.record()
+            wl.step()
+            z.record()
+        torch.cuda.synchronize()
+        cold_ms = np.array([a.elapsed_time(z) for a, z in cev])
+        del flush_src, flush_dst
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
@@ -871,9 +901,16 @@ def main():
 
     cfg = wl.cfg
     if args.workload in (2, 5, 6, 7, 9):
-        value, unit = wl.weight_bytes / (ms * 1e-3) / 1e9, "GB/s"
+        rate, unit = (lambda t: wl.weight_bytes / (t * 1e-3) / 1e9), "GB/s"
     else:
-        value, unit = wl.flops / (ms * 1e-3) / 1e12, "TFLOP/s"
+        rate, unit = (lambda t: wl.flops / (t * 1e-3) / 1e12), "TFLOP/s"
+    value = rate(ms)
+    if args.cold_steps > 0:
+        c50 = float(np.percentile(cold_ms, 50))
+        cold = {"steps": args.cold_steps,
+                "ms_per_step_p10_p50_p90": [round(float(np.percentile(cold_ms, q)), 5) for q in (10, 50, 90)],
+                "value_at_p50": round(rate(c50), 3), "unit": unit,
+                "flush": "1 GiB device read before each step, outside the step's events"}
     work, wunit = wl.dominant_work()
     tag, srcs, bound, peak = wl.dom
     if wunit == "byte":
@@ -905,6 +942,8 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
            "data": "synthetic (seeded generators, shapes of the workload)", "config": config,
            "roofline": roof}
+    if cold:
+        rec["cold_cache"] = cold
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.workload, wl.d)
     rec["host_wall_s_incl_spin"] = round(wall, 4)
