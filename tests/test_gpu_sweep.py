@@ -1,11 +1,12 @@
-"""Seeded random sweep of whole layer steps: route prep -> one grouped GEMM ->
+"""Seeded random sweeps.  Whole layer steps: route prep -> one grouped GEMM ->
 weighted combine, over random shapes (ragged, single-expert, single-token),
 routings with -1 and out-of-range ids, activation-row modes, output types,
 NVFP4 layouts and schedules.  Each step is compared with the oracle: the
 routing tables and raw INT4 accumulators exactly, each GEMM's f32 output
 within max_j |gpu - oracle| <= 2e-3 * ||oracle_row||_2 and its 16-bit
 outputs as that output rounded, the combine against the oracle's combine of
-the stored GEMM output."""
+the stored GEMM output.  Also the INT4 activation quantizer and the NVFP4
+weight repack over random shapes, types and layouts, bit-exact."""
 import numpy as np
 import pytest
 import torch
@@ -194,3 +195,55 @@ def test_sweep_nvfp4_layer_step(case):
                                      x_dtype=c["xdt"], sf_layout=c["sfl"], w_layout=c["wl"])["y"]
     y = _check_gemm(call, ref, c["odt"], "nvfp4 sweep")
     _check_combine(y, ref.shape[0], p2s, ref_t, d["topk_weights"], "nvfp4 sweep")
+
+
+def _quant_case(i):
+    rng = np.random.default_rng(3400 + i)
+    rows = int(rng.choice([1, 2, 9, 64, 257]))
+    K = 16 * int(rng.choice([1, 3, 8, 65, 300, 1024, 1100]))
+    dt = str(rng.choice(["f16", "bf16", "f32"]))
+    scale = float(rng.choice([1e-3, 1.0, 300.0]))
+    return dict(rows=rows, K=K, dt=dt, scale=scale, seed=3400 + i)
+
+
+@pytest.mark.parametrize("case", [_quant_case(i) for i in range(N_CASES)],
+                         ids=lambda c: "rows{rows}-K{K}-{dt}-x{scale}".format(**c))
+def test_sweep_int4_quantizer(case):
+    # per-row int4 codes and scales, bit-exact; some rows all zero, some with
+    # a single nonzero element
+    c = case
+    rng = np.random.default_rng(c["seed"])
+    x = (rng.standard_normal((c["rows"], c["K"])) * c["scale"]).astype(np.float32)
+    x[rng.random(c["rows"]) < 0.1] = 0.0
+    one = rng.random(c["rows"]) < 0.1
+    x[one] = 0.0
+    x[one, rng.integers(0, c["K"], size=int(one.sum()))] = -c["scale"]
+    xt = torch.from_numpy(x).to(DT[c["dt"]]).cuda()
+    q, s = mq.quantize_int4_rows(xt)
+    ref_q, ref_s = oracle.quantize_int4_rows(xt.float().cpu().numpy())
+    assert np.array_equal(host(q), ref_q)
+    assert np.array_equal(host(s).astype(np.float32), ref_s)
+
+
+def _repack_case(i):
+    rng = np.random.default_rng(3500 + i)
+    E = int(rng.choice([1, 2, 3]))
+    N = 128 * int(rng.integers(1, 4))
+    K = 64 * int(rng.choice([1, 2, 3, 5, 8]))
+    swap = bool(rng.integers(0, 2)) and N % 256 == 0
+    sfl = str(rng.choice(["rows", "quads"]))
+    wl = str(rng.choice(["rows", "tiled"]))
+    return dict(E=E, N=N, K=K, swap=swap, sfl=sfl, wl=wl, seed=3500 + i)
+
+
+@pytest.mark.parametrize("case", [_repack_case(i) for i in range(N_CASES)],
+                         ids=lambda c: "E{E}-N{N}-K{K}-swap{swap}-{sfl}-{wl}".format(**c))
+def test_sweep_nvfp4_repack(case):
+    # a pure byte permutation: bit-exact against the oracle's layouts
+    c = case
+    d = synth.nvfp4_stored_weights(c["seed"], c["E"], c["N"], c["K"])
+    w_out, sf_out = mq.nvfp4_repack(dev(d["w"]), dev(d["sf"]), swap_halves=c["swap"],
+                                    sf_layout=c["sfl"], w_layout=c["wl"])
+    ref_w, ref_sf = oracle.repack_nvfp4(d["w"], d["sf"], c["swap"], out_layout=c["sfl"], w_layout=c["wl"])
+    assert np.array_equal(host(w_out), ref_w)
+    assert np.array_equal(host(sf_out), ref_sf)
