@@ -139,6 +139,8 @@ int32_t moeq_abi_version(void);
  *                   (may be NULL when that is 0); contents on entry ignored
  * Requires T >= 0, 1 <= topk <= 64, 1 <= E <= 1024, T*topk < 2^31.
  * T == 0 writes expert_offsets = 0 and n_invalid = 0.
+ * moe_route_prep_workspace_bytes returns 0 for arguments outside these
+ * ranges (the call itself then gives MOEQ_EINVAL).
  * ---------------------------------------------------------------------- */
 size_t moe_route_prep_workspace_bytes(int64_t T, int32_t topk, int32_t E); /* host */
 

@@ -6,6 +6,7 @@
 // reported as status codes because the boundary is C.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -33,17 +34,19 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 constexpr int kMaxE = 1024;
 constexpr int kMaxTopk = 64;
 
+// Compute units of the current device, looked up once per device.  Calls
+// may come from several host threads at once; each stores the same value.
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 moeq_status hip_status(hipError_t e, const char* what) {
@@ -112,8 +115,11 @@ const char* moeq_last_error(void) { return g_err.c_str(); }
 int32_t moeq_abi_version(void) { return 3; }
 
 size_t moe_route_prep_workspace_bytes(int64_t T, int32_t topk, int32_t E) {
-  if (T < 0 || topk < 1 || E < 1) return 0;
-  return moeq::route_workspace_bytes(T * (int64_t)topk, E);
+  // T is bounded before the product so that T*topk cannot overflow
+  if (T < 0 || T >= (int64_t(1) << 31) || topk < 1 || topk > kMaxTopk || E < 1 || E > kMaxE) return 0;
+  const int64_t P = T * (int64_t)topk;
+  if (P >= (int64_t(1) << 31)) return 0;
+  return moeq::route_workspace_bytes(P, E);
 }
 
 moeq_status moe_route_prep(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
@@ -121,7 +127,7 @@ moeq_status moe_route_prep(const int32_t* topk_ids, int64_t T, int32_t topk, int
                            int32_t* pair_to_sorted, int32_t* n_invalid, void* workspace,
                            size_t workspace_bytes, void* stream) {
   const char* fn = "moe_route_prep";
-  if (T < 0) return fail(MOEQ_EINVAL, "%s: T=%lld < 0", fn, (long long)T);
+  if (T < 0 || T >= (int64_t(1) << 31)) return fail(MOEQ_EINVAL, "%s: T=%lld outside [0, 2^31)", fn, (long long)T);
   if (topk < 1 || topk > kMaxTopk) return fail(MOEQ_EINVAL, "%s: topk=%d outside [1, %d]", fn, topk, kMaxTopk);
   if (E < 1 || E > kMaxE) return fail(MOEQ_EINVAL, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
   const int64_t P = T * (int64_t)topk;
@@ -144,7 +150,7 @@ moeq_status moe_route_prep_noalloc(const int32_t* topk_ids, int64_t T, int32_t t
                                    int32_t* pair_to_sorted, int32_t* n_invalid, void* stream) {
   const char* fn = "moe_route_prep_noalloc";
   static_assert(moeq::kRouteNoallocScratchBytes == MOEQ_ROUTE_NOALLOC_SCRATCH_BYTES, "header and library agree");
-  if (T < 0) return fail(MOEQ_EINVAL, "%s: T=%lld < 0", fn, (long long)T);
+  if (T < 0 || T >= (int64_t(1) << 31)) return fail(MOEQ_EINVAL, "%s: T=%lld outside [0, 2^31)", fn, (long long)T);
   if (topk < 1 || topk > kMaxTopk) return fail(MOEQ_EINVAL, "%s: topk=%d outside [1, %d]", fn, topk, kMaxTopk);
   if (E < 1 || E > kMaxE) return fail(MOEQ_EINVAL, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
   const int64_t P = T * (int64_t)topk;
@@ -264,7 +270,7 @@ moeq_status moe_scatter_combine(const void* y, moeq_dtype y_dtype, const int32_t
                                 const float* topk_weights, int64_t T, int32_t topk, int64_t N,
                                 moeq_dtype out_dtype, void* out, void* stream) {
   const char* fn = "moe_scatter_combine";
-  if (T < 0) return fail(MOEQ_EINVAL, "%s: T=%lld < 0", fn, (long long)T);
+  if (T < 0 || T >= (int64_t(1) << 31)) return fail(MOEQ_EINVAL, "%s: T=%lld outside [0, 2^31)", fn, (long long)T);
   if (topk < 1 || topk > kMaxTopk) return fail(MOEQ_EINVAL, "%s: topk=%d outside [1, %d]", fn, topk, kMaxTopk);
   if (N <= 0 || N > (1 << 24)) return fail(MOEQ_EINVAL, "%s: N=%lld out of range", fn, (long long)N);
   if (N % 8 != 0) return fail(MOEQ_EALIGN, "%s: N=%lld must be a multiple of 8", fn, (long long)N);
@@ -285,7 +291,7 @@ moeq_status moe_scatter_combine(const void* y, moeq_dtype y_dtype, const int32_t
 moeq_status moe_sum_pairs(const void* y_pairs, moeq_dtype y_dtype, const int32_t* pair_to_sorted, int64_t T,
                           int32_t topk, int64_t N, moeq_dtype out_dtype, void* out, void* stream) {
   const char* fn = "moe_sum_pairs";
-  if (T < 0) return fail(MOEQ_EINVAL, "%s: T=%lld < 0", fn, (long long)T);
+  if (T < 0 || T >= (int64_t(1) << 31)) return fail(MOEQ_EINVAL, "%s: T=%lld outside [0, 2^31)", fn, (long long)T);
   if (topk < 1 || topk > kMaxTopk) return fail(MOEQ_EINVAL, "%s: topk=%d outside [1, %d]", fn, topk, kMaxTopk);
   if (N <= 0 || N > (1 << 24)) return fail(MOEQ_EINVAL, "%s: N=%lld out of range", fn, (long long)N);
   if (N % 8 != 0) return fail(MOEQ_EALIGN, "%s: N=%lld must be a multiple of 8", fn, (long long)N);

@@ -90,6 +90,35 @@ static int run_host(void) {
   s = grouped_gemm_qint4(buf, (const float*)buf, 8, MOEQ_AROW_TOKEN, buf, (const float*)buf, ids, ids, 8, 2, 4,
                          64, 131072, MOEQ_ACT_NONE, MOEQ_F32, buf, MOEQ_SCHED_AUTO, NULL);
   printf("int4_k131072 %d\n", (int)s);
+  /* T*topk beyond int64: T is rejected before the product is formed */
+  const int64_t huge = (int64_t)1 << 62;
+  printf("ws_huge %zu\n", moe_route_prep_workspace_bytes(huge, 4, 256));
+  s = moe_route_prep(ids, huge, 4, 4, (int32_t*)buf, (int32_t*)buf, (int32_t*)buf, (int32_t*)buf, NULL, 0, NULL);
+  printf("route_huge %d\n", (int)s);
+  s = moe_route_prep_noalloc(ids, huge, 4, 4, (int32_t*)buf, (int32_t*)buf, (int32_t*)buf, (int32_t*)buf, NULL);
+  printf("noalloc_huge %d\n", (int)s);
+  s = moe_scatter_combine(buf, MOEQ_F32, ids, (const float*)buf, huge, 4, 64, MOEQ_F32, buf, NULL);
+  printf("combine_huge %d\n", (int)s);
+  s = moe_sum_pairs(buf, MOEQ_F32, ids, huge, 4, 64, MOEQ_F32, buf, NULL);
+  printf("sum_pairs_huge %d\n", (int)s);
+  /* FP8: N not a multiple of 128 */
+  s = grouped_gemm_qfp8_block(buf, (const float*)buf, 8, MOEQ_AROW_TOKEN, buf, (const float*)buf, ids, ids, 8, 1,
+                              1, 64, 256, MOEQ_BF16, buf, MOEQ_SCHED_AUTO, NULL);
+  printf("fp8_n64 %d\n", (int)s);
+  /* NVFP4: activations must be bf16 or f16 */
+  s = grouped_gemm_qnvfp4(buf, MOEQ_F32, 8, MOEQ_AROW_TOKEN, buf, MOEQ_W_ROWS, buf, MOEQ_SF_ROWS,
+                          (const float*)buf, ids, ids, 8, 2, 4, 64, 256, MOEQ_ACT_NONE, 0.0f, NULL, MOEQ_BF16, buf,
+                          NULL, MOEQ_SCHED_AUTO, NULL);
+  printf("nvfp4_x_f32 %d\n", (int)s);
+  /* quantizer: K not a multiple of 16 */
+  s = moe_quantize_int4(buf, MOEQ_F16, 8, 40, buf, (float*)buf, NULL);
+  printf("quant_k40 %d\n", (int)s);
+  /* repack: an output overlapping an input */
+  s = moe_nvfp4_repack(buf, buf + 2048, 1, 128, 64, 0, MOEQ_W_ROWS, MOEQ_SF_ROWS, buf, buf + 3072, NULL);
+  printf("repack_overlap %d\n", (int)s);
+  /* cast: a partial overlap of x and y */
+  s = moe_cast_bf16_to_f16((const uint16_t*)buf, 64, (uint16_t*)(buf + 16), NULL);
+  printf("cast_overlap %d\n", (int)s);
   /* combine: N not a multiple of 8 */
   s = moe_scatter_combine(buf, MOEQ_F32, ids, (const float*)buf, 4, 2, 12, MOEQ_F32, buf, NULL);
   printf("combine_n12 %d\n", (int)s);

@@ -51,6 +51,11 @@ def test_workspace_bytes(L):
     assert L.moe_route_prep_workspace_bytes(64, 2, 4) == 0          # one chunk: fused kernel
     assert L.moe_route_prep_workspace_bytes(4096, 8, 256) == 32 * 257 * 4
     assert L.moe_route_prep_workspace_bytes(-1, 2, 4) == 0
+    # out-of-range sizes give 0, with T bounded before T*topk is formed
+    assert L.moe_route_prep_workspace_bytes(2 ** 62, 4, 256) == 0
+    assert L.moe_route_prep_workspace_bytes(2 ** 28, 8, 256) == 0
+    assert L.moe_route_prep_workspace_bytes(4096, 65, 256) == 0
+    assert L.moe_route_prep_workspace_bytes(4096, 8, 1025) == 0
 
 
 def _route(L, T=4, topk=2, E=4, ids=A16, offs=A16, srt=A16, p2s=A16, ninv=A16, ws=None, wsb=0):
@@ -63,6 +68,7 @@ def _route(L, T=4, topk=2, E=4, ids=A16, offs=A16, srt=A16, p2s=A16, ninv=A16, w
     (dict(offs=None), mq.EINVAL), (dict(srt=ODD), mq.EALIGN),
     (dict(T=5000, topk=8, E=16), mq.EINVAL),            # needs a workspace
     (dict(T=2 ** 28, topk=8), mq.EINVAL),               # T*topk >= 2^31
+    (dict(T=2 ** 62, topk=4), mq.EINVAL),               # T*topk would overflow int64
 ])
 def test_route_prep_rejects(L, kw, status):
     assert _route(L, **kw) == status
@@ -148,7 +154,7 @@ def _combine(L, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(N=12), mq.EALIGN), (dict(T=-2), mq.EINVAL), (dict(topk=0), mq.EINVAL),
     (dict(yd=mq.I32), mq.EUNSUPPORTED), (dict(od=7), mq.EUNSUPPORTED), (dict(y=None), mq.EINVAL),
-    (dict(out=ODD), mq.EALIGN),
+    (dict(out=ODD), mq.EALIGN), (dict(T=2 ** 28, topk=8), mq.EINVAL), (dict(T=2 ** 62, topk=4), mq.EINVAL),
 ])
 def test_combine_rejects(L, kw, status):
     assert _combine(L, **kw) == status
@@ -264,7 +270,7 @@ def _sum_pairs(L, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(N=12), mq.EALIGN), (dict(T=-2), mq.EINVAL), (dict(topk=0), mq.EINVAL),
     (dict(yd=mq.I32), mq.EUNSUPPORTED), (dict(od=7), mq.EUNSUPPORTED), (dict(y=None), mq.EINVAL),
-    (dict(p2s=None), mq.EINVAL), (dict(out=ODD), mq.EALIGN),
+    (dict(p2s=None), mq.EINVAL), (dict(out=ODD), mq.EALIGN), (dict(T=2 ** 62, topk=4), mq.EINVAL),
 ])
 def test_sum_pairs_rejects(L, kw, status):
     assert _sum_pairs(L, **kw) == status
@@ -287,6 +293,7 @@ def test_noalloc_route_rejects_before_any_device_call(L):
     assert f(A16, -1, 2, 4, A16, A16, A16, A16, None) == mq.EINVAL
     assert f(A16, 4, 0, 4, A16, A16, A16, A16, None) == mq.EINVAL
     assert f(A16, 4, 2, 4, A16, ODD, A16, A16, None) == mq.EALIGN
+    assert f(A16, 2 ** 62, 4, 4, A16, A16, A16, A16, None) == mq.EINVAL
     chunks = mq.ROUTE_NOALLOC_SCRATCH_BYTES // ((256 + 1) * 4)
     assert f(A16, chunks * 1024 + 1, 1, 256, A16, A16, A16, A16, None) == mq.EINVAL
     assert b"fixed" in L.moeq_last_error()

@@ -49,6 +49,36 @@ def test_c_consumer_host_calls():
     assert got["int4_k131072"] == "1"
     assert got["combine_n12"] == "2"
     assert "multiple of 8" in got["last_error"]
+    # T = 2^62 with topk = 4: rejected (MOEQ_EINVAL) without forming T*topk
+    assert got["ws_huge"] == "0"
+    for key in ("route_huge", "noalloc_huge", "combine_huge", "sum_pairs_huge"):
+        assert got[key] == "1", key
+    # MOEQ_EUNSUPPORTED = 3
+    assert got["fp8_n64"] == "2" and got["nvfp4_x_f32"] == "3" and got["quant_k40"] == "2"
+    assert got["repack_overlap"] == "1" and got["cast_overlap"] == "1"
+
+
+def test_c_consumer_host_calls_under_sanitizers():
+    """The library's host layer (argument checks, size arithmetic, error
+    text) rebuilt by g++ under AddressSanitizer and UndefinedBehaviorSanitizer
+    (tests/c_abi/Makefile, target sanitize) runs the host calls with no
+    report and prints exactly what the ordinary build prints."""
+    import shutil
+    import quantized_moe_grouped_route_amd as mq
+    kobj = os.path.join(os.path.dirname(mq.LIB_PATH), "_build", "route.hip.o")
+    if not (shutil.which("gcc") and shutil.which("g++") and os.path.exists(kobj)):
+        pytest.skip("needs gcc/g++ and the kernel objects of a library build")
+    r = subprocess.run(["make", "-B", "-s", "-C", CDIR, "sanitize"], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    env = dict(os.environ, ASAN_OPTIONS="halt_on_error=1:detect_leaks=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    san = subprocess.run([os.path.join(CDIR, "moeq_consumer_san"), "host"], capture_output=True, text=True,
+                         timeout=60, env=env)
+    assert san.returncode == 0, san.stderr
+    assert "runtime error" not in san.stderr and "Sanitizer" not in san.stderr, san.stderr
+    plain = subprocess.run([consumer(), "host"], capture_output=True, text=True, timeout=60)
+    assert plain.returncode == 0, plain.stderr
+    assert san.stdout == plain.stdout
 
 
 @pytest.mark.gpu
