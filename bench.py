@@ -2,7 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload {0,1,...,9}] [--cold-steps C]
     python bench.py --peaks      (the chip's sustained HBM read rate and
-                                  MFMA rate per dtype, measured on the box)
+                                  MFMA rate per dtype, measured on this GPU)
 
 One step is one pass of the whole hot path over one batch of seeded
 synthetic input already resident in HBM:
@@ -29,7 +29,7 @@ synthetic input already resident in HBM:
 Prints ONE JSON line: whole-path throughput (and the p10 / p50 / p90 of the
 per-step times), the dominant kernel's roofline fraction (its launches timed
 with HIP events on the launch stream inside the timed region) against the
-published peak and against the peak measured on the box (--peaks, summarized
+published peak and against the peak measured on this GPU (--peaks, summarized
 in profiles/peaks_mi355x.txt), and the CPU oracle's throughput on the host
 as a reported baseline.  The steps run back to back with their inputs
 resident; `cold_cache` adds C steps timed one by one after the caches were
@@ -171,7 +171,7 @@ def peak_operands(rng, name, nbytes):
 
 
 def measured_peak(key):
-    """The committed on-box measurement of one peak, or None."""
+    """The committed on-GPU measurement of one peak, or None."""
     if not os.path.exists(PEAKS_FILE):
         return None
     for line in open(PEAKS_FILE):

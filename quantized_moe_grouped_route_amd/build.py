@@ -4,7 +4,7 @@
 
 Compiles every source under csrc/ with hipcc for gfx950 and links the
 shared library next to this file; also builds libmoeq_peaks.so from
-probes/ (the on-box peak measurements bench.py --peaks runs; the library
+probes/ (the on-GPU peak measurements bench.py --peaks runs; the library
 itself never uses it).  Packed-FP32 VALU instructions are disabled for all
 device code.
 """

@@ -1,6 +1,6 @@
 // Peak probes for one MI355X (gfx950): what the chip sustains for the two
-// resources the grouped GEMMs are bound by, measured on the box instead of
-// taken from the data sheet.
+// resources the grouped GEMMs are bound by, measured on the GPU at hand instead
+// of taken from the data sheet.
 //   moeq_peak_read  streams a buffer from HBM with 16-byte nontemporal loads
 //                   into registers (every byte read once).
 //   moeq_peak_read_lds  streams it with nontemporal direct-to-LDS copies, 16

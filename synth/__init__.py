@@ -273,16 +273,17 @@ WORKLOADS = {
     3: dict(name="nvfp4_w4a16_prefill_T4096_zipf", kind="nvfp4", T=4096, E=256, k=8, H=7168,
             I=2048, routing="zipf"),
     4: dict(name="w4a4_int4_mixtral_T8192", kind="int4", T=8192, E=8, k=2, H=4096, I=14336),
-    # per-row int4 quantization of config 4's FC1 output h (T*k rows of I fp16)
+    # per-row int4 quantization of the Mixtral-sized W4A4 layer's FC1 output h
+    # (T*k rows of I fp16)
     5: dict(name="int4_quantize_rows_16384x14336_f16", kind="quant", rows=16384, K=14336),
     # the FP8 block-scaled kernel under routing: one 8-token decode step of a
     # DeepSeek-V3-shaped expert projection (gate+up, N = 2I = 4096, K = H)
     6: dict(name="fp8_block_moe_decode_T8", kind="fp8", T=8, E=256, k=8, N=4096, K=7168),
-    # one-shot repack of workload 2's gate+up weights (E=256 experts of
+    # one-shot repack of the NVFP4 decode workload's gate+up weights (E=256 experts of
     # 2I = 4096 rows, K = H = 7168) from the up-first, 128x4-swizzled-scale
     # layout of megamoe_rm.cu
     7: dict(name="nvfp4_repack_w13_E256_N4096_K7168", kind="repack", E=256, N=4096, K=7168, swap=1),
-    # the complete W4A4 layer at config 4's sizes from fp16 activations:
+    # the complete Mixtral-sized W4A4 layer from fp16 activations:
     # per-token int4 of x, FC1 (SiLU), per-row int4 of h, FC2, combine
     8: dict(name="w4a4_int4_chain_mixtral_T8192", kind="int4chain", T=8192, E=8, k=2, H=4096, I=14336),
     # the same layer for one 8-token decode step: 16 routed rows over the 8

@@ -85,7 +85,7 @@ def _token_sample(off, srt, k, T, n_rand, seed):
     return np.array(list(dict.fromkeys(int(t) for t in pick)))
 
 
-# ------------------------------------------------------------------ config 0
+# ------------------------------------------------------------------ W4A4 tiny (64 tokens, E=4)
 def test_workload0_w4a4_tiny_end_to_end():
     wl = _run(0)
     off, srt, p2s, _ = _check_route(wl)
@@ -98,7 +98,7 @@ def test_workload0_w4a4_tiny_end_to_end():
     assert np.array_equal(host(acc), ref["acc"])
 
 
-# ------------------------------------------------------------------ config 1
+# ------------------------------------------------------------------ FP8 dense 1024x4096x7168
 def test_workload1_fp8_dense_every_output():
     wl = _run(1)
     off, srt, _, _ = _check_route(wl)
@@ -107,7 +107,7 @@ def test_workload1_fp8_dense_every_output():
     assert_rows_close(host(wl.y), ref, what="fp8 1024x4096x7168")
 
 
-# ------------------------------------------------------------------ NVFP4 (configs 2, 3)
+# ------------------------------------------------------------------ NVFP4 decode (8 tokens) and Zipf prefill (4096)
 def _nvfp4_rows_layout(wl):
     """The workload's weights in the oracle's row-major layouts (one
     conversion per test instead of one per oracle call)."""
@@ -210,7 +210,7 @@ def test_nvfp4_workloads_with_fc2_pair_epilogue(idx):
     assert_rows_close(host(wl.out), oracle.sum_pairs(yp, p2s, wl.T, wl.k), what="pair sum")
 
 
-# ------------------------------------------------------------------ config 4
+# ------------------------------------------------------------------ W4A4 Mixtral-sized (8192 tokens, E=8)
 def test_workload4_w4a4_mixtral_every_row():
     wl = _run(4)
     off, srt, p2s, _ = _check_route(wl)
