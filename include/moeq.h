@@ -21,8 +21,9 @@
  *     on the current HIP device) unless marked "host".  The caller owns all
  *     memory, scratch included (route prep's workspace, the NVFP4 work
  *     queue); the library allocates nothing and never synchronizes the host
- *     with the device.  Its one piece of state is moe_route_prep_noalloc's
- *     fixed per-device scratch.
+ *     with the device.  Its state is moe_route_prep_noalloc's fixed
+ *     per-device scratch and a per-device cache of the compute-unit count
+ *     (read once from the HIP runtime; safe to fill from several threads).
  *   - Every call only validates its arguments on the host and enqueues
  *     kernels on `stream` (a hipStream_t; NULL = the null stream).  Results
  *     are visible to later work on that stream.
