@@ -70,7 +70,10 @@ __device__ __forceinline__ i32x16_a4 ld_uniform_i32x16(const int* p) { return *(
 __device__ __forceinline__ v4i lo_nibbles(u32x4 p) { return __builtin_bit_cast(v4i, (p << 4) & 0xF0F0F0F0u); }
 __device__ __forceinline__ v4i hi_nibbles(u32x4 p) { return __builtin_bit_cast(v4i, p & 0xF0F0F0F0u); }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// g * sigmoid(g) with the hardware reciprocal (about 1 ulp) in place of an
+// IEEE division: the epilogue's largest VALU cost, and its error stays far
+// below the output's own rounding.
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // LDS tiles: rows of 64 bytes (four 16-byte chunks), chunk c of row r at
 // position c ^ ((r >> 2) & 3).  The LDS serves 16 lanes of a 16-byte read

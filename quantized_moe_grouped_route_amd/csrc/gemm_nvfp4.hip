@@ -23,7 +23,10 @@
 namespace moeq {
 namespace {
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// g * sigmoid(g) with the hardware reciprocal (about 1 ulp) in place of an
+// IEEE division: the epilogue's largest VALU cost, and its error stays far
+// below the output's own rounding.
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // SiLU-gated product of the scaled gate and up outputs.  A finite limit
 // applies the clamp of megamoe_rm.cu's fc1_rm epilogue first: the gate is
